@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-KV hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--extra A,B]
+
+One step = one pass of the whole path over one synthetic batch: the step's slot mapping on the
+host (pkv_slot_mapping_step), the slots' upload, the KV append (pkv_write_kv), then the
+attention call (host work planning + decode split pass + split merge + prefill tiles). Inputs
+are resident in HBM before timing starts; the timed region is bracketed by device
+synchronisation. The headline workload is the batched bf16 decode step (64 sequences,
+lognormal lengths with median 2048, Hq 32, Hkv 8, D 128, block 16), reported as algorithmic
+GB/s (KV bytes read + append bytes moved, per step time). The mixed ragged step
+(8 x 512-row prefill chunks + 120 decodes) is reported alongside in tokens/s.
+
+Prints ONE JSON line (rank 0, N = 1). `--gpus N` with N > 1 exits: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def _parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="batched-bf16-decode")
+    ap.add_argument("--extra", default="mixed-ragged-step",
+                    help="comma-separated workloads timed the same way, reported under 'extra'")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate CPU time budget of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def _step_inputs(w, gst):
+    """Host arrays the step's slot mapping needs (prior lengths and new-row counts)."""
+    import numpy as np
+    starts = (w.ctx_lens - w.q_lens).astype(np.int32)
+    return starts, w.q_lens.astype(np.int32)
+
+
+def _kv_bytes(w):
+    from prefill_slot_mapping_amd import accounting as acc
+    return acc.decode_kv_bytes(w.ctx_lens, w.spec.Hkv, w.spec.D, w.elem_bytes)
+
+
+def time_workload(name, steps, warmup, device="cuda:0"):
+    """Build the step, then time `steps` whole steps; returns a result dict."""
+    import numpy as np
+    import torch
+    import prefill_slot_mapping_amd as pkv
+    from prefill_slot_mapping_amd import accounting as acc
+    from prefill_slot_mapping_amd.harness import build_gpu_step
+    from workloads import CONFIGS, make_workload
+
+    w = make_workload(CONFIGS[name])
+    t_build = time.time()
+    gst = build_gpu_step(w, device=device)
+    t_build = time.time() - t_build
+    s = w.spec
+    starts, n_new = _step_inputs(w, gst)
+    slots_host = torch.empty(w.T, dtype=torch.int32).pin_memory()
+    slots_np = slots_host.numpy()
+    slots_dev = torch.empty(w.T, dtype=torch.int32, device=device)
+    ws_bytes = pkv.attention_workspace_size(w.ctx_lens, w.cu_seqlens_q, s.Hq, s.Hkv, s.D,
+                                            s.kv_split, pkv.PKV_BF16 if s.dtype == "bf16"
+                                            else pkv.PKV_F32)
+    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=device)
+    out = torch.empty((w.T, s.Hq, s.D), dtype=torch.float32, device=device)
+
+    def step():
+        pkv.slot_mapping_step(gst.allocator, gst.block_tables, s.BS, starts, n_new, out=slots_np)
+        slots_dev.copy_(slots_host, non_blocking=True)
+        pkv.write_kv(gst.k_new, gst.v_new, slots_dev, gst.k_cache, gst.v_cache)
+        pkv.attention(gst.q, gst.k_cache, gst.v_cache, gst.block_tables_dev, w.ctx_lens,
+                      w.cu_seqlens_q, w.scale, out=out, workspace=workspace,
+                      kv_split=s.kv_split)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize(device)
+    pkv.profile_enable(True)
+    torch.cuda.synchronize(device)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize(device)
+    dt = time.perf_counter() - t0
+    kern = {k: pkv.profile_read(k) for k in ("write_kv", "prefill", "decode", "merge")}
+    pkv.profile_enable(False)
+    assert np.array_equal(slots_np[:w.T], gst.new_slots)
+
+    ms_step = dt / steps * 1e3
+    kv = _kv_bytes(w)
+    app = acc.append_bytes(w.T, s.Hkv, s.D, w.elem_bytes)
+    decode_rows = w.q_lens == 1
+    dec_kv = acc.decode_kv_bytes(w.ctx_lens[decode_rows], s.Hkv, s.D, w.elem_bytes)
+    flops = acc.attention_flops(w.ctx_lens[~decode_rows], w.q_lens[~decode_rows], s.Hq, s.D)
+    res = {
+        "workload": name, "B": w.B, "T": w.T, "ms_per_step": ms_step,
+        "step_gbs": (kv + app) / (ms_step * 1e-3) / 1e9, "tokens_per_s": w.T / (ms_step * 1e-3),
+        "kv_bytes": kv, "append_bytes": app, "decode_kv_bytes": dec_kv, "prefill_flops": flops,
+        "build_s": t_build,
+        "kernels_ms": {k: (v[0] / v[1] if v[1] else None) for k, v in kern.items()},
+        "kernel_launches": {k: v[1] for k, v in kern.items()},
+    }
+    t_roof = max((kv + app) / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+    res["roofline_frac_step"] = t_roof / (ms_step * 1e-3)
+    res["_gst"] = gst
+    res["_w"] = w
+    return res
+
+
+def cpu_baseline(w, budget_s):
+    """The oracle as it stands, on a bounded sample of the same workload's decode rows."""
+    import numpy as np
+    from oracle import build_oracle_step
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    rows_done = 0
+    kv_done = 0
+    spent = 0.0
+    order = list(range(w.B))
+    sample = []
+    # calibrate on the first sequence, then take as many as fit the budget
+    per_token = None
+    chosen = []
+    est = 0.0
+    for b in order:
+        if w.q_lens[b] == 0:
+            continue
+        if per_token is not None and est + per_token * int(w.ctx_lens[b]) * int(w.q_lens[b]) > budget_s:
+            continue
+        chosen.append(b)
+        if per_token is None:
+            st = build_oracle_step(w, seqs=[b], poison=False)
+            t = time.perf_counter()
+            st.attention(rows=range(int(w.cu_seqlens_q[b]), int(w.cu_seqlens_q[b + 1])))
+            el = time.perf_counter() - t
+            per_token = el / (int(w.ctx_lens[b]) * int(w.q_lens[b]))
+            est += el
+        else:
+            est += per_token * int(w.ctx_lens[b]) * int(w.q_lens[b])
+    st = build_oracle_step(w, seqs=chosen, poison=False)
+    rows = [r for b in chosen for r in range(int(w.cu_seqlens_q[b]), int(w.cu_seqlens_q[b + 1]))]
+    t = time.perf_counter()
+    st.attention(rows=rows)
+    spent = time.perf_counter() - t
+    from prefill_slot_mapping_amd import accounting as acc
+    kv_done = acc.decode_kv_bytes(w.ctx_lens[chosen], w.spec.Hkv, w.spec.D, w.elem_bytes)
+    sample = f"{len(chosen)} of {w.B} sequences ({len(rows)} query rows, " \
+             f"{int(w.ctx_lens[chosen].sum())} cached tokens), float64 per-row oracle"
+    return {"value": kv_done / spent / 1e9, "unit": "GB/s", "cores": int(blas_threads),
+            "kind": "oracle", "sample": sample, "seconds": spent,
+            "affinity_cores": len(os.sched_getaffinity(0))}
+
+
+def _traffic_for(kernel_file, launches_key):
+    """HBM bytes per launch from committed rocprofv3 PMC summaries, if the kernel is unchanged."""
+    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+        src = open(os.path.join(ROOT, "prefill_slot_mapping_amd", "csrc", kernel_file), "rb").read()
+        if rec.get("kernel_sha256") != hashlib.sha256(src).hexdigest():
+            return None
+        return rec.get(launches_key)
+    except Exception:
+        return None
+
+
+def main():
+    args = _parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
+                                   "(multi-GPU sharding is described in DESIGN.md, not run)"}))
+        sys.exit(2)
+    import torch
+    import prefill_slot_mapping_amd as pkv
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    pkv.lib()   # fail loudly if the HIP library is not built
+
+    main_res = time_workload(args.workload, args.steps, args.warmup)
+    w = main_res["_w"]
+    extra = {}
+    for name in [n for n in args.extra.split(",") if n and n != args.workload]:
+        r = time_workload(name, args.steps, args.warmup)
+        r.pop("_gst"); r.pop("_w")
+        extra[name] = r
+        torch.cuda.empty_cache()
+
+    dec_ms = main_res["kernels_ms"]["decode"]
+    achieved = main_res["decode_kv_bytes"] / (dec_ms * 1e-3) / 1e9 if dec_ms else None
+    roofline = {"bound": "hbm", "kernel": "decode_split_kernel", "achieved": achieved,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS if achieved else None,
+                "traffic": _traffic_for("kernels.hip", args.workload),
+                "bytes_per_launch": main_res["decode_kv_bytes"], "avg_launch_ms": dec_ms}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_seconds)
+    main_res.pop("_gst")
+    main_res.pop("_w")
+    s = w.spec
+    line = {
+        "metric": "paged decode KV GB/s (% HBM peak); mixed ragged step tokens/s",
+        "value": main_res["step_gbs"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": main_res["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": s.dtype, "data": "synthetic",
+        "config": {"workload": args.workload, "B": w.B, "Hq": s.Hq, "Hkv": s.Hkv, "D": s.D,
+                   "block_size": s.BS, "kv_split": s.kv_split,
+                   "cached_tokens": int(w.ctx_lens.sum()), "parallelism": "single-gpu"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "detail": main_res,
+        "extra": extra,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,193 @@
+/*
+ * pkv.h — C ABI of the paged-KV append and paged-attention library for AMD MI355X (gfx950).
+ *
+ * The library implements one hot path: new K/V rows are scattered into paged pools through an
+ * int32 slot mapping, then a flat ragged step of decode rows and chunked-prefill rows attends
+ * over the paged cache. Sources of the operations:
+ *   [P3]  "P3: native paged-KV continuous-batching sampler" (align, code/docs/P3_ENGINE.md),
+ *         section "Design > paged.py" (BlockAllocator, PagedKVCache, TritonPagedAttention
+ *         contract) and "Design > engine.py" (Scheduler, Prefix sharing).
+ *   [PKV] "Optional paged KV cache (vLLM-style) — v1 design" (mlx-bun docs/design/
+ *         paged-kv-cache.md), section "Design" (BlockPool, typed PagedPoolExhausted).
+ *   [BC]  "Finish RL Training Faster: Bitwise-Consistent ..." section 2 (kernel determinism,
+ *         batch independence).
+ *
+ * Conventions for every entry point
+ *   - Returns PKV_OK (0) or a negative status; pkv_last_error() then gives a message (per
+ *     thread, valid until the next failing call on that thread).
+ *   - Arguments are validated on the host before anything happens: on any error nothing is
+ *     launched, nothing is copied and no allocator state changes.
+ *   - No exception crosses the ABI. No entry point allocates device memory: device buffers
+ *     are owned by the caller; the library owns only allocator handles and a small ring of
+ *     pinned host staging buffers for work lists.
+ *   - Device work is enqueued on the caller's stream (a hipStream_t passed as void*; NULL is
+ *     the default stream) and is asynchronous with respect to the host.
+ *   - Element type codes: PKV_F32 (float32) and PKV_BF16 (bfloat16). q, k_new, v_new and both
+ *     pools share one element type; attention output is always float32.
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status and element types ------------------------------------------------------- */
+enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID = -1,         /* malformed argument, shape, or id */
+  PKV_ERR_POOL_EXHAUSTED = -2,  /* [PKV] typed exhaustion: never a silent truncation */
+  PKV_ERR_DOUBLE_FREE = -3,     /* [P3] free of a block whose refcount is already 0 */
+  PKV_ERR_SHARED_WRITE = -4,    /* [P3] write into a block with refcount > 1 */
+  PKV_ERR_UNSUPPORTED = -5,     /* valid request outside the built kernel set */
+  PKV_ERR_HIP = -6,             /* HIP runtime error (launch, copy, event) */
+  PKV_ERR_INCONSISTENT = -7     /* allocator books do not add up */
+};
+
+enum { PKV_F32 = 0, PKV_BF16 = 1 };
+
+/* Message for the calling thread's last failure ("" if none). */
+const char* pkv_last_error(void);
+/* Library version string. */
+const char* pkv_version(void);
+
+/* ---- host block allocator [P3 "Design > paged.py": BlockAllocator] -------------------
+ * A LIFO free list plus one refcount per block. A fresh pool hands out ids 0, 1, 2, ...
+ * (the stack is [NB-1, ..., 1, 0] with 0 on top). Multi-id calls apply ids in array order
+ * and are all-or-nothing. The handle is not thread-safe: serialise calls on one handle.
+ */
+typedef struct pkv_alloc pkv_alloc;
+
+/* New allocator over num_blocks >= 0 blocks; *out receives the handle (caller destroys). */
+int32_t pkv_alloc_create(int32_t num_blocks, pkv_alloc** out);
+/* Release a handle (NULL is ignored). */
+void pkv_alloc_destroy(pkv_alloc* a);
+/* Pop n ids into out_ids[0..n) in pop order, each with refcount 1. All or nothing: if fewer
+ * than n blocks are free, returns PKV_ERR_POOL_EXHAUSTED and changes nothing [PKV "Design"]. */
+int32_t pkv_alloc_allocate(pkv_alloc* a, int32_t n, int32_t* out_ids);
+/* Share: +1 reference on each of ids[0..n). Every id must be live (refcount >= 1), else
+ * PKV_ERR_INVALID [P3 "Prefix sharing": only a running sequence's blocks are adopted]. */
+int32_t pkv_alloc_incref(pkv_alloc* a, int32_t n, const int32_t* ids);
+/* -1 reference on each of ids[0..n) in array order; a block reaching 0 is pushed on the free
+ * stack. A free at refcount 0 (counting repeats within the call) is PKV_ERR_DOUBLE_FREE. */
+int32_t pkv_alloc_free(pkv_alloc* a, int32_t n, const int32_t* ids);
+/* Refcount of block id (>= 0), or PKV_ERR_INVALID for an id outside the pool. */
+int32_t pkv_alloc_refcount(const pkv_alloc* a, int32_t id);
+/* Number of free blocks. */
+int32_t pkv_alloc_num_free(const pkv_alloc* a);
+/* Number of blocks in the pool. */
+int32_t pkv_alloc_num_blocks(const pkv_alloc* a);
+/* PKV_OK iff free + referenced == total, no id twice on the free stack and no free-stack
+ * member referenced [P3 "Design > paged.py": check_consistent]; else PKV_ERR_INCONSISTENT. */
+int32_t pkv_alloc_check_consistent(const pkv_alloc* a);
+/* Copy the free stack (bottom to top, pkv_alloc_num_free entries) and all refcounts
+ * (pkv_alloc_num_blocks entries) into caller buffers; either pointer may be NULL. */
+int32_t pkv_alloc_snapshot(const pkv_alloc* a, int32_t* free_stack_out, int32_t* refcounts_out);
+
+/* Slot mapping [P3 "Design > paged.py": slots()]: for positions start_pos .. start_pos+n_new-1
+ * of one sequence whose block-table row is bt_row[0..n_bt), writes
+ *   slots_out[i] = bt_row[p / block_size] * block_size + p % block_size.
+ * Refuses (PKV_ERR_SHARED_WRITE) a position whose block has refcount > 1: a shared block is
+ * read-only for everyone, owner included. A free block or a position past the row is
+ * PKV_ERR_INVALID. Host only; slots_out is host memory. */
+int32_t pkv_slot_mapping(const pkv_alloc* a, const int32_t* bt_row, int32_t n_bt,
+                         int32_t block_size, int32_t start_pos, int32_t n_new,
+                         int32_t* slots_out);
+
+/* Slot mapping of a whole step: for each sequence b < B, positions start_pos[b] ..
+ * start_pos[b] + n_new[b] - 1 through row b of block_tables_host ([B, max_blocks], host int32),
+ * written contiguously in sequence order to slots_out (sum of n_new entries). Same rules as
+ * pkv_slot_mapping; all sequences are validated before any slot is written. Host only. */
+int32_t pkv_slot_mapping_step(const pkv_alloc* a, const int32_t* block_tables_host, int32_t B,
+                              int32_t max_blocks, int32_t block_size, const int32_t* start_pos,
+                              const int32_t* n_new, int32_t* slots_out);
+
+/* Host check of a slot array before pkv_write_kv: every slot is negative (padding, skipped)
+ * or in [0, num_slots), and no non-negative slot appears twice. PKV_OK or PKV_ERR_INVALID. */
+int32_t pkv_validate_slots(const int32_t* slots_host, int32_t n, int64_t num_slots);
+
+/* ---- KV append [P3 "Design > paged.py": copy-free append, write scatters into
+ *      (block, offset) in place] -----------------------------------------------------------
+ * k_new, v_new: device [n_rows, num_kv_heads, head_dim] contiguous, element type dtype.
+ * slots_dev:    device int32 [n_rows]; row t goes to slot s = slots_dev[t] (= block *
+ *               block_size + offset), i.e. k_cache[s / block_size][s % block_size] = k_new[t].
+ *               A negative slot skips its row. A slot >= num_blocks * block_size is skipped
+ *               too (never written out of bounds). Duplicate non-negative slots leave the
+ *               destination undefined: check host copies with pkv_validate_slots.
+ * k_cache, v_cache: device [num_blocks, block_size, num_kv_heads, head_dim], written in place.
+ * Bytes are copied exactly. Enqueued on stream. n_rows == 0 is a no-op. */
+int32_t pkv_write_kv(const void* k_new, const void* v_new, const int32_t* slots_dev,
+                     int32_t n_rows, void* k_cache, void* v_cache, int32_t num_blocks,
+                     int32_t block_size, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                     void* stream);
+
+/* ---- ragged paged attention [P3 "Design > paged.py": TritonPagedAttention contract —
+ *      q, k/v cache blocks, block tables, cu_seqlens_q, ctx_lens, slot mapping; fixed KV
+ *      split per context length, no atomics] ---------------------------------------------
+ *
+ * Semantics. Sequence b owns query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1; they are the
+ * LAST q_len = cu[b+1]-cu[b] positions of its ctx_lens[b] cached tokens (ctx_lens counts the
+ * cache after this step's append, new tokens included). The row at position pos attends over
+ * keys 0..pos of its own sequence (causal inside a prefill chunk, prior context fully
+ * visible). Query head h reads kv head h / (num_q_heads / num_kv_heads) [P3 "Tensor
+ * parallelism > Design": blocked GQA map]. out[t][h] = sum_j softmax_j(scale * q.k_j) v_j,
+ * accumulated in float32 and written as float32.
+ *
+ * Batch invariance [BC section 2]: a row's bits depend only on its own query, its sequence's
+ * K/V values, its position, ctx_len and its kind (decode = segment with q_len == 1, prefill =
+ * q_len > 1). They do not depend on the other sequences, the row's index in the step, the
+ * physical placement of blocks, the stream or the run. Decode rows are cut into fixed splits
+ * of kv_split tokens aligned at position 0 and merged in ascending split order; prefill rows
+ * visit 64-token key tiles aligned at position 0 in ascending order. No atomics anywhere.
+ *
+ * Arguments.
+ *   q:             device [T, num_q_heads, head_dim], element type dtype.
+ *   k_cache, v_cache: device [num_blocks, block_size, num_kv_heads, head_dim], dtype.
+ *   block_tables_dev: device int32 [B, max_blocks]; entries at and past ceil(ctx_lens[b] /
+ *                  block_size) are never read. A read entry outside [0, num_blocks) is never
+ *                  dereferenced: the rows that need it come out NaN.
+ *   ctx_lens_host, cu_seqlens_q_host: host int32 [B] and [B + 1]; they drive the host work
+ *                  planner. Need cu[0] == 0, cu non-decreasing, cu[B] == T,
+ *                  0 <= q_len <= ctx_len <= max_blocks * block_size.
+ *   head_dim:      64 or 128. num_q_heads / num_kv_heads in {1, 2, 4, 8}.
+ *   kv_split:      positive multiple of 64 (512 is the default contract; part of the numeric
+ *                  contract, so keep it fixed for bitwise comparisons).
+ *   out:           device float32 [T, num_q_heads, head_dim].
+ *   workspace:     device buffer of at least pkv_attention_workspace_size() bytes, owned by
+ *                  the caller, not read by the caller; it must stay untouched until the
+ *                  enqueued work has finished. Calls that share a workspace must be ordered
+ *                  on one stream.
+ * Errors: PKV_ERR_INVALID (shapes, lengths, workspace too small), PKV_ERR_UNSUPPORTED
+ * (head_dim or group size outside the built set), PKV_ERR_HIP. */
+int32_t pkv_attention_workspace_size(const int32_t* ctx_lens_host,
+                                     const int32_t* cu_seqlens_q_host, int32_t B,
+                                     int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t kv_split, int32_t dtype,
+                                     size_t* bytes);
+
+int32_t pkv_attention(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables_dev, int32_t max_blocks,
+                      const int32_t* ctx_lens_host, const int32_t* cu_seqlens_q_host,
+                      int32_t B, int32_t T, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                      int32_t kv_split, int32_t dtype, float* out, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* ---- diagnostics: per-kernel device time ------------------------------------------------
+ * While enabled, every kernel launched by pkv_write_kv / pkv_attention is bracketed by two HIP
+ * events recorded on its launch stream (the library owns the events). pkv_profile_read waits
+ * for the recorded launches of one kernel kind and returns their summed elapsed time and count.
+ * Kernel kinds: 0 KV append, 1 prefill tiles, 2 decode split pass, 3 split merge.
+ * pkv_profile_enable(1) clears previous records; pkv_profile_enable(0) stops recording.
+ * Not thread-safe with concurrent launches from several host threads. */
+int32_t pkv_profile_enable(int32_t enable);
+int32_t pkv_profile_read(int32_t kernel_kind, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H_ */

@@ -1,0 +1,12 @@
+"""pkv — paged-KV append and ragged paged attention for AMD MI355X (gfx950).
+
+The hot path lives in libpkv.so (hand-written HIP kernels + a C++ host runtime behind the C
+ABI of include/pkv.h). This package is the thin Python binding of that ABI plus the accounting
+helpers used to state algorithmic bytes and FLOPs.
+"""
+from ._lib import (  # noqa: F401
+    PKV_BF16, PKV_F32, BlockAllocator, DoubleFree, HipError, Inconsistent, InvalidArgument,
+    PkvError, PoolExhausted, SharedWrite, Unsupported, attention, attention_workspace_size,
+    header_functions, lib, profile_enable, profile_read, slot_mapping_step, validate_slots, version, write_kv,
+)
+from . import accounting  # noqa: F401

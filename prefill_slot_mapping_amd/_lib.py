@@ -1,0 +1,349 @@
+"""ctypes binding of libpkv.so (the C ABI declared in include/pkv.h).
+
+Argument marshalling only: every step of the path (slot mapping, allocator bookkeeping, work
+planning, the KV scatter and the attention kernels) runs inside the library. Device buffers
+are torch tensors (PyTorch is used for device memory and streams); host metadata are int32
+numpy arrays or CPU tensors. Importing this module does not need a GPU; calling a device entry
+point does. If libpkv.so is missing, every call raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                           "include", "pkv.h")
+
+PKV_OK = 0
+PKV_ERR_INVALID = -1
+PKV_ERR_POOL_EXHAUSTED = -2
+PKV_ERR_DOUBLE_FREE = -3
+PKV_ERR_SHARED_WRITE = -4
+PKV_ERR_UNSUPPORTED = -5
+PKV_ERR_HIP = -6
+PKV_ERR_INCONSISTENT = -7
+PKV_F32 = 0
+PKV_BF16 = 1
+
+
+class PkvError(RuntimeError):
+    status = None
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+        self.message = message
+
+
+class InvalidArgument(PkvError):
+    pass
+
+
+class PoolExhausted(PkvError):
+    pass
+
+
+class DoubleFree(PkvError):
+    pass
+
+
+class SharedWrite(PkvError):
+    pass
+
+
+class Unsupported(PkvError):
+    pass
+
+
+class HipError(PkvError):
+    pass
+
+
+class Inconsistent(PkvError):
+    pass
+
+
+_ERRORS = {
+    PKV_ERR_INVALID: InvalidArgument, PKV_ERR_POOL_EXHAUSTED: PoolExhausted,
+    PKV_ERR_DOUBLE_FREE: DoubleFree, PKV_ERR_SHARED_WRITE: SharedWrite,
+    PKV_ERR_UNSUPPORTED: Unsupported, PKV_ERR_HIP: HipError, PKV_ERR_INCONSISTENT: Inconsistent,
+}
+
+_lib = None
+
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+_pi32 = ctypes.POINTER(ctypes.c_int32)
+_SIGS = {
+    "pkv_last_error": ([], ctypes.c_char_p),
+    "pkv_version": ([], ctypes.c_char_p),
+    "pkv_alloc_create": ([_i32, ctypes.POINTER(_vp)], _i32),
+    "pkv_alloc_destroy": ([_vp], None),
+    "pkv_alloc_allocate": ([_vp, _i32, _pi32], _i32),
+    "pkv_alloc_incref": ([_vp, _i32, _pi32], _i32),
+    "pkv_alloc_free": ([_vp, _i32, _pi32], _i32),
+    "pkv_alloc_refcount": ([_vp, _i32], _i32),
+    "pkv_alloc_num_free": ([_vp], _i32),
+    "pkv_alloc_num_blocks": ([_vp], _i32),
+    "pkv_alloc_check_consistent": ([_vp], _i32),
+    "pkv_alloc_snapshot": ([_vp, _pi32, _pi32], _i32),
+    "pkv_slot_mapping": ([_vp, _pi32, _i32, _i32, _i32, _i32, _pi32], _i32),
+    "pkv_slot_mapping_step": ([_vp, _pi32, _i32, _i32, _i32, _pi32, _pi32, _pi32], _i32),
+    "pkv_validate_slots": ([_pi32, _i32, _i64], _i32),
+    "pkv_write_kv": ([_vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp], _i32),
+    "pkv_attention_workspace_size": ([_pi32, _pi32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                      ctypes.POINTER(ctypes.c_size_t)], _i32),
+    "pkv_attention": ([_vp, _vp, _vp, _vp, _i32, _pi32, _pi32, _i32, _i32, _i32, _i32, _i32,
+                       _i32, _i32, ctypes.c_float, _i32, _i32, _vp, _vp, ctypes.c_size_t, _vp],
+                      _i32),
+    "pkv_profile_enable": ([_i32], _i32),
+    "pkv_profile_read": ([_i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)], _i32),
+}
+
+KERNEL_KINDS = {"write_kv": 0, "prefill": 1, "decode": 2, "merge": 3}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m prefill_slot_mapping_amd.build` (no fallback path)")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(l, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = l
+    return _lib
+
+
+def header_functions() -> List[str]:
+    """Names of every function declared in include/pkv.h."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
+
+
+def _check(status: int) -> int:
+    if status >= 0:
+        return status
+    msg = lib().pkv_last_error().decode("utf-8", "replace")
+    raise _ERRORS.get(status, PkvError)(status, msg)
+
+
+def _host_i32(x) -> np.ndarray:
+    if hasattr(x, "detach"):
+        if x.device.type != "cpu":
+            raise ValueError("host metadata must be CPU arrays")
+        x = x.detach().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(_pi32)
+
+
+def version() -> str:
+    return lib().pkv_version().decode()
+
+
+# ---- host allocator ----------------------------------------------------------------------
+
+class BlockAllocator:
+    """Handle on the library's LIFO + refcount block allocator (see include/pkv.h)."""
+
+    def __init__(self, num_blocks: int):
+        h = _vp()
+        _check(lib().pkv_alloc_create(int(num_blocks), ctypes.byref(h)))
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().pkv_alloc_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def num_blocks(self) -> int:
+        return _check(lib().pkv_alloc_num_blocks(self._h))
+
+    def num_free(self) -> int:
+        return _check(lib().pkv_alloc_num_free(self._h))
+
+    def allocate(self, n: int) -> List[int]:
+        out = np.zeros(max(int(n), 1), dtype=np.int32)
+        _check(lib().pkv_alloc_allocate(self._h, int(n), _ptr(out)))
+        return out[:int(n)].tolist()
+
+    def incref(self, ids: Sequence[int]) -> None:
+        a = _host_i32(list(ids))
+        _check(lib().pkv_alloc_incref(self._h, a.size, _ptr(a)))
+
+    def free(self, ids: Sequence[int]) -> None:
+        a = _host_i32(list(ids))
+        _check(lib().pkv_alloc_free(self._h, a.size, _ptr(a)))
+
+    def refcount(self, block: int) -> int:
+        return _check(lib().pkv_alloc_refcount(self._h, int(block)))
+
+    def check_consistent(self) -> bool:
+        st = lib().pkv_alloc_check_consistent(self._h)
+        if st == PKV_ERR_INCONSISTENT:
+            return False
+        _check(st)
+        return True
+
+    def snapshot(self) -> Tuple[List[int], List[int]]:
+        nf, nb = self.num_free(), self.num_blocks
+        stack = np.zeros(max(nf, 1), dtype=np.int32)
+        rc = np.zeros(max(nb, 1), dtype=np.int32)
+        _check(lib().pkv_alloc_snapshot(self._h, _ptr(stack), _ptr(rc)))
+        return stack[:nf].tolist(), rc[:nb].tolist()
+
+    def slots(self, block_table_row, start_pos: int, n_new: int, block_size: int) -> np.ndarray:
+        row = _host_i32(block_table_row)
+        out = np.zeros(max(int(n_new), 1), dtype=np.int32)
+        _check(lib().pkv_slot_mapping(self._h, _ptr(row), row.size, int(block_size),
+                                      int(start_pos), int(n_new), _ptr(out)))
+        return out[:int(n_new)]
+
+
+def slot_mapping_step(allocator: "BlockAllocator", block_tables, block_size: int, start_pos,
+                      n_new, out: Optional[np.ndarray] = None) -> np.ndarray:
+    """pkv_slot_mapping_step: the slots of every sequence's new positions, in sequence order."""
+    bt = _host_i32(block_tables)
+    st = _host_i32(start_pos)
+    nn = _host_i32(n_new)
+    total = int(nn.sum())
+    if out is None or out.size < total or out.dtype != np.int32:
+        out = np.zeros(max(total, 1), dtype=np.int32)
+    _check(lib().pkv_slot_mapping_step(allocator._h, _ptr(bt), bt.shape[0],
+                                       bt.shape[1] if bt.ndim == 2 else 0, int(block_size),
+                                       _ptr(st), _ptr(nn), _ptr(out)))
+    return out[:total]
+
+
+def validate_slots(slots, num_slots: int) -> None:
+    a = _host_i32(slots)
+    _check(lib().pkv_validate_slots(_ptr(a), a.size, int(num_slots)))
+
+
+# ---- device entry points -------------------------------------------------------------------
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return PKV_F32
+    if t.dtype == torch.bfloat16:
+        return PKV_BF16
+    raise Unsupported(PKV_ERR_UNSUPPORTED, f"element type {t.dtype} (float32 or bfloat16)")
+
+
+def _stream_ptr(t, stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return int(stream.cuda_stream)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError("device arguments must be contiguous GPU tensors")
+
+
+def write_kv(k_new, v_new, slots, k_cache, v_cache, stream=None) -> None:
+    """pkv_write_kv: scatter rows of k_new / v_new [T_w, Hkv, D] into the pools through slots.
+
+    ``slots`` is a device int32 tensor, or a host array that is validated with
+    pkv_validate_slots (range and duplicates) and then copied to the device.
+    """
+    import torch
+    _need_cuda(k_new, v_new, k_cache, v_cache)
+    nb, bs, hkv, d = k_cache.shape
+    if hasattr(slots, "is_cuda") and slots.is_cuda:
+        sl = slots
+    else:
+        host = _host_i32(slots)
+        validate_slots(host, nb * bs)
+        sl = torch.from_numpy(host).to(k_cache.device)
+    if sl.dtype != torch.int32 or not sl.is_contiguous():
+        raise ValueError("slots must be a contiguous int32 tensor")
+    _check(lib().pkv_write_kv(k_new.data_ptr(), v_new.data_ptr(), sl.data_ptr(),
+                              int(k_new.shape[0]), k_cache.data_ptr(), v_cache.data_ptr(), nb, bs,
+                              hkv, d, _dtype_code(k_cache), _stream_ptr(k_cache, stream)))
+
+
+def attention_workspace_size(ctx_lens, cu_seqlens_q, num_q_heads: int, num_kv_heads: int,
+                             head_dim: int, kv_split: int = 512, dtype: int = PKV_BF16) -> int:
+    ctx = _host_i32(ctx_lens)
+    cu = _host_i32(cu_seqlens_q)
+    out = ctypes.c_size_t(0)
+    _check(lib().pkv_attention_workspace_size(_ptr(ctx), _ptr(cu), ctx.size, int(num_q_heads),
+                                              int(num_kv_heads), int(head_dim), int(kv_split),
+                                              int(dtype), ctypes.byref(out)))
+    return int(out.value)
+
+
+def attention(q, k_cache, v_cache, block_tables, ctx_lens, cu_seqlens_q, scale: float,
+              out=None, workspace=None, kv_split: int = 512, stream=None):
+    """pkv_attention over a flat ragged step; returns out (float32 [T, Hq, D]).
+
+    q [T, Hq, D], pools [NB, BS, Hkv, D] (same element type), block_tables int32 [B, MB] on
+    the device; ctx_lens [B] and cu_seqlens_q [B + 1] on the host.
+    """
+    import torch
+    _need_cuda(q, k_cache, v_cache, block_tables)
+    if block_tables.dtype != torch.int32:
+        raise ValueError("block_tables must be int32")
+    ctx = _host_i32(ctx_lens)
+    cu = _host_i32(cu_seqlens_q)
+    T, hq, d = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    if d2 != d or v_cache.shape != k_cache.shape or q.dtype != k_cache.dtype:
+        raise ValueError("q / pool shape or dtype mismatch")
+    B = ctx.size
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B, max_blocks]")
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty((T, hq, d), dtype=torch.float32, device=q.device)
+    _need_cuda(out)
+    need = attention_workspace_size(ctx, cu, hq, hkv, d, kv_split, dt)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().pkv_attention(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                               block_tables.data_ptr(), int(block_tables.shape[1]), _ptr(ctx),
+                               _ptr(cu), B, T, hq, hkv, d, bs, nb, float(scale), int(kv_split),
+                               dt, out.data_ptr(), workspace.data_ptr(),
+                               workspace.numel() * workspace.element_size(),
+                               _stream_ptr(q, stream)))
+    return out
+
+
+# ---- diagnostics ---------------------------------------------------------------------------
+
+def profile_enable(on: bool = True) -> None:
+    """Start (clearing old records) or stop per-kernel HIP-event timing inside the library."""
+    _check(lib().pkv_profile_enable(1 if on else 0))
+
+
+def profile_read(kind: str) -> Tuple[float, int]:
+    """(summed device ms, launch count) of one kernel kind since profile_enable(True)."""
+    ms = ctypes.c_double(0.0)
+    n = _i64(0)
+    _check(lib().pkv_profile_read(KERNEL_KINDS[kind], ctypes.byref(ms), ctypes.byref(n)))
+    return float(ms.value), int(n.value)

@@ -1,0 +1,461 @@
+// C ABI of the device path: argument validation, the host work planner, the pinned staging
+// ring for work lists, and kernel launches on the caller's stream.
+//
+// The planner follows the kernel contract of "P3: native paged-KV continuous-batching
+// sampler", section "Design > paged.py" (TritonPagedAttention): a flat ragged step described
+// by cu_seqlens_q and ctx_lens, with a fixed KV split per context length and no atomics.
+// Each query row of sequence b at position pos sees keys 0..pos; a row is "decode" when its
+// segment has q_len == 1 and "prefill" otherwise. Routing depends only on the row's own
+// segment, so a row's work (and bits) never depend on the rest of the step.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "common.h"
+#include "kernels.h"
+#include "plan.h"
+
+using pkv::fail;
+using pkv::ok;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool valid_dtype(int32_t dt) { return dt == PKV_F32 || dt == PKV_BF16; }
+int elem_bytes(int32_t dt) { return dt == PKV_BF16 ? 2 : 4; }
+
+// ---- pinned staging ring: work lists are built on the host and copied asynchronously ----
+struct StagingSlot {
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t done = nullptr;
+  bool pending = false;
+};
+
+struct DeviceRing {
+  std::mutex mu;
+  StagingSlot slots[8];
+  int next = 0;
+};
+
+std::mutex g_rings_mu;
+std::unordered_map<int, DeviceRing*> g_rings;
+
+DeviceRing* ring_for_current_device(int* dev_out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  *dev_out = dev;
+  std::lock_guard<std::mutex> lk(g_rings_mu);
+  auto it = g_rings.find(dev);
+  if (it != g_rings.end()) return it->second;
+  DeviceRing* r = new DeviceRing();
+  g_rings[dev] = r;
+  return r;
+}
+
+// ---- diagnostics: event pairs around launches -------------------------------------------
+struct ProfRecord {
+  int kind;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRecord> g_prof_pending;
+std::vector<hipEvent_t> g_prof_free;
+double g_prof_ms[4] = {0, 0, 0, 0};
+int64_t g_prof_n[4] = {0, 0, 0, 0};
+
+hipEvent_t prof_event() {
+  if (!g_prof_free.empty()) {
+    hipEvent_t e = g_prof_free.back();
+    g_prof_free.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Records the opening event of a launch of `kind`; returns the record index or -1.
+int prof_begin(int kind, hipStream_t s) {
+  if (!g_prof_on) return -1;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  ProfRecord r{kind, prof_event(), prof_event()};
+  if (r.a == nullptr || r.b == nullptr) return -1;
+  if (hipEventRecord(r.a, s) != hipSuccess) return -1;
+  g_prof_pending.push_back(r);
+  return static_cast<int>(g_prof_pending.size()) - 1;
+}
+
+void prof_end(int idx, hipStream_t s) {
+  if (idx < 0) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  (void)hipEventRecord(g_prof_pending[idx].b, s);
+}
+
+// ---- work planning ----------------------------------------------------------------------
+struct StepShape {
+  const int32_t* ctx;
+  const int32_t* cu;
+  int32_t B;
+  int32_t kv_split;
+  bool prefill_on_mfma;  // segments with q_len > 1 use the prefill kernel
+  int32_t prefill_rows_per_item;
+};
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Counts and layout only (no lists).
+pkv::WorkspaceLayout layout_for(const StepShape& s, int32_t hq, int32_t head_dim) {
+  pkv::WorkspaceLayout L;
+  for (int32_t b = 0; b < s.B; ++b) {
+    const int32_t ql = s.cu[b + 1] - s.cu[b];
+    if (ql == 0) continue;
+    if (ql > 1 && s.prefill_on_mfma) {
+      L.n_prefill += ceil_div(ql, s.prefill_rows_per_item);
+      continue;
+    }
+    for (int32_t i = 0; i < ql; ++i) {
+      const int64_t n_keys = static_cast<int64_t>(s.ctx[b]) - ql + i + 1;
+      const int64_t ns = ceil_div(n_keys, s.kv_split);
+      L.n_decode += ns;
+      if (ns > 1) {
+        L.n_merge += 1;
+        L.n_part += ns;
+      }
+    }
+  }
+  size_t off = 0;
+  L.decode_off = off;
+  off = align_up(off + L.n_decode * sizeof(pkv::DecodeItem));
+  L.merge_off = off;
+  off = align_up(off + L.n_merge * sizeof(pkv::MergeItem));
+  L.prefill_off = off;
+  off = align_up(off + L.n_prefill * sizeof(pkv::PrefillItem));
+  L.list_bytes = off;
+  L.part_m_off = off;
+  off = align_up(off + L.n_part * hq * sizeof(float));
+  L.part_l_off = off;
+  off = align_up(off + L.n_part * hq * sizeof(float));
+  L.part_acc_off = off;
+  off = align_up(off + L.n_part * hq * head_dim * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+void build_lists(const StepShape& s, const pkv::WorkspaceLayout& L, char* host) {
+  auto* dec = reinterpret_cast<pkv::DecodeItem*>(host + L.decode_off);
+  auto* mer = reinterpret_cast<pkv::MergeItem*>(host + L.merge_off);
+  auto* pre = reinterpret_cast<pkv::PrefillItem*>(host + L.prefill_off);
+  int64_t nd = 0, nm = 0, np = 0, part = 0;
+  for (int32_t b = 0; b < s.B; ++b) {
+    const int32_t ql = s.cu[b + 1] - s.cu[b];
+    if (ql == 0) continue;
+    if (ql > 1 && s.prefill_on_mfma) {
+      const int32_t prior = s.ctx[b] - ql;
+      for (int32_t r0 = 0; r0 < ql; r0 += s.prefill_rows_per_item) {
+        pkv::PrefillItem& p = pre[np++];
+        p.seq = b;
+        p.row0 = s.cu[b] + r0;
+        p.n_rows = std::min(s.prefill_rows_per_item, ql - r0);
+        p.pos0 = prior + r0;
+      }
+      continue;
+    }
+    for (int32_t i = 0; i < ql; ++i) {
+      const int32_t row = s.cu[b] + i;
+      const int32_t n_keys = s.ctx[b] - ql + i + 1;
+      const int32_t ns = static_cast<int32_t>(ceil_div(n_keys, s.kv_split));
+      int32_t pbase = -1;
+      if (ns > 1) {
+        pbase = static_cast<int32_t>(part);
+        mer[nm++] = pkv::MergeItem{row, ns, pbase, 0};
+        part += ns;
+      }
+      for (int32_t sp = 0; sp < ns; ++sp) dec[nd++] = pkv::DecodeItem{row, b, n_keys, sp, pbase, 0, 0, 0};
+    }
+  }
+}
+
+int32_t check_step(const int32_t* ctx, const int32_t* cu, int32_t B, int32_t T,
+                   int64_t max_keys) {
+  if (B < 0 || T < 0) return fail(PKV_ERR_INVALID, "B and T must be >= 0");
+  if (B > 0 && (ctx == nullptr || cu == nullptr))
+    return fail(PKV_ERR_INVALID, "ctx_lens_host / cu_seqlens_q_host is NULL");
+  if (B == 0) {
+    if (T != 0) return fail(PKV_ERR_INVALID, "T must be 0 when B is 0");
+    return PKV_OK;
+  }
+  if (cu[0] != 0) return fail(PKV_ERR_INVALID, "cu_seqlens_q[0] must be 0");
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t ql = cu[b + 1] - cu[b];
+    if (cu[b + 1] < cu[b]) return fail(PKV_ERR_INVALID, "cu_seqlens_q must be non-decreasing");
+    if (ctx[b] < 0) return fail(PKV_ERR_INVALID, "ctx_lens must be >= 0");
+    if (ql > ctx[b])
+      return fail(PKV_ERR_INVALID, "sequence " + std::to_string(b) + ": q_len " +
+                                       std::to_string(ql) + " > ctx_len " + std::to_string(ctx[b]));
+    if (max_keys >= 0 && ctx[b] > max_keys)
+      return fail(PKV_ERR_INVALID, "sequence " + std::to_string(b) +
+                                       ": ctx_len exceeds max_blocks * block_size");
+  }
+  if (cu[B] != T) return fail(PKV_ERR_INVALID, "cu_seqlens_q[B] must equal T");
+  return PKV_OK;
+}
+
+int32_t check_heads(int32_t hq, int32_t hkv, int32_t head_dim, int32_t kv_split, int32_t dtype) {
+  if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID, "dtype must be PKV_F32 or PKV_BF16");
+  if (hq <= 0 || hkv <= 0) return fail(PKV_ERR_INVALID, "head counts must be positive");
+  if (hq % hkv != 0) return fail(PKV_ERR_INVALID, "num_q_heads must be a multiple of num_kv_heads");
+  if (kv_split <= 0 || kv_split % pkv::kDecodeTile != 0)
+    return fail(PKV_ERR_INVALID, "kv_split must be a positive multiple of 64");
+  if (!pkv::decode_supported(head_dim, hq / hkv))
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim must be 64 or 128 and num_q_heads / num_kv_heads "
+                                     "one of 1, 2, 4, 8");
+  return PKV_OK;
+}
+
+StepShape shape_for(const int32_t* ctx, const int32_t* cu, int32_t B, int32_t hq, int32_t hkv,
+                    int32_t head_dim, int32_t kv_split, int32_t dtype) {
+  StepShape s;
+  s.ctx = ctx;
+  s.cu = cu;
+  s.B = B;
+  s.kv_split = kv_split;
+  const int group = hq / hkv;
+  s.prefill_on_mfma = pkv::prefill_supported(head_dim, group, dtype == PKV_BF16);
+  s.prefill_rows_per_item = pkv::kPrefillMRows / group;
+  return s;
+}
+
+}  // namespace
+
+extern "C" int32_t pkv_write_kv(const void* k_new, const void* v_new, const int32_t* slots_dev,
+                                int32_t n_rows, void* k_cache, void* v_cache, int32_t num_blocks,
+                                int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t dtype, void* stream) {
+  if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID, "write_kv: bad dtype");
+  if (n_rows < 0 || num_blocks < 0 || block_size <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+    return fail(PKV_ERR_INVALID, "write_kv: bad sizes");
+  const int64_t row_bytes = static_cast<int64_t>(num_kv_heads) * head_dim * elem_bytes(dtype);
+  if (row_bytes % 16 != 0)
+    return fail(PKV_ERR_UNSUPPORTED, "write_kv: num_kv_heads * head_dim * elem_bytes must be a "
+                                     "multiple of 16");
+  if (n_rows == 0) return ok();
+  if (k_new == nullptr || v_new == nullptr || slots_dev == nullptr || k_cache == nullptr ||
+      v_cache == nullptr)
+    return fail(PKV_ERR_INVALID, "write_kv: NULL pointer");
+  if (static_cast<int64_t>(n_rows) * (row_bytes / 16) > 0xffffffffLL)
+    return fail(PKV_ERR_UNSUPPORTED, "write_kv: too many rows in one call");
+  pkv::WriteArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.slots = slots_dev;
+  a.n_rows = n_rows;
+  a.chunks_per_row = static_cast<int32_t>(row_bytes / 16);
+  a.n_slots = static_cast<int64_t>(num_blocks) * block_size;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  const int pr = prof_begin(0, static_cast<hipStream_t>(stream));
+  hipError_t e = pkv::launch_write_kv(a, static_cast<hipStream_t>(stream));
+  prof_end(pr, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("write_kv launch: ") + hipGetErrorString(e));
+  return ok();
+}
+
+extern "C" int32_t pkv_attention_workspace_size(const int32_t* ctx_lens_host,
+                                                const int32_t* cu_seqlens_q_host, int32_t B,
+                                                int32_t num_q_heads, int32_t num_kv_heads,
+                                                int32_t head_dim, int32_t kv_split, int32_t dtype,
+                                                size_t* bytes) {
+  if (bytes == nullptr) return fail(PKV_ERR_INVALID, "workspace_size: bytes is NULL");
+  *bytes = 0;
+  int32_t st = check_heads(num_q_heads, num_kv_heads, head_dim, kv_split, dtype);
+  if (st != PKV_OK) return st;
+  const int32_t T = (B > 0 && cu_seqlens_q_host != nullptr) ? cu_seqlens_q_host[B] : 0;
+  st = check_step(ctx_lens_host, cu_seqlens_q_host, B, T, -1);
+  if (st != PKV_OK) return st;
+  if (B == 0) return ok();
+  StepShape s = shape_for(ctx_lens_host, cu_seqlens_q_host, B, num_q_heads, num_kv_heads,
+                          head_dim, kv_split, dtype);
+  *bytes = layout_for(s, num_q_heads, head_dim).total;
+  return ok();
+}
+
+extern "C" int32_t pkv_attention(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables_dev, int32_t max_blocks,
+                                 const int32_t* ctx_lens_host, const int32_t* cu_seqlens_q_host,
+                                 int32_t B, int32_t T, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                 float scale, int32_t kv_split, int32_t dtype, float* out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  int32_t st = check_heads(num_q_heads, num_kv_heads, head_dim, kv_split, dtype);
+  if (st != PKV_OK) return st;
+  if (block_size <= 0 || num_blocks <= 0 || max_blocks < 0)
+    return fail(PKV_ERR_INVALID, "block_size, num_blocks must be > 0 and max_blocks >= 0");
+  if (static_cast<int64_t>(num_blocks) * block_size > INT32_MAX)
+    return fail(PKV_ERR_UNSUPPORTED, "pool has more slots than int32 can address");
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID, "scale must be finite");
+  st = check_step(ctx_lens_host, cu_seqlens_q_host, B, T,
+                  static_cast<int64_t>(max_blocks) * block_size);
+  if (st != PKV_OK) return st;
+  if (T == 0) return ok();
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_tables_dev == nullptr ||
+      out == nullptr)
+    return fail(PKV_ERR_INVALID, "attention: NULL device pointer");
+
+  const StepShape s = shape_for(ctx_lens_host, cu_seqlens_q_host, B, num_q_heads, num_kv_heads,
+                                head_dim, kv_split, dtype);
+  const pkv::WorkspaceLayout L = layout_for(s, num_q_heads, head_dim);
+  if (workspace_bytes < L.total || (L.total > 0 && workspace == nullptr))
+    return fail(PKV_ERR_INVALID, "attention: workspace smaller than pkv_attention_workspace_size (" +
+                                     std::to_string(L.total) + " bytes)");
+  if (L.n_decode * num_kv_heads > INT32_MAX || L.n_prefill * num_kv_heads > INT32_MAX)
+    return fail(PKV_ERR_UNSUPPORTED, "attention: step too large for one launch");
+
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+
+  // work lists -> pinned staging -> workspace (async, ordered before the kernels)
+  if (L.list_bytes > 0) {
+    int dev = 0;
+    DeviceRing* ring = ring_for_current_device(&dev);
+    if (ring == nullptr) return fail(PKV_ERR_HIP, "attention: hipGetDevice failed");
+    std::lock_guard<std::mutex> lk(ring->mu);
+    StagingSlot& slot = ring->slots[ring->next];
+    ring->next = (ring->next + 1) % 8;
+    if (slot.pending) {
+      hipError_t e = hipEventSynchronize(slot.done);
+      if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("attention: staging wait: ") + hipGetErrorString(e));
+      slot.pending = false;
+    }
+    if (slot.done == nullptr) {
+      hipError_t e = hipEventCreateWithFlags(&slot.done, hipEventDisableTiming);
+      if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("attention: event: ") + hipGetErrorString(e));
+    }
+    if (slot.cap < L.list_bytes) {
+      if (slot.host != nullptr) (void)hipHostFree(slot.host);
+      slot.host = nullptr;
+      slot.cap = 0;
+      size_t want = std::max<size_t>(L.list_bytes, 1 << 16);
+      hipError_t e = hipHostMalloc(&slot.host, want, hipHostMallocDefault);
+      if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("attention: pinned staging: ") + hipGetErrorString(e));
+      slot.cap = want;
+    }
+    build_lists(s, L, static_cast<char*>(slot.host));
+    hipError_t e = hipMemcpyAsync(ws, slot.host, L.list_bytes, hipMemcpyHostToDevice, strm);
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("attention: list copy: ") + hipGetErrorString(e));
+    e = hipEventRecord(slot.done, strm);
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("attention: event record: ") + hipGetErrorString(e));
+    slot.pending = true;
+  }
+
+  const float scale_log2e = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  const int group = num_q_heads / num_kv_heads;
+  float* part_m = reinterpret_cast<float*>(ws + L.part_m_off);
+  float* part_l = reinterpret_cast<float*>(ws + L.part_l_off);
+  float* part_acc = reinterpret_cast<float*>(ws + L.part_acc_off);
+
+  if (L.n_prefill > 0) {
+    pkv::PrefillArgs p;
+    p.q = q;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.block_tables = block_tables_dev;
+    p.ctx_lens = nullptr;
+    p.max_blocks = max_blocks;
+    p.block_size = block_size;
+    p.num_blocks = num_blocks;
+    p.hq = num_q_heads;
+    p.hkv = num_kv_heads;
+    p.scale_log2e = scale_log2e;
+    p.items = reinterpret_cast<const pkv::PrefillItem*>(ws + L.prefill_off);
+    p.out = out;
+    const int pr = prof_begin(1, strm);
+    hipError_t e = pkv::launch_prefill(p, L.n_prefill, head_dim, group, strm);
+    prof_end(pr, strm);
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("prefill launch: ") + hipGetErrorString(e));
+  }
+  if (L.n_decode > 0) {
+    pkv::DecodeArgs d;
+    d.q = q;
+    d.k_cache = k_cache;
+    d.v_cache = v_cache;
+    d.block_tables = block_tables_dev;
+    d.max_blocks = max_blocks;
+    d.block_size = block_size;
+    d.num_blocks = num_blocks;
+    d.hq = num_q_heads;
+    d.hkv = num_kv_heads;
+    d.kv_split = kv_split;
+    d.scale_log2e = scale_log2e;
+    d.items = reinterpret_cast<const pkv::DecodeItem*>(ws + L.decode_off);
+    d.out = out;
+    d.part_m = part_m;
+    d.part_l = part_l;
+    d.part_acc = part_acc;
+    const int pr = prof_begin(2, strm);
+    hipError_t e = pkv::launch_decode(d, L.n_decode, head_dim, group, dtype == PKV_BF16, strm);
+    prof_end(pr, strm);
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("decode launch: ") + hipGetErrorString(e));
+  }
+  if (L.n_merge > 0) {
+    pkv::MergeArgs mg;
+    mg.items = reinterpret_cast<const pkv::MergeItem*>(ws + L.merge_off);
+    mg.hq = num_q_heads;
+    mg.part_m = part_m;
+    mg.part_l = part_l;
+    mg.part_acc = part_acc;
+    mg.out = out;
+    const int pr = prof_begin(3, strm);
+    hipError_t e = pkv::launch_merge(mg, L.n_merge, head_dim, strm);
+    prof_end(pr, strm);
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("merge launch: ") + hipGetErrorString(e));
+  }
+  return ok();
+}
+
+extern "C" int32_t pkv_profile_enable(int32_t enable) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (enable) {
+    for (auto& r : g_prof_pending) {
+      (void)hipEventSynchronize(r.b);
+      g_prof_free.push_back(r.a);
+      g_prof_free.push_back(r.b);
+    }
+    g_prof_pending.clear();
+    for (int k = 0; k < 4; ++k) {
+      g_prof_ms[k] = 0;
+      g_prof_n[k] = 0;
+    }
+  }
+  g_prof_on = enable != 0;
+  return ok();
+}
+
+extern "C" int32_t pkv_profile_read(int32_t kernel_kind, double* total_ms, int64_t* launches) {
+  if (kernel_kind < 0 || kernel_kind > 3 || total_ms == nullptr || launches == nullptr)
+    return fail(PKV_ERR_INVALID, "profile_read: bad arguments");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto& r : g_prof_pending) {
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("profile_read: ") + hipGetErrorString(e));
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("profile_read: ") + hipGetErrorString(e));
+    g_prof_ms[r.kind] += ms;
+    g_prof_n[r.kind] += 1;
+    g_prof_free.push_back(r.a);
+    g_prof_free.push_back(r.b);
+  }
+  g_prof_pending.clear();
+  *total_ms = g_prof_ms[kernel_kind];
+  *launches = g_prof_n[kernel_kind];
+  return ok();
+}

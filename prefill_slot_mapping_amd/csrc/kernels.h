@@ -1,0 +1,79 @@
+// Internal launch interface of the HIP kernels (host side of kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "plan.h"
+
+namespace pkv {
+
+struct WriteArgs {
+  const void* k_new;
+  const void* v_new;
+  const int32_t* slots;
+  int32_t n_rows;
+  int32_t chunks_per_row;  // num_kv_heads * head_dim * elem_bytes / 16
+  int64_t n_slots;         // num_blocks * block_size
+  void* k_cache;
+  void* v_cache;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  int32_t max_blocks;
+  int32_t block_size;
+  int32_t num_blocks;
+  int32_t hq;
+  int32_t hkv;
+  int32_t kv_split;
+  float scale_log2e;  // softmax scale times log2(e): scores live in the base-2 domain
+  const DecodeItem* items;
+  float* out;
+  float* part_m;
+  float* part_l;
+  float* part_acc;
+};
+
+struct MergeArgs {
+  const MergeItem* items;
+  int32_t hq;
+  const float* part_m;
+  const float* part_l;
+  const float* part_acc;
+  float* out;
+};
+
+struct PrefillArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* ctx_lens;  // unused by the kernel; kept for bounds in debug builds
+  int32_t max_blocks;
+  int32_t block_size;
+  int32_t num_blocks;
+  int32_t hq;
+  int32_t hkv;
+  float scale_log2e;
+  const PrefillItem* items;
+  float* out;
+};
+
+// Each launcher enqueues one kernel on `stream` and returns hipSuccess or the launch error.
+hipError_t launch_write_kv(const WriteArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int64_t n_items, int head_dim, int group,
+                         bool bf16, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, int64_t n_items, int head_dim, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, int64_t n_items, int head_dim, int group,
+                          hipStream_t stream);
+
+// Whether a (head_dim, group, dtype) combination has a built decode / prefill kernel.
+bool decode_supported(int head_dim, int group);
+bool prefill_supported(int head_dim, int group, bool bf16);
+
+}  // namespace pkv

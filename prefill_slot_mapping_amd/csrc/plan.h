@@ -1,0 +1,56 @@
+// Work-list records and workspace layout shared by the host planner and the HIP kernels.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+namespace pkv {
+
+// Keys per decode tile: one key per lane of a 64-wide wavefront in the score stage.
+constexpr int kDecodeTile = 64;
+// Waves per decode workgroup; tile i of a split is handled by wave i % kDecodeWaves.
+constexpr int kDecodeWaves = 4;
+// Keys per prefill KV tile (tiles are aligned at absolute position 0).
+constexpr int kPrefillKeyTile = 64;
+// Query "M-rows" (query row x head pairs) per prefill workgroup: 4 waves x 32.
+constexpr int kPrefillMRows = 128;
+
+// One decode work item: split `split` of query row `row` (sequence `seq`), covering keys
+// [split * kv_split, min(n_keys, (split + 1) * kv_split)). The kernel grid runs items x Hkv.
+// part < 0: the row has one split and the kernel writes the final output; otherwise the
+// item writes partial slot (part + split) for its heads.
+struct DecodeItem {
+  int32_t row;
+  int32_t seq;
+  int32_t n_keys;
+  int32_t split;
+  int32_t part;
+  int32_t pad0, pad1, pad2;
+};
+
+// Split merge of one query row: partial slots part .. part + n_splits - 1, in ascending order.
+struct MergeItem {
+  int32_t row;
+  int32_t n_splits;
+  int32_t part;
+  int32_t pad;
+};
+
+// One prefill tile: rows row0 .. row0 + n_rows - 1 of sequence seq, at positions
+// pos0 .. pos0 + n_rows - 1. The kernel grid runs items x Hkv.
+struct PrefillItem {
+  int32_t seq;
+  int32_t row0;
+  int32_t n_rows;
+  int32_t pos0;
+};
+
+// Byte offsets of each region inside the caller's workspace (all 256-byte aligned).
+struct WorkspaceLayout {
+  size_t decode_off = 0, merge_off = 0, prefill_off = 0, part_m_off = 0, part_l_off = 0,
+         part_acc_off = 0, total = 0;
+  int64_t n_decode = 0, n_merge = 0, n_prefill = 0, n_part = 0;
+  size_t list_bytes = 0;  // decode + merge + prefill lists (the part copied from the host)
+};
+
+}  // namespace pkv

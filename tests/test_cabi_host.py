@@ -1,0 +1,212 @@
+"""Host side of the C ABI, on the CPU: symbols, block bookkeeping, slot mapping, validation.
+
+The C++ allocator must equal the oracle's twin bit-exactly on identical event traces: same
+returned ids, same error kinds, same free-stack order and refcounts after every event.
+Device entry points are exercised only for their host-side validation (nothing reaches the GPU:
+every call below is refused before any launch).
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+import prefill_slot_mapping_amd as pkv
+from prefill_slot_mapping_amd import _lib as L
+import oracle
+
+pytestmark = []
+
+
+def test_library_exports_every_header_function():
+    lib = pkv.lib()
+    names = pkv.header_functions()
+    assert len(names) >= 17
+    for n in names:
+        assert hasattr(lib, n), n
+    assert pkv.version().startswith("pkv")
+
+
+ERRMAP = {
+    oracle.PoolExhausted: pkv.PoolExhausted,
+    oracle.DoubleFree: pkv.DoubleFree,
+    oracle.SharedWrite: pkv.SharedWrite,
+    oracle.InvalidBlock: pkv.InvalidArgument,
+}
+
+
+def _both(fn_c, fn_o):
+    """Run one event on both; return (c_result, o_result) or the matching error classes."""
+    rc = ro = None
+    ec = eo = None
+    try:
+        rc = fn_c()
+    except pkv.PkvError as e:
+        ec = type(e)
+    try:
+        ro = fn_o()
+    except oracle.AllocatorError as e:
+        eo = ERRMAP[type(e)]
+    return rc, ro, ec, eo
+
+
+def _books_equal(c, o):
+    stack, rc = c.snapshot()
+    assert stack == o.free_stack
+    assert rc == o.refcount
+    assert c.num_free() == o.num_free()
+    assert c.check_consistent() == o.check_consistent()
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_cpp_allocator_equals_oracle_twin_on_random_traces(seed):
+    rng = np.random.default_rng(seed)
+    nb = 37
+    c = pkv.BlockAllocator(nb)
+    o = oracle.BlockAllocator(nb)
+    live = []      # references we hold (ids, possibly repeated)
+    counts = {"exhausted": 0, "double_free": 0, "shared_write": 0, "invalid": 0}
+    for step in range(4000):
+        r = rng.random()
+        if r < 0.35:
+            n = int(rng.integers(0, 9))
+            rc_, ro_, ec, eo = _both(lambda: c.allocate(n), lambda: o.allocate(n))
+            assert ec == eo and rc_ == ro_
+            if ec is None:
+                live.extend(rc_)
+            else:
+                counts["exhausted"] += 1
+        elif r < 0.5:
+            if live and rng.random() < 0.8:
+                ids = [live[int(i)] for i in rng.integers(0, len(live), size=int(rng.integers(1, 4)))]
+            else:
+                ids = [int(i) for i in rng.integers(-2, nb + 2, size=2)]
+            _, _, ec, eo = _both(lambda: c.incref(ids), lambda: o.incref(ids))
+            assert ec == eo
+            if ec is None:
+                live.extend(ids)
+            else:
+                counts["invalid"] += 1
+        elif r < 0.8:
+            if live and rng.random() < 0.85:
+                k = int(rng.integers(1, min(4, len(live)) + 1))
+                pick = sorted(rng.choice(len(live), size=k, replace=False).tolist(), reverse=True)
+                ids = [live[i] for i in pick]
+                if rng.random() < 0.15:
+                    ids = ids + ids[:1]               # may be a double free
+            else:
+                ids = [int(rng.integers(0, nb))]
+            _, _, ec, eo = _both(lambda: c.free(ids), lambda: o.free(ids))
+            assert ec == eo
+            if ec is None:
+                for i in ids:
+                    live.remove(i)
+            elif ec is pkv.DoubleFree:
+                counts["double_free"] += 1
+        else:
+            bs = int(rng.integers(1, 6))
+            row = [live[int(i)] for i in rng.integers(0, len(live), size=3)] if live else [0, 1, 2]
+            start = int(rng.integers(0, 3 * bs))
+            n = int(rng.integers(0, 3 * bs - start + 2))
+            rc_, ro_, ec, eo = _both(lambda: c.slots(row, start, n, bs).tolist(),
+                                     lambda: o.slots(row, start, n, bs))
+            assert ec == eo and (ec is not None or rc_ == ro_)
+            if ec is pkv.SharedWrite:
+                counts["shared_write"] += 1
+        _books_equal(c, o)
+    assert min(counts.values()) > 10, counts
+
+
+def test_fresh_pool_order_and_lifo():
+    c = pkv.BlockAllocator(5)
+    assert c.allocate(3) == [0, 1, 2]
+    c.free([2, 0])
+    assert c.allocate(2) == [0, 2]
+    assert c.snapshot() == ([4, 3], [1, 1, 1, 0, 0])
+
+
+def test_exhaustion_is_all_or_nothing():
+    c = pkv.BlockAllocator(3)
+    c.allocate(2)
+    before = c.snapshot()
+    with pytest.raises(pkv.PoolExhausted):
+        c.allocate(2)
+    assert c.snapshot() == before
+
+
+def test_slot_mapping_refuses_shared_blocks_and_writes_nothing():
+    c = pkv.BlockAllocator(6)
+    row = c.allocate(3)
+    out = c.slots(row, 2, 6, 4)
+    assert out.tolist() == [row[0] * 4 + 2, row[0] * 4 + 3] + [row[1] * 4 + i for i in range(4)]
+    c.incref([row[1]])
+    with pytest.raises(pkv.SharedWrite):
+        c.slots(row, 3, 2, 4)
+    with pytest.raises(pkv.InvalidArgument):
+        c.slots(row, 10, 3, 4)            # past the table
+    assert c.slots(row, 8, 4, 4).tolist() == [row[2] * 4 + i for i in range(4)]
+
+
+def test_validate_slots():
+    pkv.validate_slots([0, 5, -1, 7, -1], 8)
+    with pytest.raises(pkv.InvalidArgument):
+        pkv.validate_slots([0, 5, 5], 8)
+    with pytest.raises(pkv.InvalidArgument):
+        pkv.validate_slots([0, 8], 8)
+
+
+def _attn(**kw):
+    """Raw pkv_attention call with fake device pointers: only validation may run."""
+    lib = pkv.lib()
+    a = dict(q=1, k=1, v=1, bt=1, mb=8, ctx=[5, 9], cu=[0, 1, 3], T=3, hq=8, hkv=2, d=128,
+             bs=16, nb=4, scale=0.1, split=512, dt=L.PKV_BF16, out=1, ws=1, wsb=1 << 30)
+    a.update(kw)
+    ctx = np.asarray(a["ctx"], np.int32)
+    cu = np.asarray(a["cu"], np.int32)
+    return lib.pkv_attention(a["q"], a["k"], a["v"], a["bt"], a["mb"], L._ptr(ctx), L._ptr(cu),
+                             ctx.size, a["T"], a["hq"], a["hkv"], a["d"], a["bs"], a["nb"],
+                             a["scale"], a["split"], a["dt"], a["out"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hq=6, hkv=4), L.PKV_ERR_INVALID),                 # Hq % Hkv != 0
+    (dict(d=96), L.PKV_ERR_UNSUPPORTED),                    # head_dim
+    (dict(hq=24, hkv=2), L.PKV_ERR_UNSUPPORTED),            # group 12
+    (dict(split=100), L.PKV_ERR_INVALID),                   # split not a multiple of 64
+    (dict(ctx=[5, 1], cu=[0, 1, 3]), L.PKV_ERR_INVALID),    # q_len > ctx
+    (dict(cu=[0, 2, 1], T=1), L.PKV_ERR_INVALID),           # cu decreasing
+    (dict(cu=[1, 2, 3]), L.PKV_ERR_INVALID),                # cu[0] != 0
+    (dict(T=4), L.PKV_ERR_INVALID),                         # cu[B] != T
+    (dict(ctx=[5, 200]), L.PKV_ERR_INVALID),                # ctx > max_blocks * block_size
+    (dict(wsb=16), L.PKV_ERR_INVALID),                      # workspace too small
+    (dict(q=0), L.PKV_ERR_INVALID),                         # NULL q
+    (dict(dt=7), L.PKV_ERR_INVALID),                        # dtype
+    (dict(scale=float("nan")), L.PKV_ERR_INVALID),
+])
+def test_attention_validation_refuses_before_any_launch(kw, status):
+    assert _attn(**kw) == status
+    assert pkv.lib().pkv_last_error() != b""
+
+
+def test_attention_empty_step_is_a_no_op():
+    assert _attn(ctx=[], cu=[0], T=0) == L.PKV_OK
+    assert _attn(ctx=[4, 4], cu=[0, 0, 0], T=0) == L.PKV_OK
+
+
+def test_workspace_size_counts_splits():
+    # decode rows: ctx 512 -> 1 split (direct, no partials); ctx 513 -> 2 splits (+ partials)
+    a = pkv.attention_workspace_size([512], [0, 1], 8, 2, 128, 512)
+    b = pkv.attention_workspace_size([513], [0, 1], 8, 2, 128, 512)
+    assert b > a > 0
+    # partials: 2 splits x 8 heads x (128 + 2) floats, at least
+    assert b - a >= 2 * 8 * 130 * 4
+    with pytest.raises(pkv.Unsupported):
+        pkv.attention_workspace_size([5], [0, 1], 8, 2, 96, 512)
+
+
+def test_write_kv_validation():
+    lib = pkv.lib()
+    assert lib.pkv_write_kv(1, 1, 1, 4, 1, 1, 4, 16, 2, 128, 9, None) == L.PKV_ERR_INVALID
+    assert lib.pkv_write_kv(1, 1, 1, -1, 1, 1, 4, 16, 2, 128, 1, None) == L.PKV_ERR_INVALID
+    assert lib.pkv_write_kv(0, 1, 1, 4, 1, 1, 4, 16, 2, 128, 1, None) == L.PKV_ERR_INVALID
+    assert lib.pkv_write_kv(1, 1, 1, 0, 1, 1, 4, 16, 2, 128, 1, None) == L.PKV_OK
+    assert lib.pkv_write_kv(1, 1, 1, 4, 1, 1, 4, 16, 1, 4, 1, None) == L.PKV_ERR_UNSUPPORTED

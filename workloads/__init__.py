@@ -41,9 +41,12 @@ def round_f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
     bits = x.view(np.uint32)
-    lsb = (bits >> np.uint32(16)) & np.uint32(1)
-    rounded = (bits + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
-    out = rounded.astype(np.uint16)
+    r = bits >> np.uint32(16)
+    r &= np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += bits
+    r >>= np.uint32(16)
+    out = r.astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
         out[nan] = np.uint16(0x7FC0)
@@ -178,6 +181,22 @@ class Workload:
             self._prefix_cache[g] = self._draw(self._stream("group", g), npre)
         pk, pv = self._prefix_cache[g]
         return np.concatenate([pk, tail_k]), np.concatenate([pv, tail_v])
+
+    def iter_kv(self, seqs=None, workers: int = 8):
+        """Yield (b, k, v) for the given sequences (default all) in order, drawn in threads."""
+        from concurrent.futures import ThreadPoolExecutor
+        seqs = list(range(self.B)) if seqs is None else [int(b) for b in seqs]
+        for g in sorted(set(int(self.group_of[b]) for b in seqs if self.prefix_tokens[b] > 0)):
+            if g not in self._prefix_cache:
+                b0 = next(b for b in seqs if self.group_of[b] == g)
+                self.kv(b0)
+        if workers <= 1 or len(seqs) <= 1:
+            for b in seqs:
+                yield (b,) + self.kv(b)
+            return
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            for b, (k, v) in zip(seqs, ex.map(self.kv, seqs)):
+                yield b, k, v
 
     def prior_len(self, b: int) -> int:
         return int(self.ctx_lens[b] - self.q_lens[b])
