@@ -39,7 +39,23 @@ def _parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run plain 1 GiB device copies (scale reference for PMC byte "
+                         "counters) and exit")
     return ap.parse_args()
+
+
+def copy_calibration(reps=5, nbytes=1 << 30):
+    """Plain device-to-device copies of known size: FETCH_SIZE / WRITE_SIZE per copy dispatch
+    over nbytes gives the factor that turns those counters into HBM bytes."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_per_copy": nbytes, "reps": reps,
+                                           "kib_per_copy": nbytes / 1024}}))
 
 
 def _step_inputs(w, gst):
@@ -195,6 +211,9 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     pkv.lib()   # fail loudly if the HIP library is not built
 
     main_res = time_workload(args.workload, args.steps, args.warmup)

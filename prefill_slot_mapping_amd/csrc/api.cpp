@@ -368,10 +368,13 @@ extern "C" int32_t pkv_attention(const void* q, const void* k_cache, const void*
     p.k_cache = k_cache;
     p.v_cache = v_cache;
     p.block_tables = block_tables_dev;
-    p.ctx_lens = nullptr;
     p.max_blocks = max_blocks;
     p.block_size = block_size;
+    p.bs_log2 = -1;
+    for (int sh = 0; sh < 31; ++sh)
+      if ((1 << sh) == block_size) p.bs_log2 = sh;
     p.num_blocks = num_blocks;
+    p.n_items = static_cast<int32_t>(L.n_prefill);
     p.hq = num_q_heads;
     p.hkv = num_kv_heads;
     p.scale_log2e = scale_log2e;

@@ -53,12 +53,13 @@ struct PrefillArgs {
   const void* k_cache;
   const void* v_cache;
   const int32_t* block_tables;
-  const int32_t* ctx_lens;  // unused by the kernel; kept for bounds in debug builds
   int32_t max_blocks;
   int32_t block_size;
+  int32_t bs_log2;  // log2(block_size) when it is a power of two, else -1
   int32_t num_blocks;
   int32_t hq;
   int32_t hkv;
+  int32_t n_items;
   float scale_log2e;
   const PrefillItem* items;
   float* out;

@@ -20,6 +20,7 @@
 
 #include <cstdint>
 
+#include "device_common.h"
 #include "kernels.h"
 
 namespace pkv {
@@ -29,16 +30,6 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // ---------------------------------------------------------------------------------------
 // small device helpers
 // ---------------------------------------------------------------------------------------
-
-// The dispatcher sends workgroup b to XCD b % 8. Remap so that each XCD receives a contiguous
-// range of work items (neighbouring items share blocks and cache lines).
-__device__ __forceinline__ int xcd_remap(int b, int n) {
-  const int q = n >> 3, r = n & 7;
-  const int x = b & 7, k = b >> 3;
-  return x * q + (x < r ? x : r) + k;
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll

@@ -128,6 +128,38 @@ def test_group_and_full_batch_bitwise_for_prefix_sharing():
         assert np.array_equal(out.cpu().numpy(), full[rows])
 
 
+@pytest.mark.parametrize("dims", [(32, 8, 128, 16), (16, 2, 128, 32), (8, 8, 64, 16),
+                                  (16, 2, 64, 5)])
+def test_prefill_rechunking_is_bitwise_invisible(dims):
+    """A segment's rows give the same bits as one chunk, as several chunks (each over the cache
+    as it stands after it), and as chunks batched together with strangers."""
+    hq, hkv, d, bs = dims
+    w = make_workload(explicit_spec(f"rechunk-{hq}-{hkv}-{d}-{bs}", "bf16", hq, hkv, d, bs,
+                                    [(700, 300), (90, 2), (300, 1)]))
+    gst = _harness()(w, device=DEV)
+    full = gst.attention().cpu().numpy().copy()
+    rows = full[0:300]
+    bt = gst.block_tables_dev[0:1].contiguous()
+    got = []
+    for lo, hi in [(0, 37), (37, 101), (101, 102), (102, 103), (103, 300)]:
+        if hi - lo == 1:
+            continue                        # a 1-row segment is a decode row: another kind
+        out = pkv.attention(gst.q[lo:hi].contiguous(), gst.k_cache, gst.v_cache, bt,
+                            [400 + hi], [0, hi - lo], w.scale)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), rows[lo:hi]), (lo, hi)
+    # two chunks of the same sequence as two segments of one step, next to a stranger
+    q2 = torch.cat([gst.q[0:37], gst.q[300:302], gst.q[37:300]]).contiguous()
+    bt2 = torch.cat([bt, gst.block_tables_dev[1:2], bt]).contiguous()
+    out = pkv.attention(q2, gst.k_cache, gst.v_cache, bt2, [437, 90, 700], [0, 37, 39, 302],
+                        w.scale)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.array_equal(o[0:37], rows[0:37])
+    assert np.array_equal(o[39:302], rows[37:300])
+    assert np.array_equal(o[37:39], full[300:302])
+
+
 def test_physical_block_permutation_is_bitwise_invisible():
     w = make_workload(SMALL_CONFIGS["mixed-ragged-step"])
     gst = _harness()(w, device=DEV)
