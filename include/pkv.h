@@ -153,8 +153,8 @@ int32_t pkv_write_kv(const void* k_new, const void* v_new, const int32_t* slots_
  *                  planner. Need cu[0] == 0, cu non-decreasing, cu[B] == T,
  *                  0 <= q_len <= ctx_len <= max_blocks * block_size.
  *   head_dim:      64 or 128. num_q_heads / num_kv_heads in {1, 2, 4, 8}.
- *   kv_split:      positive multiple of 64 (512 is the default contract; part of the numeric
- *                  contract, so keep it fixed for bitwise comparisons).
+ *   kv_split:      positive multiple of 64, at most 2048 (512 is the default; part of the
+ *                  numeric contract, so keep it fixed for bitwise comparisons).
  *   out:           device float32 [T, num_q_heads, head_dim].
  *   workspace:     device buffer of at least pkv_attention_workspace_size() bytes, owned by
  *                  the caller, not read by the caller; it must stay untouched until the

@@ -15,7 +15,8 @@ from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+LIB_PATH = os.environ.get("PKV_LIB_PATH") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                            "include", "pkv.h")
 

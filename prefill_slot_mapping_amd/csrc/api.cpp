@@ -9,6 +9,7 @@
 // segment, so a row's work (and bits) never depend on the rest of the step.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -182,7 +183,15 @@ void build_lists(const StepShape& s, const pkv::WorkspaceLayout& L, char* host) 
       for (int32_t sp = 0; sp < ns; ++sp) dec[nd++] = pkv::DecodeItem{row, b, n_keys, sp, pbase, 0, 0, 0};
     }
   }
+  // longest work first: short tail items then fill the gaps at the end of the launch (item
+  // order never affects any row's bits)
+  std::stable_sort(dec, dec + nd, [&](const pkv::DecodeItem& x, const pkv::DecodeItem& y) {
+    const int64_t kx = std::min<int64_t>(x.n_keys - static_cast<int64_t>(x.split) * s.kv_split, s.kv_split);
+    const int64_t ky = std::min<int64_t>(y.n_keys - static_cast<int64_t>(y.split) * s.kv_split, s.kv_split);
+    return kx > ky;
+  });
 }
+
 
 int32_t check_step(const int32_t* ctx, const int32_t* cu, int32_t B, int32_t T,
                    int64_t max_keys) {
@@ -213,8 +222,8 @@ int32_t check_heads(int32_t hq, int32_t hkv, int32_t head_dim, int32_t kv_split,
   if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID, "dtype must be PKV_F32 or PKV_BF16");
   if (hq <= 0 || hkv <= 0) return fail(PKV_ERR_INVALID, "head counts must be positive");
   if (hq % hkv != 0) return fail(PKV_ERR_INVALID, "num_q_heads must be a multiple of num_kv_heads");
-  if (kv_split <= 0 || kv_split % pkv::kDecodeTile != 0)
-    return fail(PKV_ERR_INVALID, "kv_split must be a positive multiple of 64");
+  if (kv_split <= 0 || kv_split % pkv::kDecodeTile != 0 || kv_split > pkv::kMaxDecodeSplit)
+    return fail(PKV_ERR_INVALID, "kv_split must be a positive multiple of 64, at most 2048");
   if (!pkv::decode_supported(head_dim, hq / hkv))
     return fail(PKV_ERR_UNSUPPORTED, "head_dim must be 64 or 128 and num_q_heads / num_kv_heads "
                                      "one of 1, 2, 4, 8");
@@ -316,7 +325,7 @@ extern "C" int32_t pkv_attention(const void* q, const void* k_cache, const void*
   if (workspace_bytes < L.total || (L.total > 0 && workspace == nullptr))
     return fail(PKV_ERR_INVALID, "attention: workspace smaller than pkv_attention_workspace_size (" +
                                      std::to_string(L.total) + " bytes)");
-  if (L.n_decode * num_kv_heads > INT32_MAX || L.n_prefill * num_kv_heads > INT32_MAX)
+  if (L.n_decode * num_q_heads > INT32_MAX || L.n_prefill * num_kv_heads > INT32_MAX)
     return fail(PKV_ERR_UNSUPPORTED, "attention: step too large for one launch");
 
   hipStream_t strm = static_cast<hipStream_t>(stream);
@@ -357,6 +366,9 @@ extern "C" int32_t pkv_attention(const void* q, const void* k_cache, const void*
   }
 
   const float scale_log2e = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  int32_t bs_log2 = -1;
+  for (int sh = 0; sh < 31; ++sh)
+    if ((1 << sh) == block_size) bs_log2 = sh;
   const int group = num_q_heads / num_kv_heads;
   float* part_m = reinterpret_cast<float*>(ws + L.part_m_off);
   float* part_l = reinterpret_cast<float*>(ws + L.part_l_off);
@@ -370,9 +382,7 @@ extern "C" int32_t pkv_attention(const void* q, const void* k_cache, const void*
     p.block_tables = block_tables_dev;
     p.max_blocks = max_blocks;
     p.block_size = block_size;
-    p.bs_log2 = -1;
-    for (int sh = 0; sh < 31; ++sh)
-      if ((1 << sh) == block_size) p.bs_log2 = sh;
+    p.bs_log2 = bs_log2;
     p.num_blocks = num_blocks;
     p.n_items = static_cast<int32_t>(L.n_prefill);
     p.hq = num_q_heads;
@@ -393,12 +403,14 @@ extern "C" int32_t pkv_attention(const void* q, const void* k_cache, const void*
     d.block_tables = block_tables_dev;
     d.max_blocks = max_blocks;
     d.block_size = block_size;
+    d.bs_log2 = bs_log2;
     d.num_blocks = num_blocks;
     d.hq = num_q_heads;
     d.hkv = num_kv_heads;
     d.kv_split = kv_split;
     d.scale_log2e = scale_log2e;
     d.items = reinterpret_cast<const pkv::DecodeItem*>(ws + L.decode_off);
+    d.group = group;
     d.out = out;
     d.part_m = part_m;
     d.part_l = part_l;

@@ -27,9 +27,11 @@ struct DecodeArgs {
   const int32_t* block_tables;
   int32_t max_blocks;
   int32_t block_size;
+  int32_t bs_log2;  // log2(block_size) when it is a power of two, else -1
   int32_t num_blocks;
   int32_t hq;
   int32_t hkv;
+  int32_t group;      // hq / hkv
   int32_t kv_split;
   float scale_log2e;  // softmax scale times log2(e): scores live in the base-2 domain
   const DecodeItem* items;

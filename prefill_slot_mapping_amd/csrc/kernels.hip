@@ -43,6 +43,32 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// K/V rows are streamed once: nontemporal loads
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+// value of lane ^ 1 (DPP quad permutation [1, 0, 3, 2])
+__device__ __forceinline__ float dpp_xor1(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+
+// max over a wave whose lanes hold values in equal pairs (lane 2k == lane 2k+1)
+__device__ __forceinline__ float wave_max_pairs(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF,
+                                                           false)));   // lane ^ 2
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF,
+                                                           false)));   // half-row mirror
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF,
+                                                           false)));   // row mirror
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
@@ -88,54 +114,84 @@ hipError_t launch_write_kv(const WriteArgs& a, hipStream_t stream) {
 //
 // Workgroup = 4 waves = one (query row, split, kv head) item; it serves the G query heads that
 // read that kv head, so every K/V byte of the split is loaded from HBM once.
-// Per 64-key tile a wave
-//   1. loads K and V rows with 16-byte coalesced loads (LPT lanes cover one 256/512-byte head
-//      row; the block table is read once per key, the slot broadcast by a lane shuffle),
-//   2. stages K in LDS with an XOR swizzle on the 16-byte chunk index,
-//   3. computes the G scores of one key per lane (no cross-lane reduction),
-//   4. updates the per-head running max / sum and publishes p through LDS,
-//   5. accumulates P.V in the split-D layout (each lane owns EPL columns of its key group).
+// Prologue: the split's slots (one block-table read per key) and the G query rows go to LDS.
+// The split is cut into 32-key half tiles aligned at the split start; half tile j belongs to
+// wave j % 4. Each wave double-buffers its half tiles in registers: the loads of the next
+// half tile are in flight while the current one is computed. Per half tile a wave
+//   1. has loaded K and V rows with coalesced 16-byte nontemporal loads (LPT lanes cover one
+//      head row; keys past the split end re-read the last key, whose p is 0),
+//   2. stages K in LDS (XOR swizzle on 16-byte chunks) and computes the scores with two lanes
+//      per key (each covers half of D; one DPP exchange completes the dot product),
+//   3. updates the per-head running max (wave-uniform) and publishes p through LDS,
+//   4. accumulates P.V in the split-D layout (each lane owns EPL columns of its key group).
 // ---------------------------------------------------------------------------------------
 template <int D, int G, bool BF>
 __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
+  // G = query heads served by one work item: all heads of a kv head when the group has at
+  // most 4 of them, else 4 consecutive heads (two items of a larger group share a kv head and
+  // read its K/V through the same XCD's L2)
   constexpr int E = BF ? 2 : 4;
   constexpr int ROWB = D * E;               // bytes of one head row
   constexpr int LPT = ROWB / 16;            // lanes per key row
   constexpr int TPI = 64 / LPT;             // keys per load instruction
-  constexpr int NI = kDecodeTile / TPI;     // load instructions per tile
+  constexpr int HT = kDecodeTile / 2;       // keys per half tile
+  constexpr int NI = HT / TPI;              // load instructions per half tile and tensor
   constexpr int EPL = 16 / E;               // elements per lane chunk
-  static_assert(LPT >= 1 && LPT <= 64 && (LPT & (LPT - 1)) == 0, "row must be 16..1024 bytes");
+  constexpr int CPH = LPT / 2;              // chunks per lane in the score stage
+  static_assert(LPT >= 2 && LPT <= 32 && (LPT & (LPT - 1)) == 0 && HT % TPI == 0, "shape");
 
-  __shared__ uint4 s_k[kDecodeWaves][kDecodeTile * LPT];
-  __shared__ float s_p[kDecodeWaves][kDecodeTile * G];
+  __shared__ uint4 s_k[kDecodeWaves][HT * LPT];
+  __shared__ float s_p[kDecodeWaves][HT * G];
   __shared__ uint4 s_q[G * LPT];
-  __shared__ int s_bad;
+  __shared__ int s_slot[kMaxDecodeSplit];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int f = xcd_remap(blockIdx.x, gridDim.x);
-  const int item_idx = f / a.hkv;
-  const int g = f - item_idx * a.hkv;
+  const int subs = a.hq / G;                 // work items per (row, split)
+  const int item_idx = f / subs;
+  const int hq0 = (f - item_idx * subs) * G; // first query head of this work item
+  const int g = hq0 / a.group;               // the kv head those heads read
   const DecodeItem it = a.items[item_idx];
-
-  // the G query heads of this kv head are contiguous in q[row]
-  const uint4* qsrc = reinterpret_cast<const uint4*>(
-      static_cast<const char*>(a.q) + (static_cast<int64_t>(it.row) * a.hq +
-                                       static_cast<int64_t>(g) * G) * ROWB);
-  for (int c = tid; c < G * LPT; c += 256) s_q[c] = qsrc[c];
-  if (tid == 0) s_bad = 0;
-  __syncthreads();
 
   const int t0 = it.split * a.kv_split;
   const int t1 = min(it.n_keys, t0 + a.kv_split);
   const int32_t* bt = a.block_tables + static_cast<int64_t>(it.seq) * a.max_blocks;
+  bool bad = false;
+
+  // an out-of-pool block id marks the item bad and is replaced by slot 0, so no load ever
+  // leaves the pool
+  for (int k = tid; k < t1 - t0; k += 256) {
+    const int pos = t0 + k;
+    int j, off;
+    if (a.bs_log2 >= 0) {
+      j = pos >> a.bs_log2;
+      off = pos & (a.block_size - 1);
+    } else {
+      j = pos / a.block_size;
+      off = pos - j * a.block_size;
+    }
+    const int b = bt[j];
+    const bool ok = static_cast<unsigned>(b) < static_cast<unsigned>(a.num_blocks);
+    bad |= !ok;
+    s_slot[k] = ok ? b * a.block_size + off : 0;
+  }
+  const uint4* qsrc = reinterpret_cast<const uint4*>(
+      static_cast<const char*>(a.q) + (static_cast<int64_t>(it.row) * a.hq + hq0) * ROWB);
+  for (int c = tid; c < G * LPT; c += 256) s_q[c] = qsrc[c];
+  __syncthreads();
+
   const uint4* __restrict__ kp = static_cast<const uint4*>(a.k_cache);
   const uint4* __restrict__ vp = static_cast<const uint4*>(a.v_cache);
   const int64_t slot_stride = static_cast<int64_t>(a.hkv) * LPT;  // uint4 per slot
   const int head_off = g * LPT;
-  const int grp = lane / LPT;
-  const int cl = lane & (LPT - 1);
+  const int grp = lane / LPT;               // P.V stage / loads: key group of this lane
+  const int cl = lane & (LPT - 1);          // P.V stage / loads: chunk of this lane
+  const int kk = lane >> 1;                 // score stage: key of this lane
+  const int hf = lane & 1;                  // score stage: half of D of this lane
+  uint4* sk = s_k[wave];
+  float* sp = s_p[wave];
 
   float m[G], l[G], acc[G][EPL];
 #pragma unroll
@@ -145,95 +201,81 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
-  bool bad = false;
-  uint4* sk = s_k[wave];
-  float* sp = s_p[wave];
 
-  for (int ts = t0 + wave * kDecodeTile; ts < t1; ts += kDecodeWaves * kDecodeTile) {
-    const int n = min(kDecodeTile, t1 - ts);
-    // slot of this lane's key (key ts + lane)
-    int slot_l = 0;
-    int ok_l = 0;
-    if (lane < n) {
-      const int pos = ts + lane;
-      const int j = pos / a.block_size;
-      const int off = pos - j * a.block_size;
-      const int b = bt[j];
-      ok_l = static_cast<unsigned>(b) < static_cast<unsigned>(a.num_blocks);
-      bad |= !ok_l;
-      slot_l = ok_l ? b * a.block_size + off : 0;
-    }
-    uint4 kr[NI], vr[NI];
+  auto load = [&](uint4 (&kr)[NI], uint4 (&vr)[NI], int hs) {
+    const int n = min(HT, t1 - hs);
+    const int* slots = s_slot + (hs - t0);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int tok = i * TPI + grp;
-      const int sl = __shfl(slot_l, tok);
-      const int okk = __shfl(ok_l, tok);
-      if (okk) {
-        const int64_t off = static_cast<int64_t>(sl) * slot_stride + head_off + cl;
-        kr[i] = kp[off];
-        vr[i] = vp[off];
-      } else {
-        kr[i] = make_uint4(0u, 0u, 0u, 0u);
-        vr[i] = make_uint4(0u, 0u, 0u, 0u);
-      }
+      const int tok = min(i * TPI + grp, n - 1);
+      const int64_t off = static_cast<int64_t>(slots[tok]) * slot_stride + head_off + cl;
+      kr[i] = load_nt(kp + off);
+      vr[i] = load_nt(vp + off);
     }
+  };
+
+  auto compute = [&](const uint4 (&kr)[NI], const uint4 (&vr)[NI], int hs) {
+    const int n = min(HT, t1 - hs);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int tok = i * TPI + grp;
       sk[tok * LPT + (cl ^ (tok & (LPT - 1)))] = kr[i];
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // scores: lane = key
+    // scores: lanes 2k and 2k+1 hold halves of key k's dot products
     float s[G];
-    {
-      float s0[G], s1[G];
 #pragma unroll
-      for (int h = 0; h < G; ++h) s0[h] = s1[h] = 0.f;
+    for (int h = 0; h < G; ++h) s[h] = 0.f;
 #pragma unroll
-      for (int cc = 0; cc < LPT; ++cc) {
-        const uint4 kc = sk[lane * LPT + (cc ^ (lane & (LPT - 1)))];
+    for (int u = 0; u < CPH; ++u) {
+      const int c = hf * CPH + u;
+      const uint4 kc = sk[kk * LPT + (c ^ (kk & (LPT - 1)))];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const uint4 qc = s_q[h * LPT + cc];
-          if constexpr (BF) {
-            s0[h] = dot2_bf16(qc.x, kc.x, s0[h]);
-            s1[h] = dot2_bf16(qc.y, kc.y, s1[h]);
-            s0[h] = dot2_bf16(qc.z, kc.z, s0[h]);
-            s1[h] = dot2_bf16(qc.w, kc.w, s1[h]);
-          } else {
-            s0[h] = fmaf(__uint_as_float(qc.x), __uint_as_float(kc.x), s0[h]);
-            s1[h] = fmaf(__uint_as_float(qc.y), __uint_as_float(kc.y), s1[h]);
-            s0[h] = fmaf(__uint_as_float(qc.z), __uint_as_float(kc.z), s0[h]);
-            s1[h] = fmaf(__uint_as_float(qc.w), __uint_as_float(kc.w), s1[h]);
-          }
+      for (int h = 0; h < G; ++h) {
+        const uint4 qc = s_q[h * LPT + c];
+        if constexpr (BF) {
+          float t = dot2_bf16(qc.x, kc.x, 0.f);
+          t = dot2_bf16(qc.y, kc.y, t);
+          t = dot2_bf16(qc.z, kc.z, t);
+          t = dot2_bf16(qc.w, kc.w, t);
+          s[h] += t;
+        } else {
+          float t = __uint_as_float(qc.x) * __uint_as_float(kc.x);
+          t = fmaf(__uint_as_float(qc.y), __uint_as_float(kc.y), t);
+          t = fmaf(__uint_as_float(qc.z), __uint_as_float(kc.z), t);
+          t = fmaf(__uint_as_float(qc.w), __uint_as_float(kc.w), t);
+          s[h] += t;
         }
       }
-#pragma unroll
-      for (int h = 0; h < G; ++h) s[h] = ok_l ? (s0[h] + s1[h]) * a.scale_log2e : -INFINITY;
     }
-
-    // online softmax update (per head, wave-uniform max)
+    const bool valid = kk < n;
+    bool moved = false;
+    float alpha[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float tmax = wave_max(s[h]);
-      const float mn = fmaxf(m[h], tmax);
-      const float alpha = fast_exp2(m[h] - mn);
-      const float p = fast_exp2(s[h] - mn);
-      l[h] = l[h] * alpha + p;
-      sp[lane * G + h] = p;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+      s[h] += dpp_xor1(s[h]);
+      s[h] = valid ? s[h] * a.scale_log2e : -INFINITY;
+      const float mn = fmaxf(m[h], wave_max_pairs(s[h]));
+      alpha[h] = fast_exp2(m[h] - mn);
+      moved |= alpha[h] != 1.f;
       m[h] = mn;
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // P.V, split-D layout: this lane owns columns cl*EPL .. cl*EPL+EPL-1 of keys i*TPI+grp
+    // p of (key kk, head h) is formed by the lane of that key with hf == h % 2
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      if ((h & 1) == hf) {
+        const float p = fast_exp2(s[h] - m[h]);
+        l[h] = l[h] * alpha[h] + p;
+        sp[kk * G + h] = p;
+      }
+    }
+    // rescale only when some head's max moved (multiplying by exactly 1 changes nothing)
+    if (__any(moved)) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha[h];
+    }
+    // P.V, split-D layout: this lane owns columns cl*EPL .. +EPL of keys i*TPI + grp
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int tok = i * TPI + grp;
@@ -255,7 +297,22 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pp[h], vf[e], acc[h][e]);
     }
-    __builtin_amdgcn_wave_barrier();
+  };
+
+  // this wave's half tiles: hs = t0 + HT * (wave + 4 j), j = 0, 1, ...
+  constexpr int kStep = kDecodeWaves * HT;
+  uint4 ka[NI], va[NI], kb[NI], vb[NI];
+  int hs = t0 + wave * HT;
+  if (hs < t1) load(ka, va, hs);
+  while (hs < t1) {
+    const int hs1 = hs + kStep;
+    if (hs1 < t1) load(kb, vb, hs1);
+    compute(ka, va, hs);
+    if (hs1 >= t1) break;
+    const int hs2 = hs1 + kStep;
+    if (hs2 < t1) load(ka, va, hs2);
+    compute(kb, vb, hs1);
+    hs = hs2;
   }
 
   // wave totals: l over keys (lanes), acc over the TPI key groups
@@ -268,11 +325,11 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], k);
 
-  if (bad) s_bad = 1;
-  __syncthreads();  // every wave is done with its K tiles: reuse s_k as merge scratch
+  const bool bad_row = __syncthreads_or(bad) != 0;  // also: every wave is done with s_k
   float* mg_acc = reinterpret_cast<float*>(&s_k[0][0]);      // [4][G][D]
   float* mg_m = mg_acc + kDecodeWaves * G * D;                // [4][G]
   float* mg_l = mg_m + kDecodeWaves * G;                      // [4][G]
+  static_assert(sizeof(s_k) >= sizeof(float) * kDecodeWaves * G * (D + 2), "merge scratch");
   if (lane < LPT) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
@@ -287,7 +344,6 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
     }
   }
   __syncthreads();
-  const bool bad_row = s_bad != 0;
   for (int idx = tid; idx < G * D; idx += 256) {
     const int h = idx / D;
     const int d = idx - h * D;
@@ -302,7 +358,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
       den = fmaf(fw, mg_l[w * G + h], den);
     }
     if (bad_row) num = den = __builtin_nanf("");
-    const int hq = g * G + h;
+    const int hq = hq0 + h;
     if (it.part < 0) {
       a.out[(static_cast<int64_t>(it.row) * a.hq + hq) * D + d] = num / den;
     } else {
@@ -348,14 +404,16 @@ bool decode_supported(int head_dim, int group) {
          (group == 1 || group == 2 || group == 4 || group == 8);
 }
 
+// query heads per decode work item
+static int decode_heads_per_item(int group) { return group < 4 ? group : 4; }
+
 template <int D, bool BF>
-static hipError_t launch_decode_d(const DecodeArgs& a, uint32_t grid, int group,
+static hipError_t launch_decode_d(const DecodeArgs& a, uint32_t grid, int gi,
                                   hipStream_t stream) {
-  switch (group) {
+  switch (gi) {
     case 1: hipLaunchKernelGGL((decode_split_kernel<D, 1, BF>), dim3(grid), dim3(256), 0, stream, a); break;
     case 2: hipLaunchKernelGGL((decode_split_kernel<D, 2, BF>), dim3(grid), dim3(256), 0, stream, a); break;
     case 4: hipLaunchKernelGGL((decode_split_kernel<D, 4, BF>), dim3(grid), dim3(256), 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((decode_split_kernel<D, 8, BF>), dim3(grid), dim3(256), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -363,16 +421,17 @@ static hipError_t launch_decode_d(const DecodeArgs& a, uint32_t grid, int group,
 
 hipError_t launch_decode(const DecodeArgs& a, int64_t n_items, int head_dim, int group,
                          bool bf16, hipStream_t stream) {
-  const int64_t grid64 = n_items * a.hkv;
+  const int gi = decode_heads_per_item(group);
+  const int64_t grid64 = n_items * (a.hq / gi);
   if (grid64 == 0) return hipSuccess;
-  if (grid64 > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (grid64 > 0x7fffffffLL || a.group != group) return hipErrorInvalidValue;
   const uint32_t grid = static_cast<uint32_t>(grid64);
   if (head_dim == 64)
-    return bf16 ? launch_decode_d<64, true>(a, grid, group, stream)
-                : launch_decode_d<64, false>(a, grid, group, stream);
+    return bf16 ? launch_decode_d<64, true>(a, grid, gi, stream)
+                : launch_decode_d<64, false>(a, grid, gi, stream);
   if (head_dim == 128)
-    return bf16 ? launch_decode_d<128, true>(a, grid, group, stream)
-                : launch_decode_d<128, false>(a, grid, group, stream);
+    return bf16 ? launch_decode_d<128, true>(a, grid, gi, stream)
+                : launch_decode_d<128, false>(a, grid, gi, stream);
   return hipErrorInvalidValue;
 }
 

@@ -10,13 +10,16 @@ namespace pkv {
 constexpr int kDecodeTile = 64;
 // Waves per decode workgroup; tile i of a split is handled by wave i % kDecodeWaves.
 constexpr int kDecodeWaves = 4;
+// Largest kv_split the decode kernel stages slots for (one int per key of a split in LDS).
+constexpr int kMaxDecodeSplit = 2048;
 // Keys per prefill KV tile (tiles are aligned at absolute position 0).
 constexpr int kPrefillKeyTile = 64;
 // Query "M-rows" (query row x head pairs) per prefill workgroup: 4 waves x 32.
 constexpr int kPrefillMRows = 128;
 
 // One decode work item: split `split` of query row `row` (sequence `seq`), covering keys
-// [split * kv_split, min(n_keys, (split + 1) * kv_split)). The kernel grid runs items x Hkv.
+// [split * kv_split, min(n_keys, (split + 1) * kv_split)). The kernel grid runs each item once
+// per group of (at most 4) query heads.
 // part < 0: the row has one split and the kernel writes the final output; otherwise the
 // item writes partial slot (part + split) for its heads.
 struct DecodeItem {

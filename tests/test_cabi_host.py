@@ -172,6 +172,7 @@ def _attn(**kw):
     (dict(d=96), L.PKV_ERR_UNSUPPORTED),                    # head_dim
     (dict(hq=24, hkv=2), L.PKV_ERR_UNSUPPORTED),            # group 12
     (dict(split=100), L.PKV_ERR_INVALID),                   # split not a multiple of 64
+    (dict(split=2112), L.PKV_ERR_INVALID),                  # split above 2048
     (dict(ctx=[5, 1], cu=[0, 1, 3]), L.PKV_ERR_INVALID),    # q_len > ctx
     (dict(cu=[0, 2, 1], T=1), L.PKV_ERR_INVALID),           # cu decreasing
     (dict(cu=[1, 2, 3]), L.PKV_ERR_INVALID),                # cu[0] != 0
