@@ -17,6 +17,7 @@ Prints ONE JSON line (rank 0, N = 1). `--gpus N` with N > 1 exits: this build ru
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -105,13 +106,31 @@ def time_workload(name, steps, warmup, device="cuda:0"):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize(device)
+    # long-lived objects (torch, the workload) go to the permanent generation, as serving
+    # loops do after start-up, so a collection inside the loop does not walk all of them
+    gc.collect()
+    gc.freeze()
+    gc_pauses = []
+
+    def on_gc(phase, info, _t=[0.0]):
+        if phase == "start":
+            _t[0] = time.perf_counter()
+        else:
+            gc_pauses.append(time.perf_counter() - _t[0])
+
+    gc.callbacks.append(on_gc)
     pkv.profile_enable(True)
     torch.cuda.synchronize(device)
+    host_ends = []
     t0 = time.perf_counter()
     for _ in range(steps):
         step()
+        host_ends.append(time.perf_counter())
     torch.cuda.synchronize(device)
     dt = time.perf_counter() - t0
+    gc.callbacks.remove(on_gc)
+    gc.unfreeze()
+    host_ms = np.diff(np.array([t0] + host_ends)) * 1e3
     kern = {k: pkv.profile_read(k) for k in ("write_kv", "prefill", "decode", "merge")}
     pkv.profile_enable(False)
     assert np.array_equal(slots_np[:w.T], gst.new_slots)
@@ -127,6 +146,9 @@ def time_workload(name, steps, warmup, device="cuda:0"):
         "step_gbs": (kv + app) / (ms_step * 1e-3) / 1e9, "tokens_per_s": w.T / (ms_step * 1e-3),
         "kv_bytes": kv, "append_bytes": app, "decode_kv_bytes": dec_kv, "prefill_flops": flops,
         "build_s": t_build,
+        "host_enqueue_ms": {"median": float(np.median(host_ms)), "max": float(host_ms.max())},
+        "gc_pauses_in_timed_region": {"count": len(gc_pauses),
+                                      "max_ms": max(gc_pauses, default=0.0) * 1e3},
         "kernels_ms": {k: (v[0] / v[1] if v[1] else None) for k, v in kern.items()},
         "kernel_launches": {k: v[1] for k, v in kern.items()},
     }
@@ -146,11 +168,7 @@ def cpu_baseline(w, budget_s):
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         blas_threads = 1
-    rows_done = 0
-    kv_done = 0
-    spent = 0.0
     order = list(range(w.B))
-    sample = []
     # calibrate on the first sequence, then take as many as fit the budget
     per_token = None
     chosen = []
@@ -172,20 +190,29 @@ def cpu_baseline(w, budget_s):
             est += per_token * int(w.ctx_lens[b]) * int(w.q_lens[b])
     st = build_oracle_step(w, seqs=chosen, poison=False)
     rows = [r for b in chosen for r in range(int(w.cu_seqlens_q[b]), int(w.cu_seqlens_q[b + 1]))]
+    # repeat the sample until about `budget_s` of CPU work has been timed
+    reps = 0
     t = time.perf_counter()
-    st.attention(rows=rows)
-    spent = time.perf_counter() - t
+    while True:
+        st.attention(rows=rows)
+        reps += 1
+        spent = time.perf_counter() - t
+        if spent >= 0.66 * budget_s or spent / reps * (reps + 1) > budget_s:
+            break
     from prefill_slot_mapping_amd import accounting as acc
-    kv_done = acc.decode_kv_bytes(w.ctx_lens[chosen], w.spec.Hkv, w.spec.D, w.elem_bytes)
+    kv_done = reps * acc.decode_kv_bytes(w.ctx_lens[chosen], w.spec.Hkv, w.spec.D, w.elem_bytes)
     sample = f"{len(chosen)} of {w.B} sequences ({len(rows)} query rows, " \
-             f"{int(w.ctx_lens[chosen].sum())} cached tokens), float64 per-row oracle"
+             f"{int(w.ctx_lens[chosen].sum())} cached tokens) x {reps} passes, float64 " \
+             f"per-row oracle"
     return {"value": kv_done / spent / 1e9, "unit": "GB/s", "cores": int(blas_threads),
             "kind": "oracle", "sample": sample, "seconds": spent,
             "affinity_cores": len(os.sched_getaffinity(0))}
 
 
-def _traffic_for(kernel_file, launches_key):
-    """HBM bytes per launch from committed rocprofv3 PMC summaries, if the kernel is unchanged."""
+def _traffic_for(kernel_file, workload):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, each scaled by what the counter reads for a
+    plain copy of known size) from the committed rocprofv3 PMC summary, or None when the kernel
+    source has changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "decode_traffic.json")
     if not os.path.exists(path):
         return None
@@ -194,8 +221,8 @@ def _traffic_for(kernel_file, launches_key):
         src = open(os.path.join(ROOT, "prefill_slot_mapping_amd", "csrc", kernel_file), "rb").read()
         if rec.get("kernel_sha256") != hashlib.sha256(src).hexdigest():
             return None
-        return rec.get(launches_key)
-    except Exception:
+        return rec[workload]["hbm_bytes"]
+    except (OSError, KeyError, ValueError):
         return None
 
 
@@ -230,7 +257,7 @@ def main():
     roofline = {"bound": "hbm", "kernel": "decode_split_kernel", "achieved": achieved,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS if achieved else None,
-                "traffic": _traffic_for("kernels.hip", args.workload),
+                "traffic": _traffic_for("decode.hip", args.workload),
                 "bytes_per_launch": main_res["decode_kv_bytes"], "avg_launch_ms": dec_ms}
     cpu = None
     if not args.no_cpu_baseline:

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libpkv.so")
 ARCH = "gfx950"
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
-DEVICE_SOURCES = ["kernels.hip", "prefill.hip"]
+DEVICE_SOURCES = ["write_kv.hip", "decode.hip", "merge.hip", "prefill.hip"]
 HOST_SOURCES = ["allocator.cpp", "api.cpp"]
 
 # Packed-FP32 instructions are disabled for all device code: the compiler may not form

@@ -424,6 +424,7 @@ extern "C" int32_t pkv_attention(const void* q, const void* k_cache, const void*
     pkv::MergeArgs mg;
     mg.items = reinterpret_cast<const pkv::MergeItem*>(ws + L.merge_off);
     mg.hq = num_q_heads;
+    mg.n_waves = static_cast<int32_t>(L.n_merge * num_q_heads);
     mg.part_m = part_m;
     mg.part_l = part_l;
     mg.part_acc = part_acc;

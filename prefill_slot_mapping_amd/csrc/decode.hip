@@ -1,21 +1,18 @@
-// HIP kernels for gfx950 (MI355X): KV append, decode split pass, split merge.
+// Decode split pass for gfx950 (MI355X).
 //
-// Sources of the operations:
-//  - KV append: "P3: native paged-KV continuous-batching sampler", section "Design > paged.py"
-//    (PagedKVCache: copy-free append, a write scatters into (block, offset) in place).
-//  - Attention contract: same section, TritonPagedAttention (q, k/v cache blocks, block tables,
-//    cu_seqlens_q, ctx_lens, slot mapping; a fixed KV split per context length, no atomics),
-//    and "Finish RL Training Faster: Bitwise-Consistent ..." section 2 (kernel determinism,
-//    batch independence).
+// Sources of the operation: "P3: native paged-KV continuous-batching sampler", section
+// "Design > paged.py", TritonPagedAttention (q, k/v cache blocks, block tables, cu_seqlens_q,
+// ctx_lens; a fixed KV split per context length, no atomics), and "Finish RL Training Faster:
+// Bitwise-Consistent ..." section 2 (kernel determinism, batch independence).
 //
-// Numeric contract of the decode path (every choice below depends only on the row's own
-// sequence, never on the batch): the keys of a row are cut into splits of kv_split tokens
-// aligned at position 0; inside a split, 64-key tiles aligned at the split start go to wave
-// (tile % 4) of the workgroup; each wave runs an online softmax over its tiles in ascending
-// order, in the base-2 domain (scores are scaled by scale * log2 e and exponentiated with the
-// hardware exp2); the four wave partials are merged in wave order, and the split partials in
-// ascending split order by a second kernel. Accumulation is float32 throughout; bfloat16
-// products are formed exactly by v_dot2_f32_bf16; probabilities stay float32 for P.V.
+// Numeric contract (every choice depends only on the row's own sequence, never on the batch):
+// the keys of a row are cut into splits of kv_split tokens aligned at position 0; inside a
+// split, 32-key half tiles aligned at the split start go to wave (half tile % 4); each wave
+// runs an online softmax over its half tiles in ascending order in the base-2 domain (scores
+// scaled by scale * log2 e, hardware exp2); the four wave partials are merged in wave order and
+// the split partials in ascending split order (merge kernel). Accumulation is float32
+// throughout; bfloat16 products are formed exactly by v_dot2_f32_bf16; probabilities stay
+// float32 for P.V.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -24,90 +21,6 @@
 #include "kernels.h"
 
 namespace pkv {
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-// ---------------------------------------------------------------------------------------
-// small device helpers
-// ---------------------------------------------------------------------------------------
-
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int k = 32; k >= 1; k >>= 1) x = fmaxf(x, __shfl_xor(x, k));
-  return x;
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int k = 32; k >= 1; k >>= 1) x += __shfl_xor(x, k);
-  return x;
-}
-
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-
-// K/V rows are streamed once: nontemporal loads
-__device__ __forceinline__ uint4 load_nt(const uint4* p) {
-  const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-  return make_uint4(t.x, t.y, t.z, t.w);
-}
-
-// value of lane ^ 1 (DPP quad permutation [1, 0, 3, 2])
-__device__ __forceinline__ float dpp_xor1(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
-}
-
-// max over a wave whose lanes hold values in equal pairs (lane 2k == lane 2k+1)
-__device__ __forceinline__ float wave_max_pairs(float x) {
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF,
-                                                           false)));   // lane ^ 2
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF,
-                                                           false)));   // half-row mirror
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF,
-                                                           false)));   // row mirror
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
-}
-
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                         __builtin_bit_cast(bf16x2_t, b), c, false);
-}
-
-__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
-
-// ---------------------------------------------------------------------------------------
-// KV append: row t of k_new / v_new goes to slot slots[t]; a slot row is contiguous in the
-// [num_blocks, block_size, Hkv, D] pool at byte offset slot * Hkv * D * elem_bytes.
-// ---------------------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) write_kv_kernel(WriteArgs a) {
-  const uint4* __restrict__ kn = static_cast<const uint4*>(a.k_new);
-  const uint4* __restrict__ vn = static_cast<const uint4*>(a.v_new);
-  uint4* __restrict__ kc = static_cast<uint4*>(a.k_cache);
-  uint4* __restrict__ vc = static_cast<uint4*>(a.v_cache);
-  const uint32_t chunks = static_cast<uint32_t>(a.chunks_per_row);
-  const uint32_t total = static_cast<uint32_t>(a.n_rows) * chunks;
-  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < total; i += gridDim.x * 256u) {
-    const uint32_t row = i / chunks;
-    const uint32_t c = i - row * chunks;
-    const int32_t s = a.slots[row];
-    if (s < 0 || s >= a.n_slots) continue;
-    const int64_t dst = static_cast<int64_t>(s) * chunks + c;
-    kc[dst] = kn[i];
-    vc[dst] = vn[i];
-  }
-}
-
-hipError_t launch_write_kv(const WriteArgs& a, hipStream_t stream) {
-  const int64_t total = static_cast<int64_t>(a.n_rows) * a.chunks_per_row;
-  if (total == 0) return hipSuccess;
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(write_kv_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream,
-                     a);
-  return hipGetLastError();
-}
 
 // ---------------------------------------------------------------------------------------
 // Decode split pass.
@@ -373,31 +286,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Split merge: out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s, ascending s.
-// One workgroup of D threads per (row, query head).
-// ---------------------------------------------------------------------------------------
-template <int D>
-__global__ void __launch_bounds__(D) merge_kernel(MergeArgs a) {
-  const int b = blockIdx.x;
-  const int item = b / a.hq;
-  const int h = b - item * a.hq;
-  const int d = threadIdx.x;
-  const MergeItem it = a.items[item];
-  float M = -INFINITY;
-  for (int s = 0; s < it.n_splits; ++s)
-    M = fmaxf(M, a.part_m[static_cast<int64_t>(it.part + s) * a.hq + h]);
-  float num = 0.f, den = 0.f;
-  for (int s = 0; s < it.n_splits; ++s) {
-    const int64_t p = static_cast<int64_t>(it.part + s) * a.hq + h;
-    const float fw = fast_exp2(a.part_m[p] - M);
-    num = fmaf(fw, a.part_acc[p * D + d], num);
-    den = fmaf(fw, a.part_l[p], den);
-  }
-  a.out[(static_cast<int64_t>(it.row) * a.hq + h) * D + d] = num / den;
-}
-
-// ---------------------------------------------------------------------------------------
-// launchers
+// launcher
 // ---------------------------------------------------------------------------------------
 bool decode_supported(int head_dim, int group) {
   return (head_dim == 64 || head_dim == 128) &&
@@ -433,20 +322,6 @@ hipError_t launch_decode(const DecodeArgs& a, int64_t n_items, int head_dim, int
     return bf16 ? launch_decode_d<128, true>(a, grid, gi, stream)
                 : launch_decode_d<128, false>(a, grid, gi, stream);
   return hipErrorInvalidValue;
-}
-
-hipError_t launch_merge(const MergeArgs& a, int64_t n_items, int head_dim, hipStream_t stream) {
-  const int64_t grid64 = n_items * a.hq;
-  if (grid64 == 0) return hipSuccess;
-  if (grid64 > 0x7fffffffLL) return hipErrorInvalidValue;
-  const uint32_t grid = static_cast<uint32_t>(grid64);
-  if (head_dim == 64)
-    hipLaunchKernelGGL(merge_kernel<64>, dim3(grid), dim3(64), 0, stream, a);
-  else if (head_dim == 128)
-    hipLaunchKernelGGL(merge_kernel<128>, dim3(grid), dim3(128), 0, stream, a);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
 }
 
 }  // namespace pkv

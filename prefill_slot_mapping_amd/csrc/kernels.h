@@ -1,4 +1,5 @@
-// Internal launch interface of the HIP kernels (host side of kernels.hip).
+// Internal launch interface of the HIP kernels (write_kv.hip, decode.hip, merge.hip,
+// prefill.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -44,6 +45,7 @@ struct DecodeArgs {
 struct MergeArgs {
   const MergeItem* items;
   int32_t hq;
+  int32_t n_waves;  // merge items x hq
   const float* part_m;
   const float* part_l;
   const float* part_acc;
