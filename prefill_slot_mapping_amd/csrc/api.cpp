@@ -183,8 +183,11 @@ void build_lists(const StepShape& s, const pkv::WorkspaceLayout& L, char* host) 
       for (int32_t sp = 0; sp < ns; ++sp) dec[nd++] = pkv::DecodeItem{row, b, n_keys, sp, pbase, 0, 0, 0};
     }
   }
-  // longest work first: short tail items then fill the gaps at the end of the launch (item
-  // order never affects any row's bits)
+  // longest work first: short tail items then fill the gaps at the end of each launch (item
+  // order never affects any row's bits). A prefill item's work grows with its last key.
+  std::stable_sort(pre, pre + np, [](const pkv::PrefillItem& x, const pkv::PrefillItem& y) {
+    return x.pos0 + x.n_rows > y.pos0 + y.n_rows;
+  });
   std::stable_sort(dec, dec + nd, [&](const pkv::DecodeItem& x, const pkv::DecodeItem& y) {
     const int64_t kx = std::min<int64_t>(x.n_keys - static_cast<int64_t>(x.split) * s.kv_split, s.kv_split);
     const int64_t ky = std::min<int64_t>(y.n_keys - static_cast<int64_t>(y.split) * s.kv_split, s.kv_split);

@@ -16,6 +16,8 @@ constexpr int kMaxDecodeSplit = 2048;
 constexpr int kPrefillKeyTile = 64;
 // Query "M-rows" (query row x head pairs) per prefill workgroup: 4 waves x 32.
 constexpr int kPrefillMRows = 128;
+// Block-table entries a prefill workgroup holds in LDS at a time.
+constexpr int kPrefillBlockWindow = 512;
 
 // One decode work item: split `split` of query row `row` (sequence `seq`), covering keys
 // [split * kv_split, min(n_keys, (split + 1) * kv_split)). The kernel grid runs each item once

@@ -42,17 +42,41 @@ __device__ __forceinline__ int swz(int row) {
   return ((row % H) << 1) | ((row / H) & 1);
 }
 
+// 16 bytes per lane from global memory straight into LDS at lds_base + lane * 16 (M0 holds the
+// wave-uniform LDS byte address). Issued through inline assembly so that the compiler does not
+// track these LDS writes (it would otherwise wait for every outstanding tile load before each
+// LDS read that might alias); completion is awaited explicitly in tile_barrier().
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds_base) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p))));
+}
+
+// Every tile DMA and LDS access of this wave has completed, then the workgroup meets.
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int D, int G>
-__global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+prefill_kernel(PrefillArgs a) {
   constexpr int CPR = D / 8;                 // 16-byte chunks per head row
   constexpr int KS = D / 16;                 // k-steps of S^T = K Q^T
   constexpr int DB = D / 32;                 // 32-wide d blocks of O^T
-  constexpr int NLD = kPrefillKeyTile * CPR / 256;  // chunks per thread per tensor per tile
-  static_assert(NLD >= 1, "tile must cover the workgroup");
+  constexpr int TC = kPrefillKeyTile * CPR;  // chunks per tile and tensor
+  constexpr int NJ = TC / 256;               // DMA instructions per wave per tensor per tile
+  static_assert(NJ >= 1 && TC % 256 == 0, "tile must cover the workgroup");
 
-  __shared__ uint4 s_k[kPrefillKeyTile * CPR];
-  __shared__ uint4 s_v[kPrefillKeyTile * CPR];
-  __shared__ int s_slot[2][kPrefillKeyTile];
+  // [buffer][tensor: 0 = K, 1 = V][chunk]: tile kt lives in buffer kt % 2
+  __shared__ uint4 s_kv[2][2][TC];
+  // a window of the sequence's block-table entries (validated), starting at entry win0
+  __shared__ int s_blk[kPrefillBlockWindow];
   __shared__ int s_bad;
 
   const int tid = threadIdx.x;
@@ -94,51 +118,46 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
   const int32_t* bt = a.block_tables + static_cast<int64_t>(it.seq) * a.max_blocks;
   const uint4* __restrict__ kp = static_cast<const uint4*>(a.k_cache);
   const uint4* __restrict__ vp = static_cast<const uint4*>(a.v_cache);
-  const int64_t slot_stride = static_cast<int64_t>(a.hkv) * CPR;    // uint4 per slot
+  const uint32_t slot_stride = static_cast<uint32_t>(a.hkv * CPR);  // uint4 per slot
   const int head_off = g * CPR;
   bool bad = false;
 
-  // slot of key (tile kt, key t) for t < 64, or -1 when not needed / not valid
-  auto tile_slots = [&](int kt, int buf) {
-    if (tid < kPrefillKeyTile) {
-      const int kabs = kt * kPrefillKeyTile + tid;
-      int slot = -1;
-      if (kabs < key_limit) {
-        int j, off;
-        if (a.bs_log2 >= 0) {
-          j = kabs >> a.bs_log2;
-          off = kabs & (a.block_size - 1);
-        } else {
-          j = kabs / a.block_size;
-          off = kabs - j * a.block_size;
-        }
-        const int b = bt[j];
-        if (static_cast<unsigned>(b) < static_cast<unsigned>(a.num_blocks)) {
-          slot = b * a.block_size + off;
-        } else {
-          bad = true;
-        }
-      }
-      s_slot[buf][tid] = slot;
+  auto entry_of = [&](int key) { return a.bs_log2 >= 0 ? key >> a.bs_log2 : key / a.block_size; };
+  const int n_entries = entry_of(key_limit - 1) + 1;
+  int win0 = 0;
+
+  // Block-table entries win0 .. win0 + window - 1 into s_blk. An out-of-pool block id marks the
+  // item bad and is replaced by block 0, so no load ever leaves the pool.
+  auto load_window = [&]() {
+    const int n = min(kPrefillBlockWindow, n_entries - win0);
+    for (int i = tid; i < n; i += 256) {
+      const int b = bt[win0 + i];
+      const bool ok = static_cast<unsigned>(b) < static_cast<unsigned>(a.num_blocks);
+      bad |= !ok;
+      s_blk[i] = ok ? b : 0;
     }
   };
 
-  uint4 kreg[NLD], vreg[NLD];
-  auto load_tile = [&](int buf) {
+  // K and V of tile kt into LDS buffer buf. Chunk position P holds chunk (P % CPR) ^ swz(row)
+  // of key row P / CPR, so the swizzled layout comes from the source addresses. Keys no row
+  // needs re-read the item's last key (finite data whose p is exactly 0).
+  auto dma_tile = [&](int kt, int buf) {
+    uint64_t off[NJ];
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int ci = tid + 256 * i;
-      const int key = ci / CPR;
-      const int c = ci - key * CPR;
-      const int slot = s_slot[buf][key];
-      if (slot >= 0) {
-        const int64_t off = static_cast<int64_t>(slot) * slot_stride + head_off + c;
-        kreg[i] = kp[off];
-        vreg[i] = vp[off];
-      } else {
-        kreg[i] = make_uint4(0u, 0u, 0u, 0u);
-        vreg[i] = make_uint4(0u, 0u, 0u, 0u);
-      }
+    for (int j = 0; j < NJ; ++j) {
+      const int P = (wave * NJ + j) * 64 + lane;
+      const int row = P / CPR;
+      const int key = min(kt * kPrefillKeyTile + row, key_limit - 1);
+      const int e = entry_of(key);
+      const int in_blk = key - e * a.block_size;
+      const uint32_t slot = static_cast<uint32_t>(s_blk[e - win0] * a.block_size + in_blk);
+      off[j] = static_cast<uint64_t>(slot) * slot_stride + head_off + ((P % CPR) ^ swz<CPR>(row));
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int base = (wave * NJ + j) * 64;
+      dma16(kp + off[j], lds_addr(&s_kv[buf][0][base]));
+      dma16(vp + off[j], lds_addr(&s_kv[buf][1][base]));
     }
   };
 
@@ -152,27 +171,26 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
   const float sl2 = a.scale_log2e;
 
   if (tid == 0) s_bad = 0;
-  tile_slots(0, 0);
+  load_window();
   __syncthreads();
-  load_tile(0);
+  dma_tile(0, 0);
 
   for (int kt = 0; kt < n_tiles; ++kt) {
     const int buf = kt & 1;
-    __syncthreads();  // every wave is done with the previous tile's LDS
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int ci = tid + 256 * i;
-      const int key = ci / CPR;
-      const int c = ci - key * CPR;
-      const int p = key * CPR + (c ^ swz<CPR>(key));
-      s_k[p] = kreg[i];
-      s_v[p] = vreg[i];
+    // tile kt has landed in LDS; every wave is done with tile kt - 1 and with the block window
+    tile_barrier();
+    if (kt + 1 < n_tiles) {
+      const int last_key = min((kt + 2) * kPrefillKeyTile, key_limit) - 1;
+      if (entry_of(last_key) >= win0 + kPrefillBlockWindow) {   // uniform: slide the window
+        win0 = entry_of((kt + 1) * kPrefillKeyTile);
+        load_window();
+        tile_barrier();
+      }
+      dma_tile(kt + 1, buf ^ 1);                       // in flight while this tile is computed
     }
-    if (kt + 1 < n_tiles) tile_slots(kt + 1, buf ^ 1);
-    __syncthreads();
-    if (kt + 1 < n_tiles) load_tile(buf ^ 1);   // in flight while this tile is computed
 
     if (kt * kPrefillKeyTile > wave_last_pos) continue;  // no row of this wave sees this tile
+    const uint4* sk = s_kv[buf][0];
 
     // ---- S^T = K Q^T: two 32-key blocks ----
     f32x16_t s[2];
@@ -183,7 +201,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
       const int row = kb * 32 + l32;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const uint4 kv = s_k[row * CPR + ((2 * ks + h32) ^ swz<CPR>(row))];
+        const uint4 kv = sk[row * CPR + ((2 * ks + h32) ^ swz<CPR>(row))];
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv), qf[ks],
                                                         s[kb], 0, 0, 0);
       }
@@ -221,7 +239,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
     const int rsub = i16 >> 2;            // row this lane addresses inside a 4-row read
     const int csub = 4 * (i16 & 3);       // element column offset inside the 16-wide d strip
     __attribute__((address_space(3))) char* vbase =
-        (__attribute__((address_space(3))) char*)(s_v);
+        (__attribute__((address_space(3))) char*)(s_kv[buf][1]);
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
