@@ -98,6 +98,7 @@ prefill_kernel(PrefillArgs a) {
   const int wave_rows_lo = wave * 32 / G;
   const int wave_rows_hi = min(it.n_rows, (wave + 1) * 32 / G);
   const int wave_last_pos = wave_rows_hi > wave_rows_lo ? it.pos0 + wave_rows_hi - 1 : -1;
+  const int wave_first_pos = it.pos0 + wave_rows_lo;   // every real row of the wave sees keys <= this
 
   // Q fragments (B operand of S^T = K Q^T): Q[mrow][16 ks + 8 h32 .. + 8]
   bf16x8_t qf[KS];
@@ -209,15 +210,27 @@ prefill_kernel(PrefillArgs a) {
 
     // ---- masked online softmax for this lane's M-row (keys split with lane ^ 32) ----
     float tmax = -INFINITY;
+    if ((kt + 1) * kPrefillKeyTile <= wave_first_pos + 1 && real) {
+      // every key of the tile is visible to this row: no mask (same values as the masked path)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kt * kPrefillKeyTile + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-        const float v = key <= pos ? s[kb][r] * sl2 : -INFINITY;
-        s[kb][r] = v;
-        tmax = fmaxf(tmax, v);
-      }
+        for (int r = 0; r < 16; ++r) {
+          const float v = s[kb][r] * sl2;
+          s[kb][r] = v;
+          tmax = fmaxf(tmax, v);
+        }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kt * kPrefillKeyTile + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+          const float v = key <= pos ? s[kb][r] * sl2 : -INFINITY;
+          s[kb][r] = v;
+          tmax = fmaxf(tmax, v);
+        }
+    }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     const float m_new = fmaxf(m_run, tmax);
     const bool live = m_new != -INFINITY;
