@@ -40,6 +40,9 @@ def _parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--consistent", default="batched-bf16-decode,mixed-ragged-step",
+                    help="comma-separated workloads also timed in the phase-consistent mode, "
+                         "reported under 'extra' as '<name>/phase-consistent'")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 1 GiB device copies (scale reference for PMC byte "
                          "counters) and exit")
@@ -71,8 +74,10 @@ def _kv_bytes(w):
     return acc.decode_kv_bytes(w.ctx_lens, w.spec.Hkv, w.spec.D, w.elem_bytes)
 
 
-def time_workload(name, steps, warmup, device="cuda:0"):
-    """Build the step, then time `steps` whole steps; returns a result dict."""
+def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False):
+    """Build the step, then time `steps` whole steps; returns a result dict. With
+    phase_consistent the attention runs with PKV_ATTN_PHASE_CONSISTENT (decode rows on the
+    prefill tile path, bitwise equal to the same tokens inside prefill chunks)."""
     import numpy as np
     import torch
     import prefill_slot_mapping_amd as pkv
@@ -91,7 +96,7 @@ def time_workload(name, steps, warmup, device="cuda:0"):
     slots_dev = torch.empty(w.T, dtype=torch.int32, device=device)
     ws_bytes = pkv.attention_workspace_size(w.ctx_lens, w.cu_seqlens_q, s.Hq, s.Hkv, s.D,
                                             s.kv_split, pkv.PKV_BF16 if s.dtype == "bf16"
-                                            else pkv.PKV_F32)
+                                            else pkv.PKV_F32, phase_consistent)
     workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=device)
     out = torch.empty((w.T, s.Hq, s.D), dtype=torch.float32, device=device)
 
@@ -101,7 +106,7 @@ def time_workload(name, steps, warmup, device="cuda:0"):
         pkv.write_kv(gst.k_new, gst.v_new, slots_dev, gst.k_cache, gst.v_cache)
         pkv.attention(gst.q, gst.k_cache, gst.v_cache, gst.block_tables_dev, w.ctx_lens,
                       w.cu_seqlens_q, w.scale, out=out, workspace=workspace,
-                      kv_split=s.kv_split)
+                      kv_split=s.kv_split, phase_consistent=phase_consistent)
 
     for _ in range(warmup):
         step()
@@ -142,7 +147,8 @@ def time_workload(name, steps, warmup, device="cuda:0"):
     dec_kv = acc.decode_kv_bytes(w.ctx_lens[decode_rows], s.Hkv, s.D, w.elem_bytes)
     flops = acc.attention_flops(w.ctx_lens[~decode_rows], w.q_lens[~decode_rows], s.Hq, s.D)
     res = {
-        "workload": name, "B": w.B, "T": w.T, "ms_per_step": ms_step,
+        "workload": name, "phase_consistent": phase_consistent, "B": w.B, "T": w.T,
+        "ms_per_step": ms_step,
         "step_gbs": (kv + app) / (ms_step * 1e-3) / 1e9, "tokens_per_s": w.T / (ms_step * 1e-3),
         "kv_bytes": kv, "append_bytes": app, "decode_kv_bytes": dec_kv, "prefill_flops": flops,
         "build_s": t_build,
@@ -250,6 +256,12 @@ def main():
         r = time_workload(name, args.steps, args.warmup)
         r.pop("_gst"); r.pop("_w")
         extra[name] = r
+        torch.cuda.empty_cache()
+
+    for name in [n for n in args.consistent.split(",") if n]:
+        r = time_workload(name, args.steps, args.warmup, phase_consistent=True)
+        r.pop("_gst"); r.pop("_w")
+        extra[name + "/phase-consistent"] = r
         torch.cuda.empty_cache()
 
     dec_ms = main_res["kernels_ms"]["decode"]

@@ -49,6 +49,9 @@ enum {
 
 enum { PKV_F32 = 0, PKV_BF16 = 1 };
 
+/* Flag bits of pkv_attention_ex / pkv_attention_workspace_size_ex. */
+enum { PKV_ATTN_PHASE_CONSISTENT = 1 };
+
 /* Message for the calling thread's last failure ("" if none). */
 const char* pkv_last_error(void);
 /* Library version string. */
@@ -175,6 +178,32 @@ int32_t pkv_attention(const void* q, const void* k_cache, const void* v_cache,
                       int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
                       int32_t kv_split, int32_t dtype, float* out, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/* ---- phase-consistent attention ------------------------------------------------------
+ * Same as pkv_attention / pkv_attention_workspace_size with a flags word. flags = 0 is exactly
+ * pkv_attention. PKV_ATTN_PHASE_CONSISTENT routes every segment, decode rows (q_len == 1)
+ * included, through the prefill tile path (64-key tiles aligned at position 0, visited in
+ * ascending order, bf16 MFMA for both contractions), so a token's output bits are the same
+ * whether it is computed inside a prefill chunk of any size or as a decode row (phase
+ * consistency, [BC section 2]; the page names the shared path as the main cost of the
+ * consistent version). Decode rows then give
+ * up the KV split, so one workgroup streams a row's whole context per kv head; the extra cost
+ * over the split decode pass is measured, not hidden.
+ * Errors: as pkv_attention, plus PKV_ERR_INVALID for unknown flag bits and PKV_ERR_UNSUPPORTED
+ * when the flag is set for float32 inputs (the tile path is bf16 MFMA only). */
+int32_t pkv_attention_workspace_size_ex(const int32_t* ctx_lens_host,
+                                        const int32_t* cu_seqlens_q_host, int32_t B,
+                                        int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t kv_split, int32_t dtype,
+                                        uint32_t flags, size_t* bytes);
+
+int32_t pkv_attention_ex(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables_dev, int32_t max_blocks,
+                         const int32_t* ctx_lens_host, const int32_t* cu_seqlens_q_host,
+                         int32_t B, int32_t T, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                         int32_t kv_split, int32_t dtype, uint32_t flags, float* out,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- diagnostics: per-kernel device time ------------------------------------------------
  * While enabled, every kernel launched by pkv_write_kv / pkv_attention is bracketed by two HIP

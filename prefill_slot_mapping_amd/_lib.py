@@ -30,6 +30,7 @@ PKV_ERR_HIP = -6
 PKV_ERR_INCONSISTENT = -7
 PKV_F32 = 0
 PKV_BF16 = 1
+PKV_ATTN_PHASE_CONSISTENT = 1
 
 
 class PkvError(RuntimeError):
@@ -100,6 +101,12 @@ _SIGS = {
     "pkv_write_kv": ([_vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp], _i32),
     "pkv_attention_workspace_size": ([_pi32, _pi32, _i32, _i32, _i32, _i32, _i32, _i32,
                                       ctypes.POINTER(ctypes.c_size_t)], _i32),
+    "pkv_attention_workspace_size_ex": ([_pi32, _pi32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                         ctypes.c_uint32, ctypes.POINTER(ctypes.c_size_t)],
+                                        _i32),
+    "pkv_attention_ex": ([_vp, _vp, _vp, _vp, _i32, _pi32, _pi32, _i32, _i32, _i32, _i32, _i32,
+                          _i32, _i32, ctypes.c_float, _i32, _i32, ctypes.c_uint32, _vp, _vp,
+                          ctypes.c_size_t, _vp], _i32),
     "pkv_attention": ([_vp, _vp, _vp, _vp, _i32, _pi32, _pi32, _i32, _i32, _i32, _i32, _i32,
                        _i32, _i32, ctypes.c_float, _i32, _i32, _vp, _vp, ctypes.c_size_t, _vp],
                       _i32),
@@ -289,22 +296,26 @@ def write_kv(k_new, v_new, slots, k_cache, v_cache, stream=None) -> None:
 
 
 def attention_workspace_size(ctx_lens, cu_seqlens_q, num_q_heads: int, num_kv_heads: int,
-                             head_dim: int, kv_split: int = 512, dtype: int = PKV_BF16) -> int:
+                             head_dim: int, kv_split: int = 512, dtype: int = PKV_BF16,
+                             phase_consistent: bool = False) -> int:
     ctx = _host_i32(ctx_lens)
     cu = _host_i32(cu_seqlens_q)
     out = ctypes.c_size_t(0)
-    _check(lib().pkv_attention_workspace_size(_ptr(ctx), _ptr(cu), ctx.size, int(num_q_heads),
-                                              int(num_kv_heads), int(head_dim), int(kv_split),
-                                              int(dtype), ctypes.byref(out)))
+    flags = PKV_ATTN_PHASE_CONSISTENT if phase_consistent else 0
+    _check(lib().pkv_attention_workspace_size_ex(_ptr(ctx), _ptr(cu), ctx.size, int(num_q_heads),
+                                                 int(num_kv_heads), int(head_dim), int(kv_split),
+                                                 int(dtype), flags, ctypes.byref(out)))
     return int(out.value)
 
 
 def attention(q, k_cache, v_cache, block_tables, ctx_lens, cu_seqlens_q, scale: float,
-              out=None, workspace=None, kv_split: int = 512, stream=None):
+              out=None, workspace=None, kv_split: int = 512, stream=None,
+              phase_consistent: bool = False):
     """pkv_attention over a flat ragged step; returns out (float32 [T, Hq, D]).
 
     q [T, Hq, D], pools [NB, BS, Hkv, D] (same element type), block_tables int32 [B, MB] on
-    the device; ctx_lens [B] and cu_seqlens_q [B + 1] on the host.
+    the device; ctx_lens [B] and cu_seqlens_q [B + 1] on the host. phase_consistent=True calls
+    pkv_attention_ex with PKV_ATTN_PHASE_CONSISTENT (decode rows on the prefill tile path).
     """
     import torch
     _need_cuda(q, k_cache, v_cache, block_tables)
@@ -323,15 +334,18 @@ def attention(q, k_cache, v_cache, block_tables, ctx_lens, cu_seqlens_q, scale: 
     if out is None:
         out = torch.empty((T, hq, d), dtype=torch.float32, device=q.device)
     _need_cuda(out)
-    need = attention_workspace_size(ctx, cu, hq, hkv, d, kv_split, dt)
+    need = attention_workspace_size(ctx, cu, hq, hkv, d, kv_split, dt, phase_consistent)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    _check(lib().pkv_attention(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                               block_tables.data_ptr(), int(block_tables.shape[1]), _ptr(ctx),
-                               _ptr(cu), B, T, hq, hkv, d, bs, nb, float(scale), int(kv_split),
-                               dt, out.data_ptr(), workspace.data_ptr(),
-                               workspace.numel() * workspace.element_size(),
-                               _stream_ptr(q, stream)))
+    args = [q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+            int(block_tables.shape[1]), _ptr(ctx), _ptr(cu), B, T, hq, hkv, d, bs, nb,
+            float(scale), int(kv_split), dt]
+    tail = [out.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            _stream_ptr(q, stream)]
+    if phase_consistent:
+        _check(lib().pkv_attention_ex(*args, PKV_ATTN_PHASE_CONSISTENT, *tail))
+    else:
+        _check(lib().pkv_attention(*args, *tail))
     return out
 
 

@@ -108,8 +108,12 @@ struct StepShape {
   int32_t B;
   int32_t kv_split;
   bool prefill_on_mfma;  // segments with q_len > 1 use the prefill kernel
+  bool all_mfma;         // phase-consistent mode: every segment (decode rows too) uses it
   int32_t prefill_rows_per_item;
 };
+
+// Whether segment b (q_len ql >= 1) runs on the prefill tile kernel.
+bool on_tiles(const StepShape& s, int32_t ql) { return s.all_mfma || (ql > 1 && s.prefill_on_mfma); }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -119,7 +123,7 @@ pkv::WorkspaceLayout layout_for(const StepShape& s, int32_t hq, int32_t head_dim
   for (int32_t b = 0; b < s.B; ++b) {
     const int32_t ql = s.cu[b + 1] - s.cu[b];
     if (ql == 0) continue;
-    if (ql > 1 && s.prefill_on_mfma) {
+    if (on_tiles(s, ql)) {
       L.n_prefill += ceil_div(ql, s.prefill_rows_per_item);
       continue;
     }
@@ -159,7 +163,7 @@ void build_lists(const StepShape& s, const pkv::WorkspaceLayout& L, char* host) 
   for (int32_t b = 0; b < s.B; ++b) {
     const int32_t ql = s.cu[b + 1] - s.cu[b];
     if (ql == 0) continue;
-    if (ql > 1 && s.prefill_on_mfma) {
+    if (on_tiles(s, ql)) {
       const int32_t prior = s.ctx[b] - ql;
       for (int32_t r0 = 0; r0 < ql; r0 += s.prefill_rows_per_item) {
         pkv::PrefillItem& p = pre[np++];
@@ -233,9 +237,20 @@ int32_t check_heads(int32_t hq, int32_t hkv, int32_t head_dim, int32_t kv_split,
   return PKV_OK;
 }
 
+int32_t check_flags(uint32_t flags, int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype) {
+  if ((flags & ~static_cast<uint32_t>(PKV_ATTN_PHASE_CONSISTENT)) != 0)
+    return fail(PKV_ERR_INVALID, "attention: unknown flag bits");
+  if ((flags & PKV_ATTN_PHASE_CONSISTENT) &&
+      !pkv::prefill_supported(head_dim, hq / hkv, dtype == PKV_BF16))
+    return fail(PKV_ERR_UNSUPPORTED, "attention: the phase-consistent mode runs on bf16 MFMA tiles "
+                                     "only (bf16, head_dim 64 or 128)");
+  return PKV_OK;
+}
+
 StepShape shape_for(const int32_t* ctx, const int32_t* cu, int32_t B, int32_t hq, int32_t hkv,
-                    int32_t head_dim, int32_t kv_split, int32_t dtype) {
+                    int32_t head_dim, int32_t kv_split, int32_t dtype, uint32_t flags) {
   StepShape s;
+  s.all_mfma = (flags & PKV_ATTN_PHASE_CONSISTENT) != 0;
   s.ctx = ctx;
   s.cu = cu;
   s.B = B;
@@ -281,33 +296,47 @@ extern "C" int32_t pkv_write_kv(const void* k_new, const void* v_new, const int3
   return ok();
 }
 
-extern "C" int32_t pkv_attention_workspace_size(const int32_t* ctx_lens_host,
-                                                const int32_t* cu_seqlens_q_host, int32_t B,
-                                                int32_t num_q_heads, int32_t num_kv_heads,
-                                                int32_t head_dim, int32_t kv_split, int32_t dtype,
-                                                size_t* bytes) {
+extern "C" int32_t pkv_attention_workspace_size_ex(const int32_t* ctx_lens_host,
+                                                   const int32_t* cu_seqlens_q_host, int32_t B,
+                                                   int32_t num_q_heads, int32_t num_kv_heads,
+                                                   int32_t head_dim, int32_t kv_split,
+                                                   int32_t dtype, uint32_t flags, size_t* bytes) {
   if (bytes == nullptr) return fail(PKV_ERR_INVALID, "workspace_size: bytes is NULL");
   *bytes = 0;
   int32_t st = check_heads(num_q_heads, num_kv_heads, head_dim, kv_split, dtype);
+  if (st != PKV_OK) return st;
+  st = check_flags(flags, num_q_heads, num_kv_heads, head_dim, dtype);
   if (st != PKV_OK) return st;
   const int32_t T = (B > 0 && cu_seqlens_q_host != nullptr) ? cu_seqlens_q_host[B] : 0;
   st = check_step(ctx_lens_host, cu_seqlens_q_host, B, T, -1);
   if (st != PKV_OK) return st;
   if (B == 0) return ok();
   StepShape s = shape_for(ctx_lens_host, cu_seqlens_q_host, B, num_q_heads, num_kv_heads,
-                          head_dim, kv_split, dtype);
+                          head_dim, kv_split, dtype, flags);
   *bytes = layout_for(s, num_q_heads, head_dim).total;
   return ok();
 }
 
-extern "C" int32_t pkv_attention(const void* q, const void* k_cache, const void* v_cache,
-                                 const int32_t* block_tables_dev, int32_t max_blocks,
-                                 const int32_t* ctx_lens_host, const int32_t* cu_seqlens_q_host,
-                                 int32_t B, int32_t T, int32_t num_q_heads, int32_t num_kv_heads,
-                                 int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                                 float scale, int32_t kv_split, int32_t dtype, float* out,
-                                 void* workspace, size_t workspace_bytes, void* stream) {
+extern "C" int32_t pkv_attention_workspace_size(const int32_t* ctx_lens_host,
+                                                const int32_t* cu_seqlens_q_host, int32_t B,
+                                                int32_t num_q_heads, int32_t num_kv_heads,
+                                                int32_t head_dim, int32_t kv_split, int32_t dtype,
+                                                size_t* bytes) {
+  return pkv_attention_workspace_size_ex(ctx_lens_host, cu_seqlens_q_host, B, num_q_heads,
+                                         num_kv_heads, head_dim, kv_split, dtype, 0u, bytes);
+}
+
+extern "C" int32_t pkv_attention_ex(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_tables_dev, int32_t max_blocks,
+                                    const int32_t* ctx_lens_host, const int32_t* cu_seqlens_q_host,
+                                    int32_t B, int32_t T, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                    int32_t num_blocks, float scale, int32_t kv_split,
+                                    int32_t dtype, uint32_t flags, float* out, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
   int32_t st = check_heads(num_q_heads, num_kv_heads, head_dim, kv_split, dtype);
+  if (st != PKV_OK) return st;
+  st = check_flags(flags, num_q_heads, num_kv_heads, head_dim, dtype);
   if (st != PKV_OK) return st;
   if (block_size <= 0 || num_blocks <= 0 || max_blocks < 0)
     return fail(PKV_ERR_INVALID, "block_size, num_blocks must be > 0 and max_blocks >= 0");
@@ -323,7 +352,7 @@ extern "C" int32_t pkv_attention(const void* q, const void* k_cache, const void*
     return fail(PKV_ERR_INVALID, "attention: NULL device pointer");
 
   const StepShape s = shape_for(ctx_lens_host, cu_seqlens_q_host, B, num_q_heads, num_kv_heads,
-                                head_dim, kv_split, dtype);
+                                head_dim, kv_split, dtype, flags);
   const pkv::WorkspaceLayout L = layout_for(s, num_q_heads, head_dim);
   if (workspace_bytes < L.total || (L.total > 0 && workspace == nullptr))
     return fail(PKV_ERR_INVALID, "attention: workspace smaller than pkv_attention_workspace_size (" +
@@ -438,6 +467,19 @@ extern "C" int32_t pkv_attention(const void* q, const void* k_cache, const void*
     if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("merge launch: ") + hipGetErrorString(e));
   }
   return ok();
+}
+
+extern "C" int32_t pkv_attention(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables_dev, int32_t max_blocks,
+                                 const int32_t* ctx_lens_host, const int32_t* cu_seqlens_q_host,
+                                 int32_t B, int32_t T, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                 float scale, int32_t kv_split, int32_t dtype, float* out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  return pkv_attention_ex(q, k_cache, v_cache, block_tables_dev, max_blocks, ctx_lens_host,
+                          cu_seqlens_q_host, B, T, num_q_heads, num_kv_heads, head_dim,
+                          block_size, num_blocks, scale, kv_split, dtype, 0u, out, workspace,
+                          workspace_bytes, stream);
 }
 
 extern "C" int32_t pkv_profile_enable(int32_t enable) {

@@ -55,7 +55,8 @@ class GpuStep:
         L.write_kv(self.k_new, self.v_new, self.new_slots_dev, self.k_cache, self.v_cache,
                    stream=stream)
 
-    def attention(self, kv_split: Optional[int] = None, stream=None):
+    def attention(self, kv_split: Optional[int] = None, stream=None,
+                  phase_consistent: bool = False):
         import torch
         w = self.workload
         split = w.spec.kv_split if kv_split is None else kv_split
@@ -64,12 +65,14 @@ class GpuStep:
                                    device=self.q.device)
         need = L.attention_workspace_size(w.ctx_lens, w.cu_seqlens_q, w.spec.Hq, w.spec.Hkv,
                                           w.spec.D, split,
-                                          L.PKV_BF16 if w.spec.dtype == "bf16" else L.PKV_F32)
+                                          L.PKV_BF16 if w.spec.dtype == "bf16" else L.PKV_F32,
+                                          phase_consistent)
         if self.workspace is None or self.workspace.numel() < need:
             self.workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=self.q.device)
         return L.attention(self.q, self.k_cache, self.v_cache, self.block_tables_dev,
                            w.ctx_lens, w.cu_seqlens_q, w.scale, out=self.out,
-                           workspace=self.workspace, kv_split=split, stream=stream)
+                           workspace=self.workspace, kv_split=split, stream=stream,
+                           phase_consistent=phase_consistent)
 
 
 def build_gpu_step(w, device="cuda", write_new: bool = True, workers: int = 8) -> GpuStep:

@@ -211,3 +211,38 @@ def test_write_kv_validation():
     assert lib.pkv_write_kv(0, 1, 1, 4, 1, 1, 4, 16, 2, 128, 1, None) == L.PKV_ERR_INVALID
     assert lib.pkv_write_kv(1, 1, 1, 0, 1, 1, 4, 16, 2, 128, 1, None) == L.PKV_OK
     assert lib.pkv_write_kv(1, 1, 1, 4, 1, 1, 4, 16, 1, 4, 1, None) == L.PKV_ERR_UNSUPPORTED
+
+
+def _attn_ex(flags, **kw):
+    """Raw pkv_attention_ex call with fake device pointers: only validation may run."""
+    lib = pkv.lib()
+    a = dict(q=1, k=1, v=1, bt=1, mb=8, ctx=[5, 9], cu=[0, 1, 3], T=3, hq=8, hkv=2, d=128,
+             bs=16, nb=4, scale=0.1, split=512, dt=L.PKV_BF16, out=1, ws=1, wsb=16)
+    a.update(kw)
+    ctx = np.asarray(a["ctx"], np.int32)
+    cu = np.asarray(a["cu"], np.int32)
+    return lib.pkv_attention_ex(a["q"], a["k"], a["v"], a["bt"], a["mb"], L._ptr(ctx),
+                                L._ptr(cu), ctx.size, a["T"], a["hq"], a["hkv"], a["d"], a["bs"],
+                                a["nb"], a["scale"], a["split"], a["dt"], flags, a["out"],
+                                a["ws"], a["wsb"], None)
+
+
+def test_phase_consistent_flag_validation():
+    # unknown bits and float32 (no MFMA tile path) are refused before any launch
+    assert _attn_ex(2) == L.PKV_ERR_INVALID
+    assert _attn_ex(L.PKV_ATTN_PHASE_CONSISTENT, dt=L.PKV_F32) == L.PKV_ERR_UNSUPPORTED
+    assert _attn_ex(L.PKV_ATTN_PHASE_CONSISTENT, d=96) == L.PKV_ERR_UNSUPPORTED
+    # a valid call with a 16-byte workspace fails on the workspace size, i.e. after the flags
+    assert _attn_ex(L.PKV_ATTN_PHASE_CONSISTENT) == L.PKV_ERR_INVALID
+    assert b"workspace" in pkv.lib().pkv_last_error()
+    with pytest.raises(pkv.Unsupported):
+        pkv.attention_workspace_size([5], [0, 1], 8, 2, 128, 512, L.PKV_F32,
+                                     phase_consistent=True)
+
+
+def test_phase_consistent_workspace_has_no_split_partials():
+    # a 4096-key decode row: 8 splits and their partials normally; one tile item when consistent
+    normal = pkv.attention_workspace_size([4096], [0, 1], 8, 2, 128, 512)
+    cons = pkv.attention_workspace_size([4096], [0, 1], 8, 2, 128, 512, phase_consistent=True)
+    assert normal >= 8 * 8 * 130 * 4
+    assert 0 < cons < 1024
