@@ -419,7 +419,8 @@ extern "C" int32_t pkv_attention_ex(const void* q, const void* k_cache, const vo
     p.n_items = static_cast<int32_t>(L.n_prefill);
     p.hq = num_q_heads;
     p.hkv = num_kv_heads;
-    p.scale_log2e = scale_log2e;
+    p.scale_log2e = std::fabs(scale_log2e);
+    p.negate_q = scale < 0.f ? 1 : 0;
     p.items = reinterpret_cast<const pkv::PrefillItem*>(ws + L.prefill_off);
     p.out = out;
     const int pr = prof_begin(1, strm);

@@ -64,7 +64,8 @@ struct PrefillArgs {
   int32_t hq;
   int32_t hkv;
   int32_t n_items;
-  float scale_log2e;
+  float scale_log2e;  // |scale| * log2(e)
+  int32_t negate_q;   // scale < 0: the kernel flips the sign of q instead
   const PrefillItem* items;
   float* out;
 };

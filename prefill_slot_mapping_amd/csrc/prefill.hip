@@ -94,11 +94,14 @@ prefill_kernel(PrefillArgs a) {
   const int qrow = mr / G;
   const int head = mr - qrow * G;
   const bool real = qrow < it.n_rows;
-  const int pos = real ? it.pos0 + qrow : -1;
+  // padding M-rows (past the item's rows) behave like the last row with a zero query: finite
+  // values, never written
+  const int pos = real ? it.pos0 + qrow : it.pos0 + it.n_rows - 1;
   const int wave_rows_lo = wave * 32 / G;
   const int wave_rows_hi = min(it.n_rows, (wave + 1) * 32 / G);
   const int wave_last_pos = wave_rows_hi > wave_rows_lo ? it.pos0 + wave_rows_hi - 1 : -1;
   const int wave_first_pos = it.pos0 + wave_rows_lo;   // every real row of the wave sees keys <= this
+  constexpr float kRescaleSlack = 8.f;
 
   // Q fragments (B operand of S^T = K Q^T): Q[mrow][16 ks + 8 h32 .. + 8]
   bf16x8_t qf[KS];
@@ -107,9 +110,14 @@ prefill_kernel(PrefillArgs a) {
         static_cast<const char*>(a.q) +
         ((static_cast<int64_t>(it.row0) + (real ? qrow : 0)) * a.hq +
          static_cast<int64_t>(g) * G + head) * (D * 2));
+    const uint32_t sign = a.negate_q ? 0x80008000u : 0u;   // scale < 0: fold its sign into q
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const uint4 v = real ? qsrc[2 * ks + h32] : make_uint4(0u, 0u, 0u, 0u);
+      uint4 v = real ? qsrc[2 * ks + h32] : make_uint4(0u, 0u, 0u, 0u);
+      v.x ^= sign;
+      v.y ^= sign;
+      v.z ^= sign;
+      v.w ^= sign;
       qf[ks] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
@@ -167,9 +175,9 @@ prefill_kernel(PrefillArgs a) {
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-  float m_run = -INFINITY;
+  float m_ref = -INFINITY;
   float l_run = 0.f;
-  const float sl2 = a.scale_log2e;
+  const float sl2 = a.scale_log2e;   // |scale| * log2(e)
 
   if (tid == 0) s_bad = 0;
   load_window();
@@ -208,42 +216,40 @@ prefill_kernel(PrefillArgs a) {
       }
     }
 
-    // ---- masked online softmax for this lane's M-row (keys split with lane ^ 32) ----
+    // ---- online softmax for this lane's M-row (keys split with lane ^ 32), base 2 ----
+    // Exponents are taken against a reference m_ref that trails the running max by less than
+    // kRescaleSlack (p <= 2^slack); O and l are rescaled only when the max rises past it.
+    const bool diag = (kt + 1) * kPrefillKeyTile > wave_first_pos + 1 || !real;
     float tmax = -INFINITY;
-    if ((kt + 1) * kPrefillKeyTile <= wave_first_pos + 1 && real) {
-      // every key of the tile is visible to this row: no mask (same values as the masked path)
+    if (!diag) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float v = s[kb][r] * sl2;
-          s[kb][r] = v;
-          tmax = fmaxf(tmax, v);
-        }
+        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[kb][r]);
     } else {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kt * kPrefillKeyTile + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-          const float v = key <= pos ? s[kb][r] * sl2 : -INFINITY;
-          s[kb][r] = v;
-          tmax = fmaxf(tmax, v);
+          tmax = fmaxf(tmax, key <= pos ? s[kb][r] : -INFINITY);
         }
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const bool live = m_new != -INFINITY;
-    const float alpha = live ? fast_exp2(m_run - m_new) : 1.f;
-    m_run = m_new;
-    // Rescale only when some row's max moved: multiplying by exactly 1 is a no-op, so skipping
-    // it when every alpha is 1 leaves every row's bits unchanged.
-    if (__any(alpha != 1.f)) {
+    // scale >= 0 keeps the order of scores; fmaxf drops the NaN of -inf * 0
+    const float m_cand = fmaxf(m_ref, tmax * sl2);
+    const bool need = m_cand > m_ref + kRescaleSlack;
+    if (__any(need)) {
+      // a multiply by exactly 1 (rows that keep their reference) changes nothing
+      const float alpha = need ? fast_exp2(m_ref - m_cand) : 1.f;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      l_run *= alpha;
+      m_ref = need ? m_cand : m_ref;
     }
+    const float neg_m = -m_ref;
 
     // ---- O^T += V^T P^T per 16-key k-step (kb, m); the A operand (V^T) comes from two
     //      transpose reads, the B operand (P^T) is this lane's own probabilities ----
@@ -261,7 +267,12 @@ prefill_kernel(PrefillArgs a) {
         bf16x8_t phi, plo;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float p = live ? fast_exp2(s[kb][8 * m + j] - m_new) : 0.f;
+          float p = fast_exp2(fmaf(s[kb][8 * m + j], sl2, neg_m));
+          if (diag) {
+            const int r = 8 * m + j;
+            const int key = kt * kPrefillKeyTile + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+            p = key <= pos ? p : 0.f;
+          }
           psum += p;
           const __bf16 ph = static_cast<__bf16>(p);
           phi[j] = ph;
@@ -286,7 +297,7 @@ prefill_kernel(PrefillArgs a) {
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, plo, acc[db], 0, 0, 0);
         }
       }
-    l_run = l_run * alpha + psum;
+    l_run += psum;
   }
 
   if (bad) s_bad = 1;
