@@ -14,6 +14,9 @@ Modules
   allocator  block bookkeeping twin: LIFO free list, refcounts, all-or-nothing allocation,
              read-only shared blocks, the slot rule.
   harness    replays a workload's admissions and prior-context writes into oracle pools.
+  scheduler  the host step builder: decodes first, chunked prefill within a token budget, FIFO
+             admission, preemption of the youngest by recompute, prefix adoption of full
+             blocks with the last prompt token recomputed, trim, copy-on-write forks.
 
 Every function is pinned by ``tests/test_oracle_*.py`` to something other than itself:
 torch's float64 scaled_dot_product_attention on contiguous K/V, closed forms (one key, zero
@@ -25,9 +28,11 @@ from .paged import (bf16_bits_to_f64, write_kv, gather, attend_rows, paged_atten
 from .allocator import (BlockAllocator, AllocatorError, PoolExhausted, DoubleFree, SharedWrite,
                         InvalidBlock)
 from .harness import OracleStep, build_oracle_step
+from .scheduler import SchedConfig, Scheduler, SchedulerError, StepPlan
 
 __all__ = [
     "bf16_bits_to_f64", "write_kv", "gather", "attend_rows", "paged_attention", "OracleError",
     "BlockAllocator", "AllocatorError", "PoolExhausted", "DoubleFree", "SharedWrite",
-    "InvalidBlock", "OracleStep", "build_oracle_step",
+    "InvalidBlock", "OracleStep", "build_oracle_step", "SchedConfig", "Scheduler",
+    "SchedulerError", "StepPlan",
 ]
