@@ -211,6 +211,8 @@ class Scheduler:
 
     # ---- one step ----------------------------------------------------------------------
     def step(self) -> StepPlan:
+        if self.last_plan is not None:
+            raise SchedulerError("step while the previous step awaits completion")
         cfg = self.cfg
         self._admission()
         budget = cfg.token_budget
@@ -226,7 +228,7 @@ class Scheduler:
                 if budget == 0:
                     break
                 rem = s.n_tokens - s.num_computed
-                if rid in scheduled or rid in preempted or (rem == 1) != decode_pass:
+                if rem <= 0 or rid in scheduled or rid in preempted or (rem == 1) != decode_pass:
                     continue
                 n_new = min(rem, cfg.chunk_size, budget)
                 if self._reserve(s, n_new, scheduled, copies, preempted):
@@ -270,6 +272,8 @@ class Scheduler:
 
     # ---- trim / fork -------------------------------------------------------------------
     def trim(self, sid: int, n_tokens: int) -> None:
+        if self.last_plan is not None:
+            raise SchedulerError("trim while a step awaits completion")
         s = self.seqs.get(sid)
         if s is None or s.state != RUNNING or not 1 <= n_tokens <= s.n_tokens:
             raise SchedulerError("trim of a non-running sequence or past its tokens")
@@ -281,6 +285,8 @@ class Scheduler:
             s.blocks = s.blocks[:keep]
 
     def fork(self, src: int, new_sid: int) -> None:
+        if self.last_plan is not None:
+            raise SchedulerError("fork while a step awaits completion")
         s = self.seqs.get(src)
         if s is None or s.state != RUNNING:
             raise SchedulerError("fork of a non-running sequence")
