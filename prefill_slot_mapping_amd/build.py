@@ -27,6 +27,10 @@ HOST_SOURCES = ["allocator.cpp", "api.cpp"]
 # Packed-FP32 instructions are disabled for all device code: the compiler may not form
 # v_pk_{add,mul,fma}_f32 from ordinary float code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-source extras. decode.hip: no floating-point operation there sees a NaN (bad rows are
+# written as a NaN bit pattern through an integer select), which lets maxima fuse with their
+# DPP lane permutes.
+SOURCE_FLAGS = {"decode.hip": ["-fno-honor-nans"]}
 
 
 def hipcc() -> str:
@@ -58,8 +62,8 @@ def build(debug: bool = False, verbose: bool = False, jobs: int = 8) -> str:
     objs = []
     for src in DEVICE_SOURCES:
         obj = os.path.join(BUILD_DIR, src.replace(".", "_") + ".o")
-        cmds.append([cc, "-x", "hip", f"--offload-arch={ARCH}", *common, *DEVICE_FLAGS, "-c",
-                     os.path.join(CSRC, src), "-o", obj])
+        cmds.append([cc, "-x", "hip", f"--offload-arch={ARCH}", *common, *DEVICE_FLAGS,
+                     *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD_DIR, src.replace(".", "_") + ".o")

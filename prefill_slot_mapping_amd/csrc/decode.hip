@@ -5,14 +5,21 @@
 // ctx_lens; a fixed KV split per context length, no atomics), and "Finish RL Training Faster:
 // Bitwise-Consistent ..." section 2 (kernel determinism, batch independence).
 //
-// Numeric contract (every choice depends only on the row's own sequence, never on the batch):
+// Numeric contract (every choice depends only on the row's own sequence and the kernel
+// instance, which is fixed by head_dim, group size and element type, never by the batch):
 // the keys of a row are cut into splits of kv_split tokens aligned at position 0; inside a
-// split, 32-key half tiles aligned at the split start go to wave (half tile % 4); each wave
-// runs an online softmax over its half tiles in ascending order in the base-2 domain (scores
-// scaled by scale * log2 e, hardware exp2); the four wave partials are merged in wave order and
-// the split partials in ascending split order (merge kernel). Accumulation is float32
-// throughout; bfloat16 products are formed exactly by v_dot2_f32_bf16; probabilities stay
-// float32 for P.V.
+// split, tiles of HT keys (16 or 32, per instance) aligned at the split start go to wave
+// (tile % 4); each wave runs an online softmax over its tiles in ascending order in the base-2
+// domain (scores scaled by scale * log2 e, hardware exp2); the four wave partials are merged
+// in wave order and the split partials in ascending split order (merge kernel). Accumulation
+// is float32 throughout; bfloat16 products are formed exactly by v_dot2_f32_bf16 and summed
+// over the head dimension in ascending 16-byte chunks, one part of the dimension per lane of a
+// key's lane group, the parts then added in a fixed butterfly; probabilities stay float32 for
+// P.V.
+//
+// This file is compiled with -fno-honor-nans (lets maxima fuse with their lane permutes): no
+// floating-point operation here sees a NaN; a row whose block table is bad is written as a NaN
+// bit pattern through an integer select.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -22,61 +29,142 @@
 
 namespace pkv {
 
+namespace {
+
+// lane ^ 2 within quads
+__device__ __forceinline__ float dpp_xor2(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
+// lane i of a 16-lane row reads lane 7 - i of its 8-lane half (row_half_mirror)
+__device__ __forceinline__ float dpp_half_mirror(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
+}
+// lane i of a 16-lane row reads lane 15 - i (row_mirror)
+__device__ __forceinline__ float dpp_mirror(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
+}
+// lane i of a 16-lane row reads lane (i + n) % 16 (row_ror:n)
+template <int N>
+__device__ __forceinline__ float dpp_ror(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xF, 0xF, false));
+}
+
+// op over the two 32-lane halves (every lane receives op(x[l], x[l ^ 32]))
+template <typename Op>
+__device__ __forceinline__ float across32(float x, Op op) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// op over lanes l and l ^ 16 (every lane receives op(x[l], x[l ^ 16]))
+template <typename Op>
+__device__ __forceinline__ float across16(float x, Op op) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+struct MaxOp {
+  __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct AddOp {
+  __device__ float operator()(float a, float b) const { return a + b; }
+};
+
+// max over the wave of values held in equal groups of SPL consecutive lanes (SPL = 2 or 4)
+template <int SPL>
+__device__ __forceinline__ float max_over_groups(float x) {
+  if constexpr (SPL == 2) x = fmaxf(x, dpp_xor2(x));
+  x = fmaxf(x, dpp_half_mirror(x));
+  x = fmaxf(x, dpp_mirror(x));
+  x = across16(x, MaxOp());
+  return across32(x, MaxOp());
+}
+
+// sum over the lanes l' of the wave with l' % SPL == l % SPL (SPL = 2 or 4); the order of the
+// additions is fixed by the lane index alone
+template <int SPL>
+__device__ __forceinline__ float sum_same_class(float x) {
+  if constexpr (SPL == 2) x += dpp_xor2(x);
+  x += dpp_ror<4>(x);
+  x += dpp_ror<8>(x);
+  x = across16(x, AddOp());
+  return across32(x, AddOp());
+}
+
+// sum over lanes l, l ^ k for k = step, 2 step, ..., 32 (step a power of two >= 8)
+template <int STEP>
+__device__ __forceinline__ float sum_key_groups(float x) {
+  if constexpr (STEP <= 8) x += dpp_ror<8>(x);
+  if constexpr (STEP <= 16) x = across16(x, AddOp());
+  if constexpr (STEP <= 32) x = across32(x, AddOp());
+  return x;
+}
+
+}  // namespace
+
 // ---------------------------------------------------------------------------------------
 // Decode split pass.
 //
-// Workgroup = 4 waves = one (query row, split, kv head) item; it serves the G query heads that
-// read that kv head, so every K/V byte of the split is loaded from HBM once.
-// Prologue: the split's slots (one block-table read per key) and the G query rows go to LDS.
-// The split is cut into 32-key half tiles aligned at the split start; half tile j belongs to
-// wave j % 4. Each wave double-buffers its half tiles in registers: the loads of the next
-// half tile are in flight while the current one is computed. Per half tile a wave
+// Workgroup = 4 waves = one (query row, split, kv head) item serving all G query heads of
+// that kv head, so every K/V byte of the split is loaded from HBM once. W waves of this kernel
+// share a SIMD (register budget 512 / W per lane).
+// Prologue: the split's slots (one block-table read per key; keys past the split end repeat
+// the last key, whose probability is forced to 0) and the G query rows go to LDS. The slots
+// are stored transposed per half tile so that a lane's slots are contiguous.
+// The split is cut into HT-key tiles aligned at the split start; tile j belongs to wave j % 4.
+// Each wave double-buffers its tiles in registers: the loads of the next tile are in flight
+// while the current one is computed. Per tile a wave
 //   1. has loaded K and V rows with coalesced 16-byte nontemporal loads (LPT lanes cover one
-//      head row; keys past the split end re-read the last key, whose p is 0),
-//   2. stages K in LDS (XOR swizzle on 16-byte chunks) and computes the scores with two lanes
-//      per key (each covers half of D; one DPP exchange completes the dot product),
-//   3. updates the per-head running max (wave-uniform) and publishes p through LDS,
+//      head row),
+//   2. stages K in LDS (XOR swizzle on 16-byte chunks) and computes the scores with SPL =
+//      64 / HT lanes per key (each covers D / SPL; DPP exchanges complete the dot product),
+//   3. updates the per-head running max (wave-uniform) and publishes p through LDS (lane
+//      h % SPL of each key's group forms p for head h),
 //   4. accumulates P.V in the split-D layout (each lane owns EPL columns of its key group).
 // ---------------------------------------------------------------------------------------
-template <int D, int G, bool BF>
-__global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
-  // G = query heads served by one work item: all heads of a kv head when the group has at
-  // most 4 of them, else 4 consecutive heads (two items of a larger group share a kv head and
-  // read its K/V through the same XCD's L2)
+template <int D, int G, bool BF, int HT, int W>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(W, W)))
+decode_split_kernel(DecodeArgs a) {
   constexpr int E = BF ? 2 : 4;
   constexpr int ROWB = D * E;               // bytes of one head row
   constexpr int LPT = ROWB / 16;            // lanes per key row
-  constexpr int TPI = 64 / LPT;             // keys per load instruction
-  constexpr int HT = kDecodeTile / 2;       // keys per half tile
-  constexpr int NI = HT / TPI;              // load instructions per half tile and tensor
+  constexpr int TPI = 64 / LPT;             // keys per load instruction (key groups)
+  constexpr int NI = HT / TPI;              // load instructions per tile and tensor
   constexpr int EPL = 16 / E;               // elements per lane chunk
-  constexpr int CPH = LPT / 2;              // chunks per lane in the score stage
-  static_assert(LPT >= 2 && LPT <= 32 && (LPT & (LPT - 1)) == 0 && HT % TPI == 0, "shape");
+  constexpr int SPL = 64 / HT;              // score stage: lanes per key (2 or 4)
+  constexpr int CPH = LPT / SPL;            // score stage: chunks per lane
+  constexpr int GO = G >= SPL ? G / SPL : 1;  // heads whose p a lane forms
+  static_assert(LPT >= 8 && LPT <= 32 && (LPT & (LPT - 1)) == 0 && HT % TPI == 0, "shape");
+  static_assert(HT == 16 || HT == 32, "tile");
+  static_assert(NI % 2 == 0, "slot reads are 8- or 16-byte vectors");
 
-  __shared__ uint4 s_k[kDecodeWaves][HT * LPT];
-  __shared__ float s_p[kDecodeWaves][HT * G];
+  // K tiles of the four waves; reused as the wave-merge scratch at the end
+  constexpr int kTileU4 = kDecodeWaves * HT * LPT;
+  constexpr int kMergeU4 = (kDecodeWaves * G * (D + 2) * 4 + 15) / 16;
+  __shared__ uint4 s_k[kTileU4 > kMergeU4 ? kTileU4 : kMergeU4];
+  __shared__ __align__(16) float s_p[kDecodeWaves][HT * G];
   __shared__ uint4 s_q[G * LPT];
-  __shared__ int s_slot[kMaxDecodeSplit];
+  __shared__ __align__(16) uint32_t s_slot[kMaxDecodeSplit];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int f = xcd_remap(blockIdx.x, gridDim.x);
-  const int subs = a.hq / G;                 // work items per (row, split)
-  const int item_idx = f / subs;
-  const int hq0 = (f - item_idx * subs) * G; // first query head of this work item
-  const int g = hq0 / a.group;               // the kv head those heads read
+  const int item_idx = f / a.hkv;
+  const int g = f - item_idx * a.hkv;        // the kv head of this work item
+  const int hq0 = g * G;                     // its first query head
   const DecodeItem it = a.items[item_idx];
 
   const int t0 = it.split * a.kv_split;
   const int t1 = min(it.n_keys, t0 + a.kv_split);
+  const int nk = t1 - t0;                    // >= 1
+  const int nk_pad = (nk + HT - 1) / HT * HT;
   const int32_t* bt = a.block_tables + static_cast<int64_t>(it.seq) * a.max_blocks;
   bool bad = false;
 
   // an out-of-pool block id marks the item bad and is replaced by slot 0, so no load ever
   // leaves the pool
-  for (int k = tid; k < t1 - t0; k += 256) {
-    const int pos = t0 + k;
+  for (int k = tid; k < nk_pad; k += 256) {
+    const int pos = t0 + min(k, nk - 1);
     int j, off;
     if (a.bs_log2 >= 0) {
       j = pos >> a.bs_log2;
@@ -88,53 +176,67 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
     const int b = bt[j];
     const bool ok = static_cast<unsigned>(b) < static_cast<unsigned>(a.num_blocks);
     bad |= !ok;
-    s_slot[k] = ok ? b * a.block_size + off : 0;
+    const int w = k % HT;
+    s_slot[(k - w) + (w % TPI) * NI + w / TPI] = ok ? static_cast<uint32_t>(b * a.block_size + off) : 0u;
   }
   const uint4* qsrc = reinterpret_cast<const uint4*>(
       static_cast<const char*>(a.q) + (static_cast<int64_t>(it.row) * a.hq + hq0) * ROWB);
   for (int c = tid; c < G * LPT; c += 256) s_q[c] = qsrc[c];
   __syncthreads();
 
-  const uint4* __restrict__ kp = static_cast<const uint4*>(a.k_cache);
-  const uint4* __restrict__ vp = static_cast<const uint4*>(a.v_cache);
-  const int64_t slot_stride = static_cast<int64_t>(a.hkv) * LPT;  // uint4 per slot
-  const int head_off = g * LPT;
   const int grp = lane / LPT;               // P.V stage / loads: key group of this lane
   const int cl = lane & (LPT - 1);          // P.V stage / loads: chunk of this lane
-  const int kk = lane >> 1;                 // score stage: key of this lane
-  const int hf = lane & 1;                  // score stage: half of D of this lane
-  uint4* sk = s_k[wave];
+  const int kk = lane / SPL;                // score stage: key of this lane
+  const int hf = lane % SPL;                // score stage: part of D of this lane
+  const uint64_t slot_bytes = static_cast<uint64_t>(a.hkv) * ROWB;
+  const char* kbase = static_cast<const char*>(a.k_cache) + g * ROWB + cl * 16;
+  const char* vbase = static_cast<const char*>(a.v_cache) + g * ROWB + cl * 16;
+  uint4* sk = s_k + wave * HT * LPT;
   float* sp = s_p[wave];
 
-  float m[G], l[G], acc[G][EPL];
+  float m[G], lo[GO], acc[G][EPL];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m[h] = -INFINITY;
-    l[h] = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
+#pragma unroll
+  for (int j = 0; j < GO; ++j) lo[j] = 0.f;
 
   auto load = [&](uint4 (&kr)[NI], uint4 (&vr)[NI], int hs) {
-    const int n = min(HT, t1 - hs);
-    const int* slots = s_slot + (hs - t0);
+    const uint32_t* sl = s_slot + (hs - t0) + grp * NI;
+    constexpr int SV = NI % 4 == 0 ? 4 : 2;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int tok = min(i * TPI + grp, n - 1);
-      const int64_t off = static_cast<int64_t>(slots[tok]) * slot_stride + head_off + cl;
-      kr[i] = load_nt(kp + off);
-      vr[i] = load_nt(vp + off);
+    for (int i4 = 0; i4 < NI; i4 += SV) {
+      uint32_t ss[4];
+      if constexpr (SV == 4) {
+        const uint4 s4 = *reinterpret_cast<const uint4*>(sl + i4);
+        ss[0] = s4.x; ss[1] = s4.y; ss[2] = s4.z; ss[3] = s4.w;
+      } else {
+        const uint2 s2 = *reinterpret_cast<const uint2*>(sl + i4);
+        ss[0] = s2.x; ss[1] = s2.y;
+      }
+#pragma unroll
+      for (int u = 0; u < SV; ++u) {
+        const uint64_t off = static_cast<uint64_t>(ss[u]) * slot_bytes;
+        kr[i4 + u] = load_nt(reinterpret_cast<const uint4*>(kbase + off));
+        vr[i4 + u] = load_nt(reinterpret_cast<const uint4*>(vbase + off));
+      }
     }
   };
 
   auto compute = [&](const uint4 (&kr)[NI], const uint4 (&vr)[NI], int hs) {
+    // q chunks are re-read from LDS in every tile: holding them in registers across the loop
+    // would cost more registers than the K/V buffers
+    asm volatile("" ::: "memory");
     const int n = min(HT, t1 - hs);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int tok = i * TPI + grp;
       sk[tok * LPT + (cl ^ (tok & (LPT - 1)))] = kr[i];
     }
-    // scores: lanes 2k and 2k+1 hold halves of key k's dot products
+    // scores: lanes SPL k .. SPL k + SPL - 1 hold parts of key k's dot products
     float s[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) s[h] = 0.f;
@@ -146,17 +248,15 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
       for (int h = 0; h < G; ++h) {
         const uint4 qc = s_q[h * LPT + c];
         if constexpr (BF) {
-          float t = dot2_bf16(qc.x, kc.x, 0.f);
-          t = dot2_bf16(qc.y, kc.y, t);
-          t = dot2_bf16(qc.z, kc.z, t);
-          t = dot2_bf16(qc.w, kc.w, t);
-          s[h] += t;
+          s[h] = dot2_bf16(qc.x, kc.x, s[h]);
+          s[h] = dot2_bf16(qc.y, kc.y, s[h]);
+          s[h] = dot2_bf16(qc.z, kc.z, s[h]);
+          s[h] = dot2_bf16(qc.w, kc.w, s[h]);
         } else {
-          float t = __uint_as_float(qc.x) * __uint_as_float(kc.x);
-          t = fmaf(__uint_as_float(qc.y), __uint_as_float(kc.y), t);
-          t = fmaf(__uint_as_float(qc.z), __uint_as_float(kc.z), t);
-          t = fmaf(__uint_as_float(qc.w), __uint_as_float(kc.w), t);
-          s[h] += t;
+          s[h] = fmaf(__uint_as_float(qc.x), __uint_as_float(kc.x), s[h]);
+          s[h] = fmaf(__uint_as_float(qc.y), __uint_as_float(kc.y), s[h]);
+          s[h] = fmaf(__uint_as_float(qc.z), __uint_as_float(kc.z), s[h]);
+          s[h] = fmaf(__uint_as_float(qc.w), __uint_as_float(kc.w), s[h]);
         }
       }
     }
@@ -166,20 +266,38 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       s[h] += dpp_xor1(s[h]);
+      if constexpr (SPL == 4) s[h] += dpp_xor2(s[h]);
       s[h] = valid ? s[h] * a.scale_log2e : -INFINITY;
-      const float mn = fmaxf(m[h], wave_max_pairs(s[h]));
+      const float mn = fmaxf(m[h], max_over_groups<SPL>(s[h]));
       alpha[h] = fast_exp2(m[h] - mn);
       moved |= alpha[h] != 1.f;
       m[h] = mn;
     }
-    // p of (key kk, head h) is formed by the lane of that key with hf == h % 2
+    // p of (key kk, head h) is formed by the lane of that key with hf == h % SPL (heads
+    // below SPL: by the lanes hf < G, the others idle)
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      if ((h & 1) == hf) {
-        const float p = fast_exp2(s[h] - m[h]);
-        l[h] = l[h] * alpha[h] + p;
-        sp[kk * G + h] = p;
+    for (int j = 0; j < GO; ++j) {
+      float sv, mv, av;
+      if constexpr (G >= SPL) {
+        sv = s[j * SPL]; mv = m[j * SPL]; av = alpha[j * SPL];
+#pragma unroll
+        for (int r = 1; r < SPL; ++r) {
+          sv = hf == r ? s[j * SPL + r] : sv;
+          mv = hf == r ? m[j * SPL + r] : mv;
+          av = hf == r ? alpha[j * SPL + r] : av;
+        }
+      } else {
+        sv = s[0]; mv = m[0]; av = alpha[0];
+#pragma unroll
+        for (int r = 1; r < G; ++r) {
+          sv = hf == r ? s[r] : sv;
+          mv = hf == r ? m[r] : mv;
+          av = hf == r ? alpha[r] : av;
+        }
       }
+      const float p = fast_exp2(sv - mv);
+      lo[j] = lo[j] * av + p;
+      if (G >= SPL || hf < G) sp[kk * G + j * SPL + hf] = p;
     }
     // rescale only when some head's max moved (multiplying by exactly 1 changes nothing)
     if (__any(moved)) {
@@ -193,8 +311,16 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
     for (int i = 0; i < NI; ++i) {
       const int tok = i * TPI + grp;
       float pp[G];
+      if constexpr (G >= 4) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) pp[h] = sp[tok * G + h];
+        for (int h4 = 0; h4 < G; h4 += 4) {
+          const float4 t = *reinterpret_cast<const float4*>(sp + tok * G + h4);
+          pp[h4] = t.x; pp[h4 + 1] = t.y; pp[h4 + 2] = t.z; pp[h4 + 3] = t.w;
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < G; ++h) pp[h] = sp[tok * G + h];
+      }
       float vf[EPL];
       if constexpr (BF) {
         vf[0] = bf16_lo(vr[i].x); vf[1] = bf16_hi(vr[i].x);
@@ -212,7 +338,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
     }
   };
 
-  // this wave's half tiles: hs = t0 + HT * (wave + 4 j), j = 0, 1, ...
+  // this wave's tiles: hs = t0 + HT * (wave + 4 j), j = 0, 1, ...
   constexpr int kStep = kDecodeWaves * HT;
   uint4 ka[NI], va[NI], kb[NI], vb[NI];
   int hs = t0 + wave * HT;
@@ -228,21 +354,18 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
     hs = hs2;
   }
 
-  // wave totals: l over keys (lanes), acc over the TPI key groups
+  // wave totals: l over the lanes that formed it, acc over the TPI key groups
 #pragma unroll
-  for (int h = 0; h < G; ++h) l[h] = wave_sum(l[h]);
+  for (int j = 0; j < GO; ++j) lo[j] = sum_same_class<SPL>(lo[j]);
 #pragma unroll
-  for (int k = LPT; k < 64; k <<= 1)
+  for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], k);
+    for (int e = 0; e < EPL; ++e) acc[h][e] = sum_key_groups<LPT>(acc[h][e]);
 
   const bool bad_row = __syncthreads_or(bad) != 0;  // also: every wave is done with s_k
-  float* mg_acc = reinterpret_cast<float*>(&s_k[0][0]);      // [4][G][D]
+  float* mg_acc = reinterpret_cast<float*>(s_k);             // [4][G][D]
   float* mg_m = mg_acc + kDecodeWaves * G * D;                // [4][G]
   float* mg_l = mg_m + kDecodeWaves * G;                      // [4][G]
-  static_assert(sizeof(s_k) >= sizeof(float) * kDecodeWaves * G * (D + 2), "merge scratch");
   if (lane < LPT) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
@@ -251,10 +374,11 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
   }
   if (lane == 0) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      mg_m[wave * G + h] = m[h];
-      mg_l[wave * G + h] = l[h];
-    }
+    for (int h = 0; h < G; ++h) mg_m[wave * G + h] = m[h];
+  }
+  if (lane < (G >= SPL ? SPL : G)) {
+#pragma unroll
+    for (int j = 0; j < GO; ++j) mg_l[wave * G + j * SPL + lane] = lo[j];
   }
   __syncthreads();
   for (int idx = tid; idx < G * D; idx += 256) {
@@ -270,16 +394,18 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
       num = fmaf(fw, mg_acc[(w * G + h) * D + d], num);
       den = fmaf(fw, mg_l[w * G + h], den);
     }
-    if (bad_row) num = den = __builtin_nanf("");
+    const uint32_t nan_bits = 0x7fc00000u;
     const int hq = hq0 + h;
     if (it.part < 0) {
-      a.out[(static_cast<int64_t>(it.row) * a.hq + hq) * D + d] = num / den;
+      const float o = num / den;
+      a.out[(static_cast<int64_t>(it.row) * a.hq + hq) * D + d] =
+          __uint_as_float(bad_row ? nan_bits : __float_as_uint(o));
     } else {
       const int64_t p = static_cast<int64_t>(it.part + it.split) * a.hq + hq;
-      a.part_acc[p * D + d] = num;
+      a.part_acc[p * D + d] = __uint_as_float(bad_row ? nan_bits : __float_as_uint(num));
       if (d == 0) {
         a.part_m[p] = M;
-        a.part_l[p] = den;
+        a.part_l[p] = __uint_as_float(bad_row ? nan_bits : __float_as_uint(den));
       }
     }
   }
@@ -293,16 +419,32 @@ bool decode_supported(int head_dim, int group) {
          (group == 1 || group == 2 || group == 4 || group == 8);
 }
 
-// query heads per decode work item
-static int decode_heads_per_item(int group) { return group < 4 ? group : 4; }
-
+// Keys per tile and waves per SIMD of each kernel instance (measured on the batched, long-
+// context and prefix-shared decode steps): a bf16 group of 4 at head_dim 128 runs 16-key tiles
+// at three waves per SIMD (160 registers); a group of 8 at head_dim 128 runs 16-key tiles at
+// two waves (its 64 accumulators per lane leave no room for more); other bf16 instances run
+// 32-key tiles at two waves; float32 (twice the bytes per row) one wave.
+template <int D, bool BF, int G>
+constexpr int tile_keys() {
+  return (BF && D == 128 && G >= 4) ? 16 : (BF && D == 64 && G == 4) ? 16 : 32;
+}
+template <int D, bool BF, int G>
+constexpr int waves_per_simd() {
+  return !BF ? 1 : (G == 4 ? 3 : 2);
+}
+template <int D, bool BF, int G>
+static void launch_one(const DecodeArgs& a, uint32_t grid, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_split_kernel<D, G, BF, tile_keys<D, BF, G>(), waves_per_simd<D, BF, G>()>),
+                     dim3(grid), dim3(256), 0, stream, a);
+}
 template <int D, bool BF>
-static hipError_t launch_decode_d(const DecodeArgs& a, uint32_t grid, int gi,
+static hipError_t launch_decode_d(const DecodeArgs& a, uint32_t grid, int group,
                                   hipStream_t stream) {
-  switch (gi) {
-    case 1: hipLaunchKernelGGL((decode_split_kernel<D, 1, BF>), dim3(grid), dim3(256), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((decode_split_kernel<D, 2, BF>), dim3(grid), dim3(256), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((decode_split_kernel<D, 4, BF>), dim3(grid), dim3(256), 0, stream, a); break;
+  switch (group) {
+    case 1: launch_one<D, BF, 1>(a, grid, stream); break;
+    case 2: launch_one<D, BF, 2>(a, grid, stream); break;
+    case 4: launch_one<D, BF, 4>(a, grid, stream); break;
+    case 8: launch_one<D, BF, 8>(a, grid, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -310,17 +452,16 @@ static hipError_t launch_decode_d(const DecodeArgs& a, uint32_t grid, int gi,
 
 hipError_t launch_decode(const DecodeArgs& a, int64_t n_items, int head_dim, int group,
                          bool bf16, hipStream_t stream) {
-  const int gi = decode_heads_per_item(group);
-  const int64_t grid64 = n_items * (a.hq / gi);
+  const int64_t grid64 = n_items * a.hkv;
   if (grid64 == 0) return hipSuccess;
   if (grid64 > 0x7fffffffLL || a.group != group) return hipErrorInvalidValue;
   const uint32_t grid = static_cast<uint32_t>(grid64);
   if (head_dim == 64)
-    return bf16 ? launch_decode_d<64, true>(a, grid, gi, stream)
-                : launch_decode_d<64, false>(a, grid, gi, stream);
+    return bf16 ? launch_decode_d<64, true>(a, grid, group, stream)
+                : launch_decode_d<64, false>(a, grid, group, stream);
   if (head_dim == 128)
-    return bf16 ? launch_decode_d<128, true>(a, grid, gi, stream)
-                : launch_decode_d<128, false>(a, grid, gi, stream);
+    return bf16 ? launch_decode_d<128, true>(a, grid, group, stream)
+                : launch_decode_d<128, false>(a, grid, group, stream);
   return hipErrorInvalidValue;
 }
 

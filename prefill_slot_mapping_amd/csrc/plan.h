@@ -6,7 +6,7 @@
 
 namespace pkv {
 
-// Keys per decode tile: one key per lane of a 64-wide wavefront in the score stage.
+// Granularity of kv_split: a multiple of every decode tile (16 or 32 keys) times the waves.
 constexpr int kDecodeTile = 64;
 // Waves per decode workgroup; tile i of a split is handled by wave i % kDecodeWaves.
 constexpr int kDecodeWaves = 4;

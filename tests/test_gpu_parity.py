@@ -70,7 +70,7 @@ def test_small_configs_match_oracle_and_pools_are_bit_exact(name):
 
 
 EDGE = [
-    # (dtype, Hq, Hkv, D, BS, sequences (ctx, q_len))
+    # (dtype, Hq, Hkv, D, BS, sequences (ctx, q_len)[, spec keywords])
     ("bf16", 8, 2, 128, 16, [(1, 1), (2, 2), (16, 1), (17, 17), (513, 1), (1024, 1), (1025, 1),
                              (600, 0), (700, 130), (64, 64), (65, 1), (1100, 70)]),
     ("bf16", 4, 4, 128, 1, [(1, 1), (5, 5), (300, 1), (70, 3)]),
@@ -80,14 +80,23 @@ EDGE = [
     ("f32", 8, 1, 128, 16, [(1, 1), (600, 1), (45, 45), (130, 9)]),
     ("f32", 4, 2, 64, 16, [(17, 1), (33, 1), (64, 1), (100, 1), (40, 12)]),
     ("f32", 2, 2, 64, 3, [(10, 10), (1030, 1), (77, 1)]),
+    # every decode kernel instance: bf16 groups of 4 and 8 at head_dim 64 and 128 (16- and
+    # 32-key tiles), and the smallest and largest KV splits
+    ("bf16", 16, 4, 64, 16, [(1, 1), (300, 1), (1029, 1), (50, 20), (2100, 1)]),
+    ("bf16", 32, 4, 64, 16, [(2, 1), (513, 1), (1500, 1), (40, 9)]),
+    ("bf16", 32, 8, 128, 16, [(1, 1), (64, 1), (65, 1), (3000, 1), (90, 31)], {"kv_split": 64}),
+    ("bf16", 64, 8, 128, 32, [(17, 1), (4097, 1), (2049, 1)], {"kv_split": 2048}),
 ]
 
 
 @pytest.mark.parametrize("case", EDGE, ids=[f"{c[0]}-G{c[1] // c[2]}-D{c[3]}-BS{c[4]}"
+                                            + (f"-split{c[6]['kv_split']}" if len(c) > 6 else "")
                                             for c in EDGE])
 def test_edge_cases_match_oracle(case):
-    dt, hq, hkv, d, bs, seqs = case
-    w = make_workload(explicit_spec(f"edge-{dt}-{hq}-{hkv}-{d}-{bs}", dt, hq, hkv, d, bs, seqs))
+    dt, hq, hkv, d, bs, seqs = case[:6]
+    kw = case[6] if len(case) > 6 else {}
+    w = make_workload(explicit_spec(f"edge-{dt}-{hq}-{hkv}-{d}-{bs}", dt, hq, hkv, d, bs, seqs,
+                                    **kw))
     check_step(w)
 
 
