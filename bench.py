@@ -43,6 +43,9 @@ def _parse():
     ap.add_argument("--consistent", default="batched-bf16-decode,mixed-ragged-step",
                     help="comma-separated workloads also timed in the phase-consistent mode, "
                          "reported under 'extra' as '<name>/phase-consistent'")
+    ap.add_argument("--kernel-events", choices=("timed", "separate"), default="timed",
+                    help="take the per-kernel HIP-event times inside the timed steps (default) "
+                         "or in a second pass of the same steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 1 GiB device copies (scale reference for PMC byte "
                          "counters) and exit")
@@ -74,7 +77,8 @@ def _kv_bytes(w):
     return acc.decode_kv_bytes(w.ctx_lens, w.spec.Hkv, w.spec.D, w.elem_bytes)
 
 
-def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False):
+def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
+                  kernel_events="timed"):
     """Build the step, then time `steps` whole steps; returns a result dict. With
     phase_consistent the attention runs with PKV_ATTN_PHASE_CONSISTENT (decode rows on the
     prefill tile path, bitwise equal to the same tokens inside prefill chunks)."""
@@ -124,7 +128,12 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False):
             gc_pauses.append(time.perf_counter() - _t[0])
 
     gc.callbacks.append(on_gc)
-    pkv.profile_enable(True)
+    # per-kernel device time: the library brackets each launch with HIP events on its launch
+    # stream, inside the timed region (kernel_events="timed") or in a second, untimed pass of
+    # the same steps (kernel_events="separate", so that the event records do not sit between
+    # the timed launches)
+    if kernel_events == "timed":
+        pkv.profile_enable(True)
     torch.cuda.synchronize(device)
     host_ends = []
     t0 = time.perf_counter()
@@ -136,8 +145,13 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False):
     gc.callbacks.remove(on_gc)
     gc.unfreeze()
     host_ms = np.diff(np.array([t0] + host_ends)) * 1e3
+    if kernel_events != "timed":
+        pkv.profile_enable(True)
+        for _ in range(steps):
+            step()
     kern = {k: pkv.profile_read(k) for k in ("write_kv", "prefill", "decode", "merge")}
     pkv.profile_enable(False)
+    torch.cuda.synchronize(device)
     assert np.array_equal(slots_np[:w.T], gst.new_slots)
 
     ms_step = dt / steps * 1e3
@@ -249,17 +263,19 @@ def main():
         return
     pkv.lib()   # fail loudly if the HIP library is not built
 
-    main_res = time_workload(args.workload, args.steps, args.warmup)
+    main_res = time_workload(args.workload, args.steps, args.warmup,
+                             kernel_events=args.kernel_events)
     w = main_res["_w"]
     extra = {}
     for name in [n for n in args.extra.split(",") if n and n != args.workload]:
-        r = time_workload(name, args.steps, args.warmup)
+        r = time_workload(name, args.steps, args.warmup, kernel_events=args.kernel_events)
         r.pop("_gst"); r.pop("_w")
         extra[name] = r
         torch.cuda.empty_cache()
 
     for name in [n for n in args.consistent.split(",") if n]:
-        r = time_workload(name, args.steps, args.warmup, phase_consistent=True)
+        r = time_workload(name, args.steps, args.warmup, phase_consistent=True,
+                          kernel_events=args.kernel_events)
         r.pop("_gst"); r.pop("_w")
         extra[name + "/phase-consistent"] = r
         torch.cuda.empty_cache()
