@@ -4,8 +4,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--extra A,B]
 
 One step = one pass of the whole path over one synthetic batch: the step's slot mapping on the
-host (pkv_slot_mapping_step), the slots' upload, the KV append (pkv_write_kv), then the
-attention call (host work planning + decode split pass + split merge + prefill tiles). Inputs
+host (pkv_slot_mapping_step), then one pkv_write_kv_attention call (host work planning, one
+host-to-device copy of the slots and work lists, the KV append, the prefill tiles, the decode
+split pass and the split merge). Inputs
 are resident in HBM before timing starts; the timed region is bracketed by device
 synchronisation. The headline workload is the batched bf16 decode step (64 sequences,
 lognormal lengths with median 2048, Hq 32, Hkv 8, D 128, block 16), reported as algorithmic
@@ -25,6 +26,7 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+EVENT_STRIDE = 5                 # timed steps per step whose dominant kernel is bracketed
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
@@ -32,8 +34,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 def _parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="batched-bf16-decode")
     ap.add_argument("--extra", default="mixed-ragged-step",
                     help="comma-separated workloads timed the same way, reported under 'extra'")
@@ -95,22 +97,24 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
     t_build = time.time() - t_build
     s = w.spec
     starts, n_new = _step_inputs(w, gst)
-    slots_host = torch.empty(w.T, dtype=torch.int32).pin_memory()
-    slots_np = slots_host.numpy()
-    slots_dev = torch.empty(w.T, dtype=torch.int32, device=device)
-    ws_bytes = pkv.attention_workspace_size(w.ctx_lens, w.cu_seqlens_q, s.Hq, s.Hkv, s.D,
-                                            s.kv_split, pkv.PKV_BF16 if s.dtype == "bf16"
-                                            else pkv.PKV_F32, phase_consistent)
+    slots_np = np.zeros(max(w.T, 1), dtype=np.int32)
+    ctx_np = np.ascontiguousarray(w.ctx_lens, dtype=np.int32)
+    cu_np = np.ascontiguousarray(w.cu_seqlens_q, dtype=np.int32)
+    bt_np = np.ascontiguousarray(gst.block_tables, dtype=np.int32)
+    ws_bytes = pkv.write_kv_attention_workspace_size(
+        ctx_np, cu_np, s.Hq, s.Hkv, s.D, w.T, s.kv_split,
+        pkv.PKV_BF16 if s.dtype == "bf16" else pkv.PKV_F32, phase_consistent)
     workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=device)
     out = torch.empty((w.T, s.Hq, s.D), dtype=torch.float32, device=device)
 
     def step():
-        pkv.slot_mapping_step(gst.allocator, gst.block_tables, s.BS, starts, n_new, out=slots_np)
-        slots_dev.copy_(slots_host, non_blocking=True)
-        pkv.write_kv(gst.k_new, gst.v_new, slots_dev, gst.k_cache, gst.v_cache)
-        pkv.attention(gst.q, gst.k_cache, gst.v_cache, gst.block_tables_dev, w.ctx_lens,
-                      w.cu_seqlens_q, w.scale, out=out, workspace=workspace,
-                      kv_split=s.kv_split, phase_consistent=phase_consistent)
+        # host slot mapping of the step's new rows, then one library call: the slots and the
+        # attention work lists go to the device in one copy, then append, attention, merge
+        sl = pkv.slot_mapping_step(gst.allocator, bt_np, s.BS, starts, n_new, out=slots_np)
+        pkv.write_kv_attention(gst.q, gst.k_new, gst.v_new, sl, gst.k_cache, gst.v_cache,
+                               gst.block_tables_dev, ctx_np, cu_np, w.scale, out=out,
+                               workspace=workspace, kv_split=s.kv_split,
+                               phase_consistent=phase_consistent)
 
     for _ in range(warmup):
         step()
@@ -127,17 +131,22 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
         else:
             gc_pauses.append(time.perf_counter() - _t[0])
 
+    # The dominant kernel's device time is taken inside the timed steps: the library brackets
+    # its launch with HIP events on the launch stream in every EVENT_STRIDE-th step (an event
+    # record costs the stream a few microseconds, so bracketing every launch of every kernel
+    # would stretch the step it times). Every kernel's time is then taken in a second, untimed
+    # pass of the same steps with all launches bracketed.
+    dominant = "decode" if (w.q_lens == 1).any() and not phase_consistent else "prefill"
     gc.callbacks.append(on_gc)
-    # per-kernel device time: the library brackets each launch with HIP events on its launch
-    # stream, inside the timed region (kernel_events="timed") or in a second, untimed pass of
-    # the same steps (kernel_events="separate", so that the event records do not sit between
-    # the timed launches)
     if kernel_events == "timed":
+        pkv.profile_set_kinds([])
         pkv.profile_enable(True)
     torch.cuda.synchronize(device)
     host_ends = []
     t0 = time.perf_counter()
-    for _ in range(steps):
+    for i in range(steps):
+        if kernel_events == "timed":
+            pkv.profile_set_kinds([dominant] if i % EVENT_STRIDE == 0 else [])
         step()
         host_ends.append(time.perf_counter())
     torch.cuda.synchronize(device)
@@ -145,11 +154,17 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
     gc.callbacks.remove(on_gc)
     gc.unfreeze()
     host_ms = np.diff(np.array([t0] + host_ends)) * 1e3
-    if kernel_events != "timed":
-        pkv.profile_enable(True)
-        for _ in range(steps):
-            step()
-    kern = {k: pkv.profile_read(k) for k in ("write_kv", "prefill", "decode", "merge")}
+    timed = {}
+    if kernel_events == "timed":
+        tms, tn = pkv.profile_read(dominant)
+        timed = {"kernel": dominant, "launches_bracketed": tn,
+                 "avg_ms": tms / tn if tn else None}
+    kinds = ("write_kv", "prefill", "decode", "merge")
+    pkv.profile_set_kinds(list(kinds))
+    pkv.profile_enable(True)
+    for _ in range(steps):
+        step()
+    kern = {k: pkv.profile_read(k) for k in kinds}
     pkv.profile_enable(False)
     torch.cuda.synchronize(device)
     assert np.array_equal(slots_np[:w.T], gst.new_slots)
@@ -170,6 +185,7 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
         "gc_pauses_in_timed_region": {"count": len(gc_pauses),
                                       "max_ms": max(gc_pauses, default=0.0) * 1e3},
         "kernels_ms": {k: (v[0] / v[1] if v[1] else None) for k, v in kern.items()},
+        "timed_region_kernel": timed,
         "kernel_launches": {k: v[1] for k, v in kern.items()},
     }
     t_roof = max((kv + app) / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12))
@@ -280,7 +296,8 @@ def main():
         extra[name + "/phase-consistent"] = r
         torch.cuda.empty_cache()
 
-    dec_ms = main_res["kernels_ms"]["decode"]
+    tr = main_res["timed_region_kernel"]
+    dec_ms = tr.get("avg_ms") if tr.get("kernel") == "decode" else main_res["kernels_ms"]["decode"]
     achieved = main_res["decode_kv_bytes"] / (dec_ms * 1e-3) / 1e9 if dec_ms else None
     roofline = {"bound": "hbm", "kernel": "decode_split_kernel", "achieved": achieved,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -205,6 +205,41 @@ int32_t pkv_attention_ex(const void* q, const void* k_cache, const void* v_cache
                          int32_t kv_split, int32_t dtype, uint32_t flags, float* out,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- fused step: KV append + attention in one call [P3 "Design > paged.py": the
+ *      TritonPagedAttention contract takes the slot mapping together with q, the cache
+ *      blocks, block tables, cu_seqlens_q and ctx_lens; it writes the new K/V and returns
+ *      [T, H, D]] -----------------------------------------------------------------------
+ * Same result as pkv_write_kv(k_new, v_new, <slots>, n_rows, k_cache, v_cache, ...) followed
+ * by pkv_attention_ex(..., flags, ...) on the same stream, but the slots are read from host
+ * memory and travel to the device in the same host-to-device copy as the attention work lists
+ * (one copy per step instead of two).
+ *   slots_host:   host int32 [n_rows]; row t of k_new / v_new ([n_rows, num_kv_heads,
+ *                 head_dim], device, dtype) goes to slot slots_host[t]. A negative slot skips
+ *                 its row; a slot >= num_blocks * block_size is PKV_ERR_INVALID (checked before
+ *                 anything is enqueued). Duplicate non-negative slots leave the destination
+ *                 undefined (pkv_validate_slots checks a host array). The array is copied
+ *                 before the call returns.
+ *   workspace:    at least pkv_write_kv_attention_workspace_size() bytes (the attention
+ *                 workspace plus the staged slots); same ownership rules as pkv_attention.
+ * Every other argument as in pkv_write_kv and pkv_attention_ex. n_rows == 0 is the plain
+ * attention call; T == 0 is the plain KV append.
+ * Errors: as pkv_write_kv and pkv_attention_ex. */
+int32_t pkv_write_kv_attention_workspace_size(const int32_t* ctx_lens_host,
+                                              const int32_t* cu_seqlens_q_host, int32_t B,
+                                              int32_t num_q_heads, int32_t num_kv_heads,
+                                              int32_t head_dim, int32_t kv_split, int32_t dtype,
+                                              uint32_t flags, int32_t n_rows, size_t* bytes);
+
+int32_t pkv_write_kv_attention(const void* q, const void* k_new, const void* v_new,
+                               const int32_t* slots_host, int32_t n_rows, void* k_cache,
+                               void* v_cache, const int32_t* block_tables_dev,
+                               int32_t max_blocks, const int32_t* ctx_lens_host,
+                               const int32_t* cu_seqlens_q_host, int32_t B, int32_t T,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int32_t num_blocks, float scale,
+                               int32_t kv_split, int32_t dtype, uint32_t flags, float* out,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- diagnostics: per-kernel device time ------------------------------------------------
  * While enabled, every kernel launched by pkv_write_kv / pkv_attention is bracketed by two HIP
  * events recorded on its launch stream (the library owns the events). pkv_profile_read waits
@@ -214,6 +249,11 @@ int32_t pkv_attention_ex(const void* q, const void* k_cache, const void* v_cache
  * Not thread-safe with concurrent launches from several host threads. */
 int32_t pkv_profile_enable(int32_t enable);
 int32_t pkv_profile_read(int32_t kernel_kind, double* total_ms, int64_t* launches);
+/* Kernel kinds bracketed from now on while profiling is enabled: bit k = kind k (default all,
+ * 0xF); records already taken are kept. Each event record costs the stream a few
+ * microseconds, so a caller timing whole steps can bracket only the kernel it reports, or
+ * only some of its launches. PKV_ERR_INVALID for bits above kind 3. */
+int32_t pkv_profile_set_kinds(uint32_t kinds);
 
 #ifdef __cplusplus
 }

@@ -110,6 +110,13 @@ _SIGS = {
     "pkv_attention": ([_vp, _vp, _vp, _vp, _i32, _pi32, _pi32, _i32, _i32, _i32, _i32, _i32,
                        _i32, _i32, ctypes.c_float, _i32, _i32, _vp, _vp, ctypes.c_size_t, _vp],
                       _i32),
+    "pkv_write_kv_attention_workspace_size": ([_pi32, _pi32, _i32, _i32, _i32, _i32, _i32,
+                                               _i32, ctypes.c_uint32, _i32,
+                                               ctypes.POINTER(ctypes.c_size_t)], _i32),
+    "pkv_write_kv_attention": ([_vp, _vp, _vp, _pi32, _i32, _vp, _vp, _vp, _i32, _pi32, _pi32,
+                                _i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32,
+                                _i32, ctypes.c_uint32, _vp, _vp, ctypes.c_size_t, _vp], _i32),
+    "pkv_profile_set_kinds": ([ctypes.c_uint32], _i32),
     "pkv_profile_enable": ([_i32], _i32),
     "pkv_profile_read": ([_i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)], _i32),
 }
@@ -349,11 +356,76 @@ def attention(q, k_cache, v_cache, block_tables, ctx_lens, cu_seqlens_q, scale: 
     return out
 
 
+def write_kv_attention_workspace_size(ctx_lens, cu_seqlens_q, num_q_heads: int,
+                                     num_kv_heads: int, head_dim: int, n_rows: int,
+                                     kv_split: int = 512, dtype: int = PKV_BF16,
+                                     phase_consistent: bool = False) -> int:
+    ctx = _host_i32(ctx_lens)
+    cu = _host_i32(cu_seqlens_q)
+    out = ctypes.c_size_t(0)
+    flags = PKV_ATTN_PHASE_CONSISTENT if phase_consistent else 0
+    _check(lib().pkv_write_kv_attention_workspace_size(
+        _ptr(ctx), _ptr(cu), ctx.size, int(num_q_heads), int(num_kv_heads), int(head_dim),
+        int(kv_split), int(dtype), flags, int(n_rows), ctypes.byref(out)))
+    return int(out.value)
+
+
+def write_kv_attention(q, k_new, v_new, slots, k_cache, v_cache, block_tables, ctx_lens,
+                       cu_seqlens_q, scale: float, out=None, workspace=None, kv_split: int = 512,
+                       stream=None, phase_consistent: bool = False):
+    """pkv_write_kv_attention: the KV append of k_new / v_new [T_w, Hkv, D] through host slots
+    [T_w] and the attention over the step in one call (one host-to-device copy); returns out.
+    """
+    import torch
+    _need_cuda(q, k_new, v_new, k_cache, v_cache, block_tables)
+    if block_tables.dtype != torch.int32:
+        raise ValueError("block_tables must be int32")
+    sl = slots if isinstance(slots, np.ndarray) and slots.dtype == np.int32 and \
+        slots.flags.c_contiguous else _host_i32(slots)
+    ctx = _host_i32(ctx_lens)
+    cu = _host_i32(cu_seqlens_q)
+    T, hq, d = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    if d2 != d or v_cache.shape != k_cache.shape or q.dtype != k_cache.dtype:
+        raise ValueError("q / pool shape or dtype mismatch")
+    n_rows = int(k_new.shape[0])
+    if sl.size != n_rows or v_new.shape != k_new.shape:
+        raise ValueError("slots / k_new / v_new row counts differ")
+    B = ctx.size
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B, max_blocks]")
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty((T, hq, d), dtype=torch.float32, device=q.device)
+    _need_cuda(out)
+    ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if workspace is None:
+        need = write_kv_attention_workspace_size(ctx, cu, hq, hkv, d, n_rows, kv_split, dt,
+                                                 phase_consistent)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        ws_have = workspace.numel()
+    flags = PKV_ATTN_PHASE_CONSISTENT if phase_consistent else 0
+    _check(lib().pkv_write_kv_attention(
+        q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), _ptr(sl), n_rows, k_cache.data_ptr(),
+        v_cache.data_ptr(), block_tables.data_ptr(), int(block_tables.shape[1]), _ptr(ctx),
+        _ptr(cu), B, T, hq, hkv, d, bs, nb, float(scale), int(kv_split), dt, flags,
+        out.data_ptr(), workspace.data_ptr(), ws_have, _stream_ptr(q, stream)))
+    return out
+
+
 # ---- diagnostics ---------------------------------------------------------------------------
 
 def profile_enable(on: bool = True) -> None:
     """Start (clearing old records) or stop per-kernel HIP-event timing inside the library."""
     _check(lib().pkv_profile_enable(1 if on else 0))
+
+
+def profile_set_kinds(kinds: Sequence[str]) -> None:
+    """Bracket only these kernel kinds from now on while profiling is enabled."""
+    mask = 0
+    for k in kinds:
+        mask |= 1 << KERNEL_KINDS[k]
+    _check(lib().pkv_profile_set_kinds(mask))
 
 
 def profile_read(kind: str) -> Tuple[float, int]:

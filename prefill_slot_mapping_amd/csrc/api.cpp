@@ -12,6 +12,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <deque>
 #include <mutex>
 #include <string>
 #include <unordered_map>
@@ -33,17 +34,34 @@ bool valid_dtype(int32_t dt) { return dt == PKV_F32 || dt == PKV_BF16; }
 int elem_bytes(int32_t dt) { return dt == PKV_BF16 ? 2 : 4; }
 
 // ---- pinned staging ring: work lists are built on the host and copied asynchronously ----
+// A ring of pinned buffers per device. Slot n % kRingSlots holds the data of call n until its
+// host-to-device copy has run; before the host rewrites a slot it waits for a fence (an event
+// recorded on the stream of the slot's previous copy) that covers that copy. Fences are
+// recorded every kFenceEvery calls, not every call: each event record costs the stream a few
+// microseconds. A copy left uncovered because its stream was not used again before the slot
+// came round is waited for with a device synchronisation.
+constexpr int kRingSlots = 16;
+constexpr int kFenceEvery = 4;
+
 struct StagingSlot {
   void* host = nullptr;
   size_t cap = 0;
-  hipEvent_t done = nullptr;
-  bool pending = false;
+  int64_t call = -1;            // call whose copy last read this slot (-1: none)
+  hipStream_t stream = nullptr; // the stream of that copy
+};
+
+struct Fence {
+  hipEvent_t ev;
+  hipStream_t stream;
+  int64_t covers;  // every call <= covers made on `stream` was enqueued before ev
 };
 
 struct DeviceRing {
   std::mutex mu;
-  StagingSlot slots[8];
-  int next = 0;
+  StagingSlot slots[kRingSlots];
+  int64_t calls = 0;
+  std::deque<Fence> fences;       // in record order
+  std::vector<hipEvent_t> spare;  // event objects for reuse
 };
 
 std::mutex g_rings_mu;
@@ -61,6 +79,87 @@ DeviceRing* ring_for_current_device(int* dev_out) {
   return r;
 }
 
+// Returns completed fences at the front of the queue to the spare list.
+void drop_completed_fences(DeviceRing* r) {
+  while (!r->fences.empty() && hipEventQuery(r->fences.front().ev) == hipSuccess) {
+    r->spare.push_back(r->fences.front().ev);
+    r->fences.pop_front();
+  }
+}
+
+// Blocks until the copy of call `call` on `stream` has completed.
+hipError_t wait_for_copy(DeviceRing* r, int64_t call, hipStream_t stream) {
+  for (const Fence& f : r->fences) {
+    if (f.stream == stream && f.covers >= call) {
+      hipError_t e = hipEventSynchronize(f.ev);
+      if (e != hipSuccess) return e;
+      drop_completed_fences(r);
+      return hipSuccess;
+    }
+  }
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return e;
+  for (const Fence& f : r->fences) r->spare.push_back(f.ev);
+  r->fences.clear();
+  return hipSuccess;
+}
+
+hipError_t record_fence(DeviceRing* r, hipStream_t stream, int64_t covers) {
+  hipEvent_t ev = nullptr;
+  if (!r->spare.empty()) {
+    ev = r->spare.back();
+    r->spare.pop_back();
+  } else {
+    hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = hipEventRecord(ev, stream);
+  if (e != hipSuccess) {
+    r->spare.push_back(ev);
+    return e;
+  }
+  r->fences.push_back(Fence{ev, stream, covers});
+  if (r->fences.size() > 4 * kRingSlots) drop_completed_fences(r);
+  return hipSuccess;
+}
+
+// Copies `bytes` of host-built data to device memory dst on stream strm through the current
+// device's staging ring; fill(host) writes the data into the staging buffer.
+template <typename Fill>
+int32_t stage_and_copy(void* dst, size_t bytes, hipStream_t strm, const char* what, Fill fill) {
+  int dev = 0;
+  DeviceRing* ring = ring_for_current_device(&dev);
+  if (ring == nullptr) return fail(PKV_ERR_HIP, std::string(what) + ": hipGetDevice failed");
+  std::lock_guard<std::mutex> lk(ring->mu);
+  const int64_t call = ring->calls;
+  StagingSlot& slot = ring->slots[call % kRingSlots];
+  if (slot.call >= 0) {
+    hipError_t e = wait_for_copy(ring, slot.call, slot.stream);
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string(what) + ": staging wait: " + hipGetErrorString(e));
+    slot.call = -1;
+  }
+  if (slot.cap < bytes) {
+    if (slot.host != nullptr) (void)hipHostFree(slot.host);
+    slot.host = nullptr;
+    slot.cap = 0;
+    const size_t want = std::max<size_t>(bytes, 1 << 16);
+    hipError_t e = hipHostMalloc(&slot.host, want, hipHostMallocDefault);
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string(what) + ": pinned staging: " + hipGetErrorString(e));
+    slot.cap = want;
+  }
+  fill(static_cast<char*>(slot.host));
+  hipError_t e = hipMemcpyAsync(dst, slot.host, bytes, hipMemcpyHostToDevice, strm);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string(what) + ": list copy: " + hipGetErrorString(e));
+  ring->calls = call + 1;
+  slot.call = call;
+  slot.stream = strm;
+  if (call % kFenceEvery == kFenceEvery - 1) {
+    e = record_fence(ring, strm, call);
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string(what) + ": fence: " + hipGetErrorString(e));
+  }
+  return PKV_OK;
+}
+
 // ---- diagnostics: event pairs around launches -------------------------------------------
 struct ProfRecord {
   int kind;
@@ -68,6 +167,7 @@ struct ProfRecord {
 };
 std::mutex g_prof_mu;
 bool g_prof_on = false;
+uint32_t g_prof_kinds = 0xFu;  // kernel kinds bracketed while profiling is on
 std::vector<ProfRecord> g_prof_pending;
 std::vector<hipEvent_t> g_prof_free;
 double g_prof_ms[4] = {0, 0, 0, 0};
@@ -86,7 +186,7 @@ hipEvent_t prof_event() {
 
 // Records the opening event of a launch of `kind`; returns the record index or -1.
 int prof_begin(int kind, hipStream_t s) {
-  if (!g_prof_on) return -1;
+  if (!g_prof_on || ((g_prof_kinds >> kind) & 1u) == 0) return -1;
   std::lock_guard<std::mutex> lk(g_prof_mu);
   ProfRecord r{kind, prof_event(), prof_event()};
   if (r.a == nullptr || r.b == nullptr) return -1;
@@ -117,8 +217,10 @@ bool on_tiles(const StepShape& s, int32_t ql) { return s.all_mfma || (ql > 1 && 
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Counts and layout only (no lists).
-pkv::WorkspaceLayout layout_for(const StepShape& s, int32_t hq, int32_t head_dim) {
+// Counts and layout only (no lists). n_write_rows > 0 reserves the slot array of a fused KV
+// append after the work lists (copied from the host with them).
+pkv::WorkspaceLayout layout_for(const StepShape& s, int32_t hq, int32_t head_dim,
+                                int32_t n_write_rows = 0) {
   pkv::WorkspaceLayout L;
   for (int32_t b = 0; b < s.B; ++b) {
     const int32_t ql = s.cu[b + 1] - s.cu[b];
@@ -144,6 +246,8 @@ pkv::WorkspaceLayout layout_for(const StepShape& s, int32_t hq, int32_t head_dim
   off = align_up(off + L.n_merge * sizeof(pkv::MergeItem));
   L.prefill_off = off;
   off = align_up(off + L.n_prefill * sizeof(pkv::PrefillItem));
+  L.slots_off = off;
+  off = align_up(off + static_cast<size_t>(n_write_rows) * sizeof(int32_t));
   L.list_bytes = off;
   L.part_m_off = off;
   off = align_up(off + L.n_part * hq * sizeof(float));
@@ -261,12 +365,10 @@ StepShape shape_for(const int32_t* ctx, const int32_t* cu, int32_t B, int32_t hq
   return s;
 }
 
-}  // namespace
-
-extern "C" int32_t pkv_write_kv(const void* k_new, const void* v_new, const int32_t* slots_dev,
-                                int32_t n_rows, void* k_cache, void* v_cache, int32_t num_blocks,
-                                int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
-                                int32_t dtype, void* stream) {
+// Validated arguments of a KV append (pkv_write_kv or the append of pkv_write_kv_attention).
+int32_t check_write(const void* k_new, const void* v_new, int32_t n_rows, const void* k_cache,
+                    const void* v_cache, int32_t num_blocks, int32_t block_size,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t dtype, pkv::WriteArgs* a) {
   if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID, "write_kv: bad dtype");
   if (n_rows < 0 || num_blocks < 0 || block_size <= 0 || num_kv_heads <= 0 || head_dim <= 0)
     return fail(PKV_ERR_INVALID, "write_kv: bad sizes");
@@ -274,66 +376,40 @@ extern "C" int32_t pkv_write_kv(const void* k_new, const void* v_new, const int3
   if (row_bytes % 16 != 0)
     return fail(PKV_ERR_UNSUPPORTED, "write_kv: num_kv_heads * head_dim * elem_bytes must be a "
                                      "multiple of 16");
-  if (n_rows == 0) return ok();
-  if (k_new == nullptr || v_new == nullptr || slots_dev == nullptr || k_cache == nullptr ||
-      v_cache == nullptr)
+  if (n_rows > 0 && (k_new == nullptr || v_new == nullptr || k_cache == nullptr ||
+                     v_cache == nullptr))
     return fail(PKV_ERR_INVALID, "write_kv: NULL pointer");
   if (static_cast<int64_t>(n_rows) * (row_bytes / 16) > 0xffffffffLL)
     return fail(PKV_ERR_UNSUPPORTED, "write_kv: too many rows in one call");
-  pkv::WriteArgs a;
-  a.k_new = k_new;
-  a.v_new = v_new;
-  a.slots = slots_dev;
-  a.n_rows = n_rows;
-  a.chunks_per_row = static_cast<int32_t>(row_bytes / 16);
-  a.n_slots = static_cast<int64_t>(num_blocks) * block_size;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  const int pr = prof_begin(0, static_cast<hipStream_t>(stream));
-  hipError_t e = pkv::launch_write_kv(a, static_cast<hipStream_t>(stream));
-  prof_end(pr, static_cast<hipStream_t>(stream));
+  a->k_new = k_new;
+  a->v_new = v_new;
+  a->slots = nullptr;
+  a->n_rows = n_rows;
+  a->chunks_per_row = static_cast<int32_t>(row_bytes / 16);
+  a->n_slots = static_cast<int64_t>(num_blocks) * block_size;
+  a->k_cache = const_cast<void*>(k_cache);
+  a->v_cache = const_cast<void*>(v_cache);
+  return PKV_OK;
+}
+
+int32_t launch_write(const pkv::WriteArgs& a, hipStream_t strm) {
+  const int pr = prof_begin(0, strm);
+  hipError_t e = pkv::launch_write_kv(a, strm);
+  prof_end(pr, strm);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("write_kv launch: ") + hipGetErrorString(e));
-  return ok();
+  return PKV_OK;
 }
 
-extern "C" int32_t pkv_attention_workspace_size_ex(const int32_t* ctx_lens_host,
-                                                   const int32_t* cu_seqlens_q_host, int32_t B,
-                                                   int32_t num_q_heads, int32_t num_kv_heads,
-                                                   int32_t head_dim, int32_t kv_split,
-                                                   int32_t dtype, uint32_t flags, size_t* bytes) {
-  if (bytes == nullptr) return fail(PKV_ERR_INVALID, "workspace_size: bytes is NULL");
-  *bytes = 0;
-  int32_t st = check_heads(num_q_heads, num_kv_heads, head_dim, kv_split, dtype);
-  if (st != PKV_OK) return st;
-  st = check_flags(flags, num_q_heads, num_kv_heads, head_dim, dtype);
-  if (st != PKV_OK) return st;
-  const int32_t T = (B > 0 && cu_seqlens_q_host != nullptr) ? cu_seqlens_q_host[B] : 0;
-  st = check_step(ctx_lens_host, cu_seqlens_q_host, B, T, -1);
-  if (st != PKV_OK) return st;
-  if (B == 0) return ok();
-  StepShape s = shape_for(ctx_lens_host, cu_seqlens_q_host, B, num_q_heads, num_kv_heads,
-                          head_dim, kv_split, dtype, flags);
-  *bytes = layout_for(s, num_q_heads, head_dim).total;
-  return ok();
-}
-
-extern "C" int32_t pkv_attention_workspace_size(const int32_t* ctx_lens_host,
-                                                const int32_t* cu_seqlens_q_host, int32_t B,
-                                                int32_t num_q_heads, int32_t num_kv_heads,
-                                                int32_t head_dim, int32_t kv_split, int32_t dtype,
-                                                size_t* bytes) {
-  return pkv_attention_workspace_size_ex(ctx_lens_host, cu_seqlens_q_host, B, num_q_heads,
-                                         num_kv_heads, head_dim, kv_split, dtype, 0u, bytes);
-}
-
-extern "C" int32_t pkv_attention_ex(const void* q, const void* k_cache, const void* v_cache,
-                                    const int32_t* block_tables_dev, int32_t max_blocks,
-                                    const int32_t* ctx_lens_host, const int32_t* cu_seqlens_q_host,
-                                    int32_t B, int32_t T, int32_t num_q_heads,
-                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                                    int32_t num_blocks, float scale, int32_t kv_split,
-                                    int32_t dtype, uint32_t flags, float* out, void* workspace,
-                                    size_t workspace_bytes, void* stream) {
+// One attention call, optionally preceded by a KV append whose slots come from host memory
+// (wr != nullptr): the slots travel in the same host-to-device copy as the work lists.
+int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables_dev, int32_t max_blocks,
+                       const int32_t* ctx_lens_host, const int32_t* cu_seqlens_q_host,
+                       int32_t B, int32_t T, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                       int32_t kv_split, int32_t dtype, uint32_t flags, float* out,
+                       void* workspace, size_t workspace_bytes, void* stream,
+                       pkv::WriteArgs* wr, const int32_t* slots_host) {
   int32_t st = check_heads(num_q_heads, num_kv_heads, head_dim, kv_split, dtype);
   if (st != PKV_OK) return st;
   st = check_flags(flags, num_q_heads, num_kv_heads, head_dim, dtype);
@@ -346,16 +422,24 @@ extern "C" int32_t pkv_attention_ex(const void* q, const void* k_cache, const vo
   st = check_step(ctx_lens_host, cu_seqlens_q_host, B, T,
                   static_cast<int64_t>(max_blocks) * block_size);
   if (st != PKV_OK) return st;
-  if (T == 0) return ok();
-  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_tables_dev == nullptr ||
-      out == nullptr)
+  const int32_t n_write = wr != nullptr ? wr->n_rows : 0;
+  if (n_write > 0) {
+    if (slots_host == nullptr) return fail(PKV_ERR_INVALID, "write_kv_attention: slots_host is NULL");
+    for (int32_t i = 0; i < n_write; ++i)
+      if (slots_host[i] >= wr->n_slots)
+        return fail(PKV_ERR_INVALID, "write_kv_attention: slot " + std::to_string(slots_host[i]) +
+                                         " outside the pool");
+  }
+  if (T == 0 && n_write == 0) return ok();
+  if (T > 0 && (q == nullptr || k_cache == nullptr || v_cache == nullptr ||
+                block_tables_dev == nullptr || out == nullptr))
     return fail(PKV_ERR_INVALID, "attention: NULL device pointer");
 
   const StepShape s = shape_for(ctx_lens_host, cu_seqlens_q_host, B, num_q_heads, num_kv_heads,
                                 head_dim, kv_split, dtype, flags);
-  const pkv::WorkspaceLayout L = layout_for(s, num_q_heads, head_dim);
+  const pkv::WorkspaceLayout L = layout_for(s, num_q_heads, head_dim, n_write);
   if (workspace_bytes < L.total || (L.total > 0 && workspace == nullptr))
-    return fail(PKV_ERR_INVALID, "attention: workspace smaller than pkv_attention_workspace_size (" +
+    return fail(PKV_ERR_INVALID, "attention: workspace smaller than the workspace-size query (" +
                                      std::to_string(L.total) + " bytes)");
   if (L.n_decode * num_q_heads > INT32_MAX || L.n_prefill * num_kv_heads > INT32_MAX)
     return fail(PKV_ERR_UNSUPPORTED, "attention: step too large for one launch");
@@ -363,39 +447,21 @@ extern "C" int32_t pkv_attention_ex(const void* q, const void* k_cache, const vo
   hipStream_t strm = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
 
-  // work lists -> pinned staging -> workspace (async, ordered before the kernels)
+  // work lists (and fused-append slots) -> pinned staging -> workspace, one async copy ordered
+  // before the kernels
   if (L.list_bytes > 0) {
-    int dev = 0;
-    DeviceRing* ring = ring_for_current_device(&dev);
-    if (ring == nullptr) return fail(PKV_ERR_HIP, "attention: hipGetDevice failed");
-    std::lock_guard<std::mutex> lk(ring->mu);
-    StagingSlot& slot = ring->slots[ring->next];
-    ring->next = (ring->next + 1) % 8;
-    if (slot.pending) {
-      hipError_t e = hipEventSynchronize(slot.done);
-      if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("attention: staging wait: ") + hipGetErrorString(e));
-      slot.pending = false;
-    }
-    if (slot.done == nullptr) {
-      hipError_t e = hipEventCreateWithFlags(&slot.done, hipEventDisableTiming);
-      if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("attention: event: ") + hipGetErrorString(e));
-    }
-    if (slot.cap < L.list_bytes) {
-      if (slot.host != nullptr) (void)hipHostFree(slot.host);
-      slot.host = nullptr;
-      slot.cap = 0;
-      size_t want = std::max<size_t>(L.list_bytes, 1 << 16);
-      hipError_t e = hipHostMalloc(&slot.host, want, hipHostMallocDefault);
-      if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("attention: pinned staging: ") + hipGetErrorString(e));
-      slot.cap = want;
-    }
-    build_lists(s, L, static_cast<char*>(slot.host));
-    hipError_t e = hipMemcpyAsync(ws, slot.host, L.list_bytes, hipMemcpyHostToDevice, strm);
-    if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("attention: list copy: ") + hipGetErrorString(e));
-    e = hipEventRecord(slot.done, strm);
-    if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("attention: event record: ") + hipGetErrorString(e));
-    slot.pending = true;
+    st = stage_and_copy(ws, L.list_bytes, strm, "attention", [&](char* host) {
+      build_lists(s, L, host);
+      if (n_write > 0) std::memcpy(host + L.slots_off, slots_host, sizeof(int32_t) * n_write);
+    });
+    if (st != PKV_OK) return st;
   }
+  if (n_write > 0) {
+    wr->slots = reinterpret_cast<const int32_t*>(ws + L.slots_off);
+    st = launch_write(*wr, strm);
+    if (st != PKV_OK) return st;
+  }
+  if (T == 0) return ok();
 
   const float scale_log2e = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   int32_t bs_log2 = -1;
@@ -470,6 +536,84 @@ extern "C" int32_t pkv_attention_ex(const void* q, const void* k_cache, const vo
   return ok();
 }
 
+int32_t workspace_size_impl(const int32_t* ctx_lens_host, const int32_t* cu_seqlens_q_host,
+                            int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t kv_split, int32_t dtype, uint32_t flags,
+                            int32_t n_write_rows, size_t* bytes) {
+  if (bytes == nullptr) return fail(PKV_ERR_INVALID, "workspace_size: bytes is NULL");
+  *bytes = 0;
+  if (n_write_rows < 0) return fail(PKV_ERR_INVALID, "workspace_size: n_rows must be >= 0");
+  int32_t st = check_heads(num_q_heads, num_kv_heads, head_dim, kv_split, dtype);
+  if (st != PKV_OK) return st;
+  st = check_flags(flags, num_q_heads, num_kv_heads, head_dim, dtype);
+  if (st != PKV_OK) return st;
+  const int32_t T = (B > 0 && cu_seqlens_q_host != nullptr) ? cu_seqlens_q_host[B] : 0;
+  st = check_step(ctx_lens_host, cu_seqlens_q_host, B, T, -1);
+  if (st != PKV_OK) return st;
+  StepShape s = shape_for(ctx_lens_host, cu_seqlens_q_host, B, num_q_heads, num_kv_heads,
+                          head_dim, kv_split, dtype, flags);
+  *bytes = layout_for(s, num_q_heads, head_dim, n_write_rows).total;
+  return ok();
+}
+
+}  // namespace
+
+extern "C" int32_t pkv_write_kv(const void* k_new, const void* v_new, const int32_t* slots_dev,
+                                int32_t n_rows, void* k_cache, void* v_cache, int32_t num_blocks,
+                                int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t dtype, void* stream) {
+  pkv::WriteArgs a;
+  int32_t st = check_write(k_new, v_new, n_rows, k_cache, v_cache, num_blocks, block_size,
+                           num_kv_heads, head_dim, dtype, &a);
+  if (st != PKV_OK) return st;
+  if (n_rows == 0) return ok();
+  if (slots_dev == nullptr) return fail(PKV_ERR_INVALID, "write_kv: NULL pointer");
+  a.slots = slots_dev;
+  st = launch_write(a, static_cast<hipStream_t>(stream));
+  if (st != PKV_OK) return st;
+  return ok();
+}
+
+extern "C" int32_t pkv_attention_workspace_size_ex(const int32_t* ctx_lens_host,
+                                                   const int32_t* cu_seqlens_q_host, int32_t B,
+                                                   int32_t num_q_heads, int32_t num_kv_heads,
+                                                   int32_t head_dim, int32_t kv_split,
+                                                   int32_t dtype, uint32_t flags, size_t* bytes) {
+  return workspace_size_impl(ctx_lens_host, cu_seqlens_q_host, B, num_q_heads, num_kv_heads,
+                             head_dim, kv_split, dtype, flags, 0, bytes);
+}
+
+extern "C" int32_t pkv_attention_workspace_size(const int32_t* ctx_lens_host,
+                                                const int32_t* cu_seqlens_q_host, int32_t B,
+                                                int32_t num_q_heads, int32_t num_kv_heads,
+                                                int32_t head_dim, int32_t kv_split, int32_t dtype,
+                                                size_t* bytes) {
+  return pkv_attention_workspace_size_ex(ctx_lens_host, cu_seqlens_q_host, B, num_q_heads,
+                                         num_kv_heads, head_dim, kv_split, dtype, 0u, bytes);
+}
+
+extern "C" int32_t pkv_write_kv_attention_workspace_size(
+    const int32_t* ctx_lens_host, const int32_t* cu_seqlens_q_host, int32_t B,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t kv_split,
+    int32_t dtype, uint32_t flags, int32_t n_rows, size_t* bytes) {
+  return workspace_size_impl(ctx_lens_host, cu_seqlens_q_host, B, num_q_heads, num_kv_heads,
+                             head_dim, kv_split, dtype, flags, n_rows, bytes);
+}
+
+extern "C" int32_t pkv_attention_ex(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_tables_dev, int32_t max_blocks,
+                                    const int32_t* ctx_lens_host, const int32_t* cu_seqlens_q_host,
+                                    int32_t B, int32_t T, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                    int32_t num_blocks, float scale, int32_t kv_split,
+                                    int32_t dtype, uint32_t flags, float* out, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  return attention_impl(q, k_cache, v_cache, block_tables_dev, max_blocks, ctx_lens_host,
+                        cu_seqlens_q_host, B, T, num_q_heads, num_kv_heads, head_dim, block_size,
+                        num_blocks, scale, kv_split, dtype, flags, out, workspace,
+                        workspace_bytes, stream, nullptr, nullptr);
+}
+
 extern "C" int32_t pkv_attention(const void* q, const void* k_cache, const void* v_cache,
                                  const int32_t* block_tables_dev, int32_t max_blocks,
                                  const int32_t* ctx_lens_host, const int32_t* cu_seqlens_q_host,
@@ -481,6 +625,30 @@ extern "C" int32_t pkv_attention(const void* q, const void* k_cache, const void*
                           cu_seqlens_q_host, B, T, num_q_heads, num_kv_heads, head_dim,
                           block_size, num_blocks, scale, kv_split, dtype, 0u, out, workspace,
                           workspace_bytes, stream);
+}
+
+extern "C" int32_t pkv_write_kv_attention(
+    const void* q, const void* k_new, const void* v_new, const int32_t* slots_host,
+    int32_t n_rows, void* k_cache, void* v_cache, const int32_t* block_tables_dev,
+    int32_t max_blocks, const int32_t* ctx_lens_host, const int32_t* cu_seqlens_q_host,
+    int32_t B, int32_t T, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t num_blocks, float scale, int32_t kv_split, int32_t dtype,
+    uint32_t flags, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  pkv::WriteArgs a;
+  int32_t st = check_write(k_new, v_new, n_rows, k_cache, v_cache, num_blocks, block_size,
+                           num_kv_heads, head_dim, dtype, &a);
+  if (st != PKV_OK) return st;
+  return attention_impl(q, k_cache, v_cache, block_tables_dev, max_blocks, ctx_lens_host,
+                        cu_seqlens_q_host, B, T, num_q_heads, num_kv_heads, head_dim, block_size,
+                        num_blocks, scale, kv_split, dtype, flags, out, workspace,
+                        workspace_bytes, stream, &a, slots_host);
+}
+
+extern "C" int32_t pkv_profile_set_kinds(uint32_t kinds) {
+  if ((kinds & ~0xFu) != 0) return fail(PKV_ERR_INVALID, "profile_set_kinds: unknown kind bits");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_kinds = kinds;
+  return ok();
 }
 
 extern "C" int32_t pkv_profile_enable(int32_t enable) {

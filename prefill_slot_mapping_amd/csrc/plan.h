@@ -52,10 +52,10 @@ struct PrefillItem {
 
 // Byte offsets of each region inside the caller's workspace (all 256-byte aligned).
 struct WorkspaceLayout {
-  size_t decode_off = 0, merge_off = 0, prefill_off = 0, part_m_off = 0, part_l_off = 0,
-         part_acc_off = 0, total = 0;
+  size_t decode_off = 0, merge_off = 0, prefill_off = 0, slots_off = 0, part_m_off = 0,
+         part_l_off = 0, part_acc_off = 0, total = 0;
   int64_t n_decode = 0, n_merge = 0, n_prefill = 0, n_part = 0;
-  size_t list_bytes = 0;  // decode + merge + prefill lists (the part copied from the host)
+  size_t list_bytes = 0;  // lists (+ fused-append slots): the part copied from the host
 };
 
 }  // namespace pkv

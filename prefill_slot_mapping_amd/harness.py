@@ -75,6 +75,27 @@ class GpuStep:
                            phase_consistent=phase_consistent)
 
 
+    def fused_step(self, kv_split: Optional[int] = None, stream=None,
+                   phase_consistent: bool = False):
+        """The step's KV append and attention in one pkv_write_kv_attention call."""
+        import torch
+        w = self.workload
+        split = w.spec.kv_split if kv_split is None else kv_split
+        if self.out is None:
+            self.out = torch.empty((w.T, w.spec.Hq, w.spec.D), dtype=torch.float32,
+                                   device=self.q.device)
+        need = L.write_kv_attention_workspace_size(
+            w.ctx_lens, w.cu_seqlens_q, w.spec.Hq, w.spec.Hkv, w.spec.D, w.T, split,
+            L.PKV_BF16 if w.spec.dtype == "bf16" else L.PKV_F32, phase_consistent)
+        if self.workspace is None or self.workspace.numel() < need:
+            self.workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=self.q.device)
+        return L.write_kv_attention(self.q, self.k_new, self.v_new, self.new_slots, self.k_cache,
+                                    self.v_cache, self.block_tables_dev, w.ctx_lens,
+                                    w.cu_seqlens_q, w.scale, out=self.out,
+                                    workspace=self.workspace, kv_split=split, stream=stream,
+                                    phase_consistent=phase_consistent)
+
+
 def build_gpu_step(w, device="cuda", write_new: bool = True, workers: int = 8) -> GpuStep:
     import torch
     s = w.spec

@@ -246,3 +246,55 @@ def test_phase_consistent_workspace_has_no_split_partials():
     cons = pkv.attention_workspace_size([4096], [0, 1], 8, 2, 128, 512, phase_consistent=True)
     assert normal >= 8 * 8 * 130 * 4
     assert 0 < cons < 1024
+
+
+def _fused(**kw):
+    """Raw pkv_write_kv_attention call with fake device pointers: only validation may run."""
+    lib = pkv.lib()
+    a = dict(q=1, kn=1, vn=1, slots=[3, -1, 60], n=3, k=1, v=1, bt=1, mb=8, ctx=[5, 9],
+             cu=[0, 1, 3], T=3, hq=8, hkv=2, d=128, bs=16, nb=4, scale=0.1, split=512,
+             dt=L.PKV_BF16, flags=0, out=1, ws=1, wsb=1 << 30)
+    a.update(kw)
+    ctx = np.asarray(a["ctx"], np.int32)
+    cu = np.asarray(a["cu"], np.int32)
+    sl = np.asarray(a["slots"] if a["slots"] is not None else [0], np.int32)
+    sp = L._ptr(sl) if a["slots"] is not None else None
+    return lib.pkv_write_kv_attention(a["q"], a["kn"], a["vn"], sp, a["n"], a["k"], a["v"],
+                                      a["bt"], a["mb"], L._ptr(ctx), L._ptr(cu), ctx.size,
+                                      a["T"], a["hq"], a["hkv"], a["d"], a["bs"], a["nb"],
+                                      a["scale"], a["split"], a["dt"], a["flags"], a["out"],
+                                      a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(slots=[3, -1, 64]), L.PKV_ERR_INVALID),           # slot == num_blocks * block_size
+    (dict(n=-1), L.PKV_ERR_INVALID),                        # negative row count
+    (dict(slots=None), L.PKV_ERR_INVALID),                  # NULL host slots
+    (dict(kn=0), L.PKV_ERR_INVALID),                        # NULL k_new
+    (dict(dt=5), L.PKV_ERR_INVALID),                        # dtype
+    (dict(hkv=1, hq=4, d=4, dt=L.PKV_BF16), L.PKV_ERR_UNSUPPORTED),  # 8-byte rows
+    (dict(hq=6, hkv=4), L.PKV_ERR_INVALID),                 # attention part still validated
+    (dict(T=4), L.PKV_ERR_INVALID),
+    (dict(wsb=16), L.PKV_ERR_INVALID),                      # workspace too small
+    (dict(flags=2), L.PKV_ERR_INVALID),
+])
+def test_fused_step_validation_refuses_before_any_copy(kw, status):
+    assert _fused(**kw) == status
+    assert pkv.lib().pkv_last_error() != b""
+
+
+def test_fused_step_workspace_holds_the_slots():
+    a = pkv.attention_workspace_size([513, 40], [0, 1, 2], 8, 2, 128, 512)
+    b = pkv.write_kv_attention_workspace_size([513, 40], [0, 1, 2], 8, 2, 128, 1000, 512)
+    assert b >= a + 4 * 1000
+    assert pkv.write_kv_attention_workspace_size([513, 40], [0, 1, 2], 8, 2, 128, 0, 512) == a
+    # a pure append (no sequences) still needs room for its slots
+    assert pkv.write_kv_attention_workspace_size([], [0], 8, 2, 128, 10, 512) >= 40
+    with pytest.raises(pkv.InvalidArgument):
+        pkv.write_kv_attention_workspace_size([5], [0, 1], 8, 2, 128, -1, 512)
+
+
+def test_profile_kind_mask_validation():
+    assert pkv.lib().pkv_profile_set_kinds(0x10) == L.PKV_ERR_INVALID
+    pkv.profile_set_kinds(["decode"])
+    pkv.profile_set_kinds(["write_kv", "prefill", "decode", "merge"])
