@@ -10,8 +10,9 @@
 // the keys of a row are cut into splits of kv_split tokens aligned at position 0; inside a
 // split, tiles of HT keys (16 or 32, per instance) aligned at the split start go to wave
 // (tile % 4); each wave runs an online softmax over its tiles in ascending order in the base-2
-// domain (scores scaled by scale * log2 e, hardware exp2); the four wave partials are merged
-// in wave order and the split partials in ascending split order (merge kernel). Accumulation
+// domain (scores scaled by scale * log2 e, hardware exp2) whose per-head reference moves to
+// the tile maximum only when a score exceeds it by more than 8; the four wave partials are
+// merged in wave order and the split partials in ascending split order (merge kernel). Accumulation
 // is float32 throughout; bfloat16 products are formed exactly by v_dot2_f32_bf16 and summed
 // over the head dimension in ascending 16-byte chunks, one part of the dimension per lane of a
 // key's lane group, the parts then added in a fixed butterfly; probabilities stay float32 for
@@ -60,6 +61,14 @@ template <typename Op>
 __device__ __forceinline__ float across16(float x, Op op) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// x through an empty register-to-register asm: a select between such values stays a select
+// of registers (the optimizer would otherwise turn a select between array elements into a
+// select between their addresses, which keeps the array in memory)
+__device__ __forceinline__ float opaque(float x) {
+  asm("" : "+v"(x));
+  return x;
 }
 
 struct MaxOp {
@@ -133,6 +142,10 @@ decode_split_kernel(DecodeArgs a) {
   constexpr int SPL = 64 / HT;              // score stage: lanes per key (2 or 4)
   constexpr int CPH = LPT / SPL;            // score stage: chunks per lane
   constexpr int GO = G >= SPL ? G / SPL : 1;  // heads whose p a lane forms
+  constexpr float kRescaleLog2 = 8.f;       // lazy rescale threshold (log2 units)
+  // groups of 8 keep the running maximum (the lazy reference's extra live registers would
+  // spill at two waves per SIMD)
+  constexpr bool kLazy = G < 8;
   static_assert(LPT >= 8 && LPT <= 32 && (LPT & (LPT - 1)) == 0 && HT % TPI == 0, "shape");
   static_assert(HT == 16 || HT == 32, "tile");
   static_assert(NI % 2 == 0, "slot reads are 8- or 16-byte vectors");
@@ -188,7 +201,7 @@ decode_split_kernel(DecodeArgs a) {
   const int cl = lane & (LPT - 1);          // P.V stage / loads: chunk of this lane
   const int kk = lane / SPL;                // score stage: key of this lane
   const int hf = lane % SPL;                // score stage: part of D of this lane
-  const uint64_t slot_bytes = static_cast<uint64_t>(a.hkv) * ROWB;
+  const uint32_t slot_bytes = static_cast<uint32_t>(a.hkv) * ROWB;  // < 2^32 for any head count
   const char* kbase = static_cast<const char*>(a.k_cache) + g * ROWB + cl * 16;
   const char* vbase = static_cast<const char*>(a.v_cache) + g * ROWB + cl * 16;
   uint4* sk = s_k + wave * HT * LPT;
@@ -261,50 +274,72 @@ decode_split_kernel(DecodeArgs a) {
       }
     }
     const bool valid = kk < n;
-    bool moved = false;
-    float alpha[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       s[h] += dpp_xor1(s[h]);
       if constexpr (SPL == 4) s[h] += dpp_xor2(s[h]);
       s[h] = valid ? s[h] * a.scale_log2e : -INFINITY;
-      const float mn = fmaxf(m[h], max_over_groups<SPL>(s[h]));
-      alpha[h] = fast_exp2(m[h] - mn);
-      moved |= alpha[h] != 1.f;
-      m[h] = mn;
+    }
+    if constexpr (kLazy) {
+      // A head's reference m moves only when one of its scores rises more than kRescaleLog2
+      // above it (then to the tile maximum): p = exp2(s - m) stays below 2^kRescaleLog2, and
+      // tiles that do not move it skip the wave maxima and the accumulator rescale.
+      bool over = false;
+#pragma unroll
+      for (int h = 0; h < G; ++h) over |= s[h] > m[h] + kRescaleLog2;
+      if (__any(over)) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float mt = max_over_groups<SPL>(s[h]);
+          const float mn = mt > m[h] + kRescaleLog2 ? mt : m[h];
+          const float al = fast_exp2(m[h] - mn);  // exactly 1 for a head that keeps m
+          m[h] = mn;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] *= al;
+          const int j = G >= SPL ? h / SPL : 0;
+          lo[j] = hf == (G >= SPL ? h % SPL : h) ? lo[j] * al : lo[j];
+        }
+      }
+    } else {
+      // m is the running maximum; the accumulators are rescaled when some head's maximum
+      // moved (multiplying by exactly 1 changes nothing)
+      bool moved = false;
+      float alpha[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float mn = fmaxf(m[h], max_over_groups<SPL>(s[h]));
+        alpha[h] = fast_exp2(m[h] - mn);
+        moved |= alpha[h] != 1.f;
+        m[h] = mn;
+      }
+#pragma unroll
+      for (int j = 0; j < GO; ++j) {
+        float av = alpha[G >= SPL ? j * SPL : 0];
+#pragma unroll
+        for (int r = 1; r < (G >= SPL ? SPL : G); ++r)
+          av = hf == r ? opaque(alpha[j * SPL + r]) : av;
+        lo[j] *= av;
+      }
+      if (__any(moved)) {
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha[h];
+      }
     }
     // p of (key kk, head h) is formed by the lane of that key with hf == h % SPL (heads
     // below SPL: by the lanes hf < G, the others idle)
 #pragma unroll
     for (int j = 0; j < GO; ++j) {
-      float sv, mv, av;
-      if constexpr (G >= SPL) {
-        sv = s[j * SPL]; mv = m[j * SPL]; av = alpha[j * SPL];
+      float sv = s[G >= SPL ? j * SPL : 0], mv = m[G >= SPL ? j * SPL : 0];
 #pragma unroll
-        for (int r = 1; r < SPL; ++r) {
-          sv = hf == r ? s[j * SPL + r] : sv;
-          mv = hf == r ? m[j * SPL + r] : mv;
-          av = hf == r ? alpha[j * SPL + r] : av;
-        }
-      } else {
-        sv = s[0]; mv = m[0]; av = alpha[0];
-#pragma unroll
-        for (int r = 1; r < G; ++r) {
-          sv = hf == r ? s[r] : sv;
-          mv = hf == r ? m[r] : mv;
-          av = hf == r ? alpha[r] : av;
-        }
+      for (int r = 1; r < (G >= SPL ? SPL : G); ++r) {
+        sv = hf == r ? opaque(s[j * SPL + r]) : sv;
+        mv = hf == r ? opaque(m[j * SPL + r]) : mv;
       }
       const float p = fast_exp2(sv - mv);
-      lo[j] = lo[j] * av + p;
+      lo[j] += p;
       if (G >= SPL || hf < G) sp[kk * G + j * SPL + hf] = p;
-    }
-    // rescale only when some head's max moved (multiplying by exactly 1 changes nothing)
-    if (__any(moved)) {
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha[h];
     }
     // P.V, split-D layout: this lane owns columns cl*EPL .. +EPL of keys i*TPI + grp
 #pragma unroll
