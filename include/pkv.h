@@ -112,6 +112,79 @@ int32_t pkv_slot_mapping_step(const pkv_alloc* a, const int32_t* block_tables_ho
  * or in [0, num_slots), and no non-negative slot appears twice. PKV_OK or PKV_ERR_INVALID. */
 int32_t pkv_validate_slots(const int32_t* slots_host, int32_t n, int64_t num_slots);
 
+/* ---- host step builder [P3 "Design > engine.py": Scheduler, Prefix sharing; "Optional
+ *      paged KV cache (vLLM-style) — v1 design", sections "Design" (trim) and "Follow-ups"
+ *      (block-level copy-on-write)] ------------------------------------------------------
+ * Turns requests into the flat ragged steps the device path consumes (cu_seqlens_q, ctx_lens,
+ * block tables, slots). A sequence is a token count plus num_computed; a step gives each
+ * scheduled sequence n_new = min(remaining, chunk_size, budget) new rows: decodes (remaining
+ * == 1) first, oldest first, then the others, oldest first, while the token budget lasts.
+ * Admission is FIFO and takes the first waiting sequence only if its whole token list fits in
+ * the free blocks not promised to sequences admitted earlier in the same step (at most
+ * max_num_seqs running). When a scheduled sequence cannot get its blocks, the youngest running
+ * sequence that holds blocks and is not yet scheduled in this step is preempted by recompute
+ * (its blocks are freed, num_computed drops to 0, its tokens are kept); it may be the asking
+ * sequence, which then waits for a later step. With prefix sharing, a waiting sequence adopts
+ * the first (prompt_len - 1) / block_size blocks of the oldest running sequence of its group
+ * and prompt length once that one has computed them (it waits until then), and recomputes its
+ * last prompt token. A chunk that writes into a block with refcount > 1 first gets a fresh copy
+ * of it (copy-on-write): the step lists (src, dst) block pairs the caller copies before the
+ * append. After the forward pass, pkv_sched_complete advances num_computed; a sequence whose
+ * tokens are all computed samples: it finishes (blocks freed) if listed in `finished` or at
+ * max_blocks_per_seq * block_size tokens, else it grows by one token.
+ * The handle owns its block allocator (pkv_sched_allocator returns it for queries and slot
+ * mapping; do not destroy it separately). Not thread-safe. Errors: PKV_ERR_INVALID. */
+typedef struct pkv_sched pkv_sched;
+
+/* New scheduler over a fresh pool of num_blocks blocks; every size >= 1 (num_blocks >= 0);
+ * prefix_sharing != 0 enables adoption. *out receives the handle (caller destroys). */
+int32_t pkv_sched_create(int32_t num_blocks, int32_t block_size, int32_t chunk_size,
+                         int32_t token_budget, int32_t max_num_seqs, int32_t max_blocks_per_seq,
+                         int32_t prefix_sharing, pkv_sched** out);
+void pkv_sched_destroy(pkv_sched* s);
+/* The scheduler's allocator (owned by the handle). */
+pkv_alloc* pkv_sched_allocator(pkv_sched* s);
+/* Queue a request: a new id, prompt_len in [1, max_blocks_per_seq * block_size], group >= 0
+ * to take part in prefix sharing (-1: none). */
+int32_t pkv_sched_add(pkv_sched* s, int32_t seq_id, int32_t prompt_len, int32_t group);
+/* Build the next step (refused while the previous one awaits pkv_sched_complete). Writes the
+ * number of scheduled sequences B, rows T, copy-on-write pairs and preempted sequences; the
+ * plan itself is read with pkv_sched_plan. */
+int32_t pkv_sched_step(pkv_sched* s, int32_t* B, int32_t* T, int32_t* n_copies,
+                       int32_t* n_preempted);
+/* Copy the pending plan into caller buffers (any may be NULL): seq_ids, n_new, ctx_lens [B];
+ * cu_seqlens_q [B + 1]; block_tables [B, max_blocks_per_seq] (whole tables after the step,
+ * -1 past each sequence's blocks); slots [T] in step order; copies [2 * n_copies] as (src, dst)
+ * pairs; preempted [n_preempted]. */
+int32_t pkv_sched_plan(const pkv_sched* s, int32_t* seq_ids, int32_t* n_new, int32_t* ctx_lens,
+                       int32_t* cu_seqlens_q, int32_t* block_tables, int32_t* slots,
+                       int32_t* copies, int32_t* preempted);
+/* Apply the pending plan after its forward pass; `finished` lists sequences whose sampled token
+ * ends them. Writes the sequences that sampled, in plan order, to sampled [<= B] (may be NULL)
+ * and their count to *n_sampled. */
+int32_t pkv_sched_complete(pkv_sched* s, const int32_t* finished, int32_t n_finished,
+                           int32_t* sampled, int32_t* n_sampled);
+/* Rewind a running sequence to n_tokens in [1, its token count]: num_computed becomes
+ * min(num_computed, n_tokens - 1) (the last kept token is fed again) and the blocks past
+ * ceil(num_computed / block_size) are freed. Refused while a step is pending. */
+int32_t pkv_sched_trim(pkv_sched* s, int32_t seq_id, int32_t n_tokens);
+/* Fork a running sequence into new_id: the fork shares every block (refcount + 1) and is
+ * admitted now; the first write into a shared block copies it. Refused while a step is pending
+ * or at max_num_seqs. */
+int32_t pkv_sched_fork(pkv_sched* s, int32_t src_id, int32_t new_id);
+/* Per-sequence state (0 waiting, 1 running, 2 finished), token count, num_computed, blocks held;
+ * any pointer may be NULL. pkv_sched_seq_blocks copies the held block ids (n_blocks entries). */
+int32_t pkv_sched_seq_info(const pkv_sched* s, int32_t seq_id, int32_t* state,
+                           int32_t* n_tokens, int32_t* num_computed, int32_t* n_blocks);
+int32_t pkv_sched_seq_blocks(const pkv_sched* s, int32_t seq_id, int32_t* blocks);
+/* Counters: preemptions so far, tokens adopted through prefix sharing, running and waiting
+ * sequences. */
+int32_t pkv_sched_stats(const pkv_sched* s, int64_t* preemptions, int64_t* shared_tokens,
+                        int32_t* n_running, int32_t* n_waiting);
+/* PKV_OK iff the allocator is consistent, refcounts equal the references held by the live
+ * tables and no running sequence has computed past its blocks; else PKV_ERR_INCONSISTENT. */
+int32_t pkv_sched_check(const pkv_sched* s);
+
 /* ---- KV append [P3 "Design > paged.py": copy-free append, write scatters into
  *      (block, offset) in place] -----------------------------------------------------------
  * k_new, v_new: device [n_rows, num_kv_heads, head_dim] contiguous, element type dtype.

@@ -98,6 +98,19 @@ _SIGS = {
     "pkv_slot_mapping": ([_vp, _pi32, _i32, _i32, _i32, _i32, _pi32], _i32),
     "pkv_slot_mapping_step": ([_vp, _pi32, _i32, _i32, _i32, _pi32, _pi32, _pi32], _i32),
     "pkv_validate_slots": ([_pi32, _i32, _i64], _i32),
+    "pkv_sched_create": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_vp)], _i32),
+    "pkv_sched_destroy": ([_vp], None),
+    "pkv_sched_allocator": ([_vp], _vp),
+    "pkv_sched_add": ([_vp, _i32, _i32, _i32], _i32),
+    "pkv_sched_step": ([_vp, _pi32, _pi32, _pi32, _pi32], _i32),
+    "pkv_sched_plan": ([_vp, _pi32, _pi32, _pi32, _pi32, _pi32, _pi32, _pi32, _pi32], _i32),
+    "pkv_sched_complete": ([_vp, _pi32, _i32, _pi32, _pi32], _i32),
+    "pkv_sched_trim": ([_vp, _i32, _i32], _i32),
+    "pkv_sched_fork": ([_vp, _i32, _i32], _i32),
+    "pkv_sched_seq_info": ([_vp, _i32, _pi32, _pi32, _pi32, _pi32], _i32),
+    "pkv_sched_seq_blocks": ([_vp, _i32, _pi32], _i32),
+    "pkv_sched_stats": ([_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i64), _pi32, _pi32], _i32),
+    "pkv_sched_check": ([_vp], _i32),
     "pkv_write_kv": ([_vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp], _i32),
     "pkv_attention_workspace_size": ([_pi32, _pi32, _i32, _i32, _i32, _i32, _i32, _i32,
                                       ctypes.POINTER(ctypes.c_size_t)], _i32),
@@ -180,10 +193,18 @@ class BlockAllocator:
         _check(lib().pkv_alloc_create(int(num_blocks), ctypes.byref(h)))
         self._h = h
 
+    @classmethod
+    def _view(cls, handle, owner):
+        """A non-owning view of an allocator that another handle owns (kept alive by it)."""
+        a = cls.__new__(cls)
+        a._h = handle
+        a._owner = owner
+        return a
+
     def close(self):
-        if getattr(self, "_h", None):
+        if getattr(self, "_h", None) and getattr(self, "_owner", None) is None:
             lib().pkv_alloc_destroy(self._h)
-            self._h = None
+        self._h = None
 
     def __del__(self):
         try:
@@ -234,6 +255,109 @@ class BlockAllocator:
         _check(lib().pkv_slot_mapping(self._h, _ptr(row), row.size, int(block_size),
                                       int(start_pos), int(n_new), _ptr(out)))
         return out[:int(n_new)]
+
+
+# ---- host step builder ------------------------------------------------------------------
+
+class SchedPlan:
+    """One step built by the scheduler (fields as pkv_sched_plan, as Python lists)."""
+    __slots__ = ("seq_ids", "n_new", "ctx_lens", "cu_seqlens", "block_tables", "slots",
+                 "copies", "preempted")
+
+    def __init__(self, **kw):
+        for k in self.__slots__:
+            setattr(self, k, kw[k])
+
+
+class Scheduler:
+    """Handle on the library's host step builder (pkv_sched_* in include/pkv.h)."""
+
+    def __init__(self, num_blocks: int, block_size: int, chunk_size: int, token_budget: int,
+                 max_num_seqs: int, max_blocks_per_seq: int, prefix_sharing: bool = False):
+        h = _vp()
+        _check(lib().pkv_sched_create(int(num_blocks), int(block_size), int(chunk_size),
+                                      int(token_budget), int(max_num_seqs),
+                                      int(max_blocks_per_seq), 1 if prefix_sharing else 0,
+                                      ctypes.byref(h)))
+        self._h = h
+        self.max_blocks_per_seq = int(max_blocks_per_seq)
+        self.allocator = BlockAllocator._view(_vp(lib().pkv_sched_allocator(h)), self)
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().pkv_sched_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add(self, seq_id: int, prompt_len: int, group: int = -1) -> None:
+        _check(lib().pkv_sched_add(self._h, int(seq_id), int(prompt_len), int(group)))
+
+    def step(self) -> SchedPlan:
+        B, T, nc, npre = (ctypes.c_int32(0) for _ in range(4))
+        _check(lib().pkv_sched_step(self._h, ctypes.byref(B), ctypes.byref(T), ctypes.byref(nc),
+                                    ctypes.byref(npre)))
+        b, t, c, pr = B.value, T.value, nc.value, npre.value
+        mb = self.max_blocks_per_seq
+        ids, nn, ctx = (np.zeros(max(b, 1), np.int32) for _ in range(3))
+        cu = np.zeros(b + 1, np.int32)
+        bt = np.zeros(max(b, 1) * mb, np.int32)
+        sl = np.zeros(max(t, 1), np.int32)
+        cp = np.zeros(max(2 * c, 1), np.int32)
+        pp = np.zeros(max(pr, 1), np.int32)
+        _check(lib().pkv_sched_plan(self._h, _ptr(ids), _ptr(nn), _ptr(ctx), _ptr(cu), _ptr(bt),
+                                    _ptr(sl), _ptr(cp), _ptr(pp)))
+        bt = bt[:b * mb].reshape(b, mb)
+        tables = [[int(x) for x in row if x >= 0] for row in bt]
+        return SchedPlan(seq_ids=ids[:b].tolist(), n_new=nn[:b].tolist(),
+                         ctx_lens=ctx[:b].tolist(), cu_seqlens=cu.tolist(), block_tables=tables,
+                         slots=sl[:t].tolist(),
+                         copies=[(int(cp[2 * i]), int(cp[2 * i + 1])) for i in range(c)],
+                         preempted=pp[:pr].tolist())
+
+    def complete(self, finished: Sequence[int] = ()) -> List[int]:
+        fin = _host_i32(list(finished) or [0])
+        n = len(list(finished))
+        _, _, _, running = self.stats_tuple()
+        out = np.zeros(max(running, 1), np.int32)
+        ns = ctypes.c_int32(0)
+        _check(lib().pkv_sched_complete(self._h, _ptr(fin), n, _ptr(out), ctypes.byref(ns)))
+        return out[:ns.value].tolist()
+
+    def trim(self, seq_id: int, n_tokens: int) -> None:
+        _check(lib().pkv_sched_trim(self._h, int(seq_id), int(n_tokens)))
+
+    def fork(self, src_id: int, new_id: int) -> None:
+        _check(lib().pkv_sched_fork(self._h, int(src_id), int(new_id)))
+
+    def seq_info(self, seq_id: int) -> Tuple[int, int, int, int]:
+        v = [ctypes.c_int32(0) for _ in range(4)]
+        _check(lib().pkv_sched_seq_info(self._h, int(seq_id), *[ctypes.byref(x) for x in v]))
+        return tuple(x.value for x in v)
+
+    def seq_blocks(self, seq_id: int) -> List[int]:
+        n = self.seq_info(seq_id)[3]
+        out = np.zeros(max(n, 1), np.int32)
+        _check(lib().pkv_sched_seq_blocks(self._h, int(seq_id), _ptr(out)))
+        return out[:n].tolist()
+
+    def stats_tuple(self) -> Tuple[int, int, int, int]:
+        pre, sh = _i64(0), _i64(0)
+        run, wait = ctypes.c_int32(0), ctypes.c_int32(0)
+        _check(lib().pkv_sched_stats(self._h, ctypes.byref(pre), ctypes.byref(sh),
+                                     ctypes.byref(run), ctypes.byref(wait)))
+        return pre.value, sh.value, wait.value, run.value
+
+    def check(self) -> bool:
+        st = lib().pkv_sched_check(self._h)
+        if st == PKV_ERR_INCONSISTENT:
+            return False
+        _check(st)
+        return True
 
 
 def slot_mapping_step(allocator: "BlockAllocator", block_tables, block_size: int, start_pos,

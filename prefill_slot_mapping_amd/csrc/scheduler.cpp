@@ -222,7 +222,6 @@ extern "C" int32_t pkv_sched_step(pkv_sched* s, int32_t* B, int32_t* T, int32_t*
   admission(s);
   int32_t budget = s->budget;
   std::unordered_set<int32_t> scheduled;
-  std::unordered_set<int32_t> preempted_now;
   std::vector<std::pair<int32_t, int32_t>> order;
   for (int pass = 0; pass < 2; ++pass) {
     const bool decode_pass = pass == 0;
