@@ -200,6 +200,21 @@ int32_t pkv_write_kv(const void* k_new, const void* v_new, const int32_t* slots_
                      int32_t block_size, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
                      void* stream);
 
+/* ---- block copy for copy-on-write ["Optional paged KV cache (vLLM-style) — v1 design",
+ *      section "Follow-ups": block-level copy-on-write, a fork copies a shared block on its
+ *      first divergent write] ------------------------------------------------------------
+ * For each pair i, block pairs_host[2i + 1] of both pools becomes a byte copy of block
+ * pairs_host[2i] (all block_size slots, all heads): the (src, dst) pairs pkv_sched_step lists,
+ * applied before the step's append. Validated on the host before anything is enqueued: ids in
+ * [0, num_blocks), no destination twice, no destination that is also a source
+ * (PKV_ERR_INVALID). The pairs go to the device through the library's pinned staging into
+ * workspace (device, >= 8 * n_pairs bytes rounded up to 256, caller-owned; untouched until the
+ * copy has run). Pools as in pkv_write_kv. Enqueued on stream; n_pairs == 0 is a no-op. */
+int32_t pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs_host,
+                        int32_t n_pairs, int32_t num_blocks, int32_t block_size,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t dtype, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
 /* ---- ragged paged attention [P3 "Design > paged.py": TritonPagedAttention contract —
  *      q, k/v cache blocks, block tables, cu_seqlens_q, ctx_lens, slot mapping; fixed KV
  *      split per context length, no atomics] ---------------------------------------------

@@ -111,6 +111,8 @@ _SIGS = {
     "pkv_sched_seq_blocks": ([_vp, _i32, _pi32], _i32),
     "pkv_sched_stats": ([_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i64), _pi32, _pi32], _i32),
     "pkv_sched_check": ([_vp], _i32),
+    "pkv_copy_blocks": ([_vp, _vp, _pi32, _i32, _i32, _i32, _i32, _i32, _i32, _vp,
+                         ctypes.c_size_t, _vp], _i32),
     "pkv_write_kv": ([_vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp], _i32),
     "pkv_attention_workspace_size": ([_pi32, _pi32, _i32, _i32, _i32, _i32, _i32, _i32,
                                       ctypes.POINTER(ctypes.c_size_t)], _i32),
@@ -424,6 +426,24 @@ def write_kv(k_new, v_new, slots, k_cache, v_cache, stream=None) -> None:
     _check(lib().pkv_write_kv(k_new.data_ptr(), v_new.data_ptr(), sl.data_ptr(),
                               int(k_new.shape[0]), k_cache.data_ptr(), v_cache.data_ptr(), nb, bs,
                               hkv, d, _dtype_code(k_cache), _stream_ptr(k_cache, stream)))
+
+
+def copy_blocks(pairs, k_cache, v_cache, workspace=None, stream=None) -> None:
+    """pkv_copy_blocks: for each (src, dst) pair, dst block of both pools := src block."""
+    import torch
+    _need_cuda(k_cache, v_cache)
+    pr = _host_i32(np.asarray(list(pairs), dtype=np.int32).reshape(-1))
+    n = pr.size // 2
+    if n == 0:
+        return
+    nb, bs, hkv, d = k_cache.shape
+    need = (8 * n + 255) // 256 * 256
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=k_cache.device)
+    _check(lib().pkv_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), _ptr(pr), n, nb, bs, hkv,
+                                 d, _dtype_code(k_cache), workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(),
+                                 _stream_ptr(k_cache, stream)))
 
 
 def attention_workspace_size(ctx_lens, cu_seqlens_q, num_q_heads: int, num_kv_heads: int,

@@ -574,6 +574,56 @@ extern "C" int32_t pkv_write_kv(const void* k_new, const void* v_new, const int3
   return ok();
 }
 
+extern "C" int32_t pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs_host,
+                                   int32_t n_pairs, int32_t num_blocks, int32_t block_size,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID, "copy_blocks: bad dtype");
+  if (n_pairs < 0 || num_blocks < 0 || block_size <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+    return fail(PKV_ERR_INVALID, "copy_blocks: bad sizes");
+  const int64_t block_bytes =
+      static_cast<int64_t>(block_size) * num_kv_heads * head_dim * elem_bytes(dtype);
+  if (block_bytes % 16 != 0)
+    return fail(PKV_ERR_UNSUPPORTED, "copy_blocks: block bytes must be a multiple of 16");
+  if (n_pairs == 0) return ok();
+  if (pairs_host == nullptr || k_cache == nullptr || v_cache == nullptr)
+    return fail(PKV_ERR_INVALID, "copy_blocks: NULL pointer");
+  if (static_cast<int64_t>(n_pairs) * (block_bytes / 16) > 0xffffffffLL)
+    return fail(PKV_ERR_UNSUPPORTED, "copy_blocks: too many chunks in one call");
+  const size_t need = align_up(sizeof(int32_t) * 2 * static_cast<size_t>(n_pairs));
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(PKV_ERR_INVALID, "copy_blocks: workspace smaller than 8 bytes per pair");
+  std::vector<int32_t> dsts, srcs;
+  for (int32_t i = 0; i < n_pairs; ++i) {
+    const int32_t a = pairs_host[2 * i], b = pairs_host[2 * i + 1];
+    if (a < 0 || a >= num_blocks || b < 0 || b >= num_blocks)
+      return fail(PKV_ERR_INVALID, "copy_blocks: block id outside the pool");
+    srcs.push_back(a);
+    dsts.push_back(b);
+  }
+  std::sort(dsts.begin(), dsts.end());
+  std::sort(srcs.begin(), srcs.end());
+  if (std::adjacent_find(dsts.begin(), dsts.end()) != dsts.end())
+    return fail(PKV_ERR_INVALID, "copy_blocks: a destination block appears twice");
+  for (int32_t d : dsts)
+    if (std::binary_search(srcs.begin(), srcs.end(), d))
+      return fail(PKV_ERR_INVALID, "copy_blocks: a destination block is also a source");
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  const size_t bytes = sizeof(int32_t) * 2 * static_cast<size_t>(n_pairs);
+  int32_t st = stage_and_copy(workspace, bytes, strm, "copy_blocks",
+                              [&](char* host) { std::memcpy(host, pairs_host, bytes); });
+  if (st != PKV_OK) return st;
+  pkv::CopyArgs c;
+  c.k_cache = k_cache;
+  c.v_cache = v_cache;
+  c.pairs = static_cast<const int32_t*>(workspace);
+  c.n_pairs = n_pairs;
+  c.chunks_per_block = static_cast<int32_t>(block_bytes / 16);
+  hipError_t e = pkv::launch_copy_blocks(c, strm);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("copy_blocks launch: ") + hipGetErrorString(e));
+  return ok();
+}
+
 extern "C" int32_t pkv_attention_workspace_size_ex(const int32_t* ctx_lens_host,
                                                    const int32_t* cu_seqlens_q_host, int32_t B,
                                                    int32_t num_q_heads, int32_t num_kv_heads,

@@ -21,6 +21,14 @@ struct WriteArgs {
   void* v_cache;
 };
 
+struct CopyArgs {
+  void* k_cache;
+  void* v_cache;
+  const int32_t* pairs;       // [2 * n_pairs] (src, dst) block ids, validated on the host
+  int32_t n_pairs;
+  int32_t chunks_per_block;   // block_size * num_kv_heads * head_dim * elem_bytes / 16
+};
+
 struct DecodeArgs {
   const void* q;
   const void* k_cache;
@@ -72,6 +80,7 @@ struct PrefillArgs {
 
 // Each launcher enqueues one kernel on `stream` and returns hipSuccess or the launch error.
 hipError_t launch_write_kv(const WriteArgs& a, hipStream_t stream);
+hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int64_t n_items, int head_dim, int group,
                          bool bf16, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int64_t n_items, int head_dim, hipStream_t stream);

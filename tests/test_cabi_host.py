@@ -298,3 +298,18 @@ def test_profile_kind_mask_validation():
     assert pkv.lib().pkv_profile_set_kinds(0x10) == L.PKV_ERR_INVALID
     pkv.profile_set_kinds(["decode"])
     pkv.profile_set_kinds(["write_kv", "prefill", "decode", "merge"])
+
+
+def test_copy_blocks_validation():
+    lib = pkv.lib()
+    pairs = np.asarray([1, 2, 3, 4], np.int32)
+    call = lambda pr, n=2, nb=8, dt=L.PKV_BF16, wsb=256: lib.pkv_copy_blocks(
+        1, 1, L._ptr(np.asarray(pr, np.int32)), n, nb, 16, 2, 128, dt, 1, wsb, None)
+    assert call([1, 2, 3, 8]) == L.PKV_ERR_INVALID          # id outside the pool
+    assert call([1, 2, 3, 2]) == L.PKV_ERR_INVALID          # destination twice
+    assert call([1, 2, 2, 4]) == L.PKV_ERR_INVALID          # destination is also a source
+    assert call([1, 2, 3, 4], wsb=8) == L.PKV_ERR_INVALID   # workspace too small
+    assert call([1, 2, 3, 4], dt=3) == L.PKV_ERR_INVALID
+    assert call([1, 2], n=0) == L.PKV_OK                    # nothing to copy
+    assert lib.pkv_copy_blocks(1, 1, L._ptr(pairs), 1, 8, 1, 1, 4, L.PKV_BF16, 1, 256,
+                               None) == L.PKV_ERR_UNSUPPORTED   # 8-byte blocks
