@@ -17,6 +17,8 @@ Modules
   scheduler  the host step builder: decodes first, chunked prefill within a token budget, FIFO
              admission, preemption of the youngest by recompute, prefix adoption of full
              blocks with the last prompt token recomputed, trim, copy-on-write forks.
+  fp8        the OCP E4M3 codec (nearest, ties to even, saturating at 448) and the FP8 KV
+             write with per-tensor scales (one float32 multiply by the float32 reciprocal).
 
 Every function is pinned by ``tests/test_oracle_*.py`` to something other than itself:
 torch's float64 scaled_dot_product_attention on contiguous K/V, closed forms (one key, zero
@@ -29,10 +31,11 @@ from .allocator import (BlockAllocator, AllocatorError, PoolExhausted, DoubleFre
                         InvalidBlock)
 from .harness import OracleStep, build_oracle_step
 from .scheduler import SchedConfig, Scheduler, SchedulerError, StepPlan
+from . import fp8
 
 __all__ = [
     "bf16_bits_to_f64", "write_kv", "gather", "attend_rows", "paged_attention", "OracleError",
     "BlockAllocator", "AllocatorError", "PoolExhausted", "DoubleFree", "SharedWrite",
     "InvalidBlock", "OracleStep", "build_oracle_step", "SchedConfig", "Scheduler",
-    "SchedulerError", "StepPlan",
+    "SchedulerError", "StepPlan", "fp8",
 ]

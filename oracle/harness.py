@@ -17,7 +17,8 @@ from typing import Iterable, Optional
 import numpy as np
 
 from .allocator import BlockAllocator
-from .paged import paged_attention, write_kv
+from .fp8 import dequantize, quantize_rows
+from .paged import attend_rows, bf16_bits_to_f64, gather, paged_attention, write_kv
 
 
 @dataclass
@@ -35,17 +36,51 @@ class OracleStep:
     def write_new(self) -> None:
         """The step's append: scatter the new rows through their slots."""
         w = self.workload
-        write_kv(self.k_pool, self.v_pool, self.k_new, self.v_new, self.new_slots, w.spec.BS)
+        _write(w, self.k_pool, self.v_pool, self.k_new, self.v_new, self.new_slots)
         self.written_new = True
 
     def attention(self, rows: Optional[Iterable[int]] = None) -> np.ndarray:
         w = self.workload
-        return paged_attention(w.q, self.k_pool, self.v_pool, self.block_tables, w.ctx_lens,
-                               w.cu_seqlens_q, w.scale,
-                               rows=None if rows is None else list(rows))
+        if not getattr(w, "kv_fp8", False):
+            return paged_attention(w.q, self.k_pool, self.v_pool, self.block_tables, w.ctx_lens,
+                                   w.cu_seqlens_q, w.scale,
+                                   rows=None if rows is None else list(rows))
+        # FP8 pools: each sequence's codes are gathered, then dequantised (code * scale) to
+        # float64 and attended exactly like any other pool
+        s = w.spec
+        want = None if rows is None else set(int(r) for r in rows)
+        out = np.full(w.q.shape, np.nan, dtype=np.float64)
+        for b in range(w.B):
+            lo, hi = int(w.cu_seqlens_q[b]), int(w.cu_seqlens_q[b + 1])
+            ts = [t for t in range(lo, hi) if want is None or t in want]
+            if not ts:
+                continue
+            ctx = int(w.ctx_lens[b])
+            kc = dequantize(gather(self.k_pool, self.block_tables[b], ctx, s.BS), s.k_scale)
+            vc = dequantize(gather(self.v_pool, self.block_tables[b], ctx, s.BS), s.v_scale)
+            positions = [ctx - (hi - lo) + (t - lo) for t in ts]
+            out[ts] = attend_rows(w.q[ts], kc, vc, positions, w.scale)
+        return out
+
+
+def _as_f32(rows: np.ndarray) -> np.ndarray:
+    """bfloat16 bits or float32 rows -> float32 values (exact)."""
+    if rows.dtype == np.uint16:
+        return bf16_bits_to_f64(rows).astype(np.float32)
+    return np.asarray(rows, dtype=np.float32)
+
+
+def _write(w, k_pool, v_pool, k_rows, v_rows, slots) -> None:
+    """The append of rows through slots; FP8 pools store the rows' E4M3 codes."""
+    if getattr(w, "kv_fp8", False):
+        k_rows = quantize_rows(_as_f32(k_rows), w.spec.k_scale)
+        v_rows = quantize_rows(_as_f32(v_rows), w.spec.v_scale)
+    write_kv(k_pool, v_pool, k_rows, v_rows, slots, w.spec.BS)
 
 
 def _poison(shape, dtype):
+    if dtype == np.uint8:
+        return np.full(shape, 0x7F, dtype=np.uint8)        # E4M3 NaN
     if dtype == np.uint16:
         return np.full(shape, 0x7FC0, dtype=np.uint16)     # bfloat16 quiet NaN
     return np.full(shape, np.nan, dtype=np.float32)
@@ -67,9 +102,10 @@ def build_oracle_step(w, seqs: Optional[Iterable[int]] = None, poison: bool = Tr
 
     tables = np.full((B, w.max_blocks), -1, dtype=np.int32)
     dt = w.np_dtype
+    pdt = np.uint8 if getattr(w, "kv_fp8", False) else dt
     shape = (NB, BS, s.Hkv, s.D)
-    k_pool = _poison(shape, dt) if poison else np.zeros(shape, dtype=dt)
-    v_pool = _poison(shape, dt) if poison else np.zeros(shape, dtype=dt)
+    k_pool = _poison(shape, pdt) if poison else np.zeros(shape, dtype=pdt)
+    v_pool = _poison(shape, pdt) if poison else np.zeros(shape, dtype=pdt)
     chosen = set(range(B)) if seqs is None else set(int(b) for b in seqs)
 
     k_new = np.zeros((w.T, s.Hkv, s.D), dtype=dt)
@@ -94,7 +130,7 @@ def build_oracle_step(w, seqs: Optional[Iterable[int]] = None, poison: bool = Tr
             kv_cache[b] = (kk, vv)
             if prior > start:
                 sl = alloc.slots(row, start, prior - start, BS)
-                write_kv(k_pool, v_pool, kk[start:prior], vv[start:prior], sl, BS)
+                _write(w, k_pool, v_pool, kk[start:prior], vv[start:prior], sl)
 
     for b in range(B):
         ql = int(w.q_lens[b])
@@ -117,7 +153,7 @@ def build_oracle_step(w, seqs: Optional[Iterable[int]] = None, poison: bool = Tr
             for b in chosen:
                 lo, hi = int(w.cu_seqlens_q[b]), int(w.cu_seqlens_q[b + 1])
                 keep[lo:hi] = new_slots[lo:hi]
-            write_kv(k_pool, v_pool, k_new, v_new, keep, BS)
+            _write(w, k_pool, v_pool, k_new, v_new, keep)
             st.written_new = True
         else:
             st.write_new()

@@ -89,6 +89,11 @@ class Spec:
     k_outlier: Optional[tuple] = None
     interleave: bool = False
     kv_split: int = 512
+    # "fp8": the pools hold OCP E4M3 codes with per-tensor scales (q and the K/V rows that
+    # are written stay in `dtype`); "" keeps the pools in `dtype`
+    kv_dtype: str = ""
+    k_scale: float = 1.0
+    v_scale: float = 1.0
 
     @property
     def G(self) -> int:
@@ -151,6 +156,15 @@ class Workload:
     @property
     def elem_bytes(self) -> int:
         return 2 if self.spec.dtype == "bf16" else 4
+
+    @property
+    def kv_fp8(self) -> bool:
+        return self.spec.kv_dtype == "fp8"
+
+    @property
+    def kv_elem_bytes(self) -> int:
+        """Bytes per stored K/V element (the pools' element type)."""
+        return 1 if self.kv_fp8 else self.elem_bytes
 
     # ---- K/V values ---------------------------------------------------------------------
     def _draw(self, rng: np.random.Generator, n: int) -> Tuple[np.ndarray, np.ndarray]:
@@ -340,3 +354,32 @@ SMALL_CONFIGS = {
     "prefix-shared-decode": Spec("prefix-shared-decode-small", "bf16", Hq=16, Hkv=4, D=128,
                                  BS=16, shared=(2, 3, 64, 1, 600)),
 }
+
+
+# The batched decode and mixed steps with FP8 (OCP E4M3) pools and per-tensor scales 1/64
+# (N(0, 1) values of a few units stay far inside the E4M3 range): q and the written K/V rows are
+# bfloat16, the pools hold their codes.
+FP8_CONFIGS = {
+    "batched-fp8-decode": Spec("batched-fp8-decode", "bf16", Hq=32, Hkv=8, D=128, BS=16,
+                               decode_ctx=("lognormal", 2048, 1.0, 16, 16384, 64),
+                               kv_dtype="fp8", k_scale=1 / 64, v_scale=1 / 64),
+    "mixed-fp8-step": Spec("mixed-fp8-step", "bf16", Hq=32, Hkv=8, D=128, BS=16,
+                           decode_ctx=("lognormal", 3000, 1.0, 16, 16384, 120),
+                           prefill=(8, 512, 0, 8192), interleave=True,
+                           kv_dtype="fp8", k_scale=1 / 64, v_scale=1 / 64),
+}
+
+FP8_SMALL_CONFIGS = {
+    "batched-fp8-decode": Spec("batched-fp8-decode-small", "bf16", Hq=32, Hkv=8, D=128, BS=16,
+                               decode_ctx=("lognormal", 300, 1.0, 1, 1500, 6),
+                               kv_dtype="fp8", k_scale=1 / 64, v_scale=1 / 64),
+    "mixed-fp8-step": Spec("mixed-fp8-step-small", "bf16", Hq=32, Hkv=8, D=128, BS=16,
+                           decode_ctx=("lognormal", 300, 1.0, 1, 1200, 5),
+                           prefill=(3, 130, 0, 700), interleave=True,
+                           kv_dtype="fp8", k_scale=1 / 64, v_scale=1 / 32),
+    "prefix-shared-fp8-decode": Spec("prefix-shared-fp8-decode-small", "bf16", Hq=16, Hkv=4,
+                                     D=64, BS=16, shared=(2, 3, 64, 1, 600),
+                                     kv_dtype="fp8", k_scale=0.02, v_scale=0.015),
+}
+
+ALL_CONFIGS = {**CONFIGS, **FP8_CONFIGS}
