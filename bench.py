@@ -11,7 +11,9 @@ are resident in HBM before timing starts; the timed region is bracketed by devic
 synchronisation. The headline workload is the batched bf16 decode step (64 sequences,
 lognormal lengths with median 2048, Hq 32, Hkv 8, D 128, block 16), reported as algorithmic
 GB/s (KV bytes read + append bytes moved, per step time). The mixed ragged step
-(8 x 512-row prefill chunks + 120 decodes) is reported alongside in tokens/s.
+(8 x 512-row prefill chunks + 120 decodes) is reported alongside in tokens/s, and the same
+batched decode step over E4M3 pools with per-tensor scales (pkv_write_kv_attention_fp8; its
+bytes counted at one byte per cached element).
 
 Prints ONE JSON line (rank 0, N = 1). `--gpus N` with N > 1 exits: this build runs on one GPU.
 """
@@ -37,7 +39,7 @@ def _parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="batched-bf16-decode")
-    ap.add_argument("--extra", default="mixed-ragged-step",
+    ap.add_argument("--extra", default="mixed-ragged-step,batched-fp8-decode",
                     help="comma-separated workloads timed the same way, reported under 'extra'")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline sample")
@@ -76,7 +78,7 @@ def _step_inputs(w, gst):
 
 def _kv_bytes(w):
     from prefill_slot_mapping_amd import accounting as acc
-    return acc.decode_kv_bytes(w.ctx_lens, w.spec.Hkv, w.spec.D, w.elem_bytes)
+    return acc.decode_kv_bytes(w.ctx_lens, w.spec.Hkv, w.spec.D, w.kv_elem_bytes)
 
 
 def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
@@ -89,9 +91,11 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
     import prefill_slot_mapping_amd as pkv
     from prefill_slot_mapping_amd import accounting as acc
     from prefill_slot_mapping_amd.harness import build_gpu_step
-    from workloads import CONFIGS, make_workload
+    from workloads import ALL_CONFIGS, make_workload
 
-    w = make_workload(CONFIGS[name])
+    w = make_workload(ALL_CONFIGS[name])
+    if w.kv_fp8 and phase_consistent:
+        raise ValueError("E4M3 pools have no phase-consistent tile path")
     t_build = time.time()
     gst = build_gpu_step(w, device=device)
     t_build = time.time() - t_build
@@ -101,9 +105,13 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
     ctx_np = np.ascontiguousarray(w.ctx_lens, dtype=np.int32)
     cu_np = np.ascontiguousarray(w.cu_seqlens_q, dtype=np.int32)
     bt_np = np.ascontiguousarray(gst.block_tables, dtype=np.int32)
-    ws_bytes = pkv.write_kv_attention_workspace_size(
-        ctx_np, cu_np, s.Hq, s.Hkv, s.D, w.T, s.kv_split,
-        pkv.PKV_BF16 if s.dtype == "bf16" else pkv.PKV_F32, phase_consistent)
+    if w.kv_fp8:
+        ws_bytes = pkv.write_kv_attention_fp8_workspace_size(ctx_np, cu_np, s.Hq, s.Hkv, s.D,
+                                                             w.T, s.kv_split)
+    else:
+        ws_bytes = pkv.write_kv_attention_workspace_size(
+            ctx_np, cu_np, s.Hq, s.Hkv, s.D, w.T, s.kv_split,
+            pkv.PKV_BF16 if s.dtype == "bf16" else pkv.PKV_F32, phase_consistent)
     workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=device)
     out = torch.empty((w.T, s.Hq, s.D), dtype=torch.float32, device=device)
 
@@ -111,6 +119,12 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
         # host slot mapping of the step's new rows, then one library call: the slots and the
         # attention work lists go to the device in one copy, then append, attention, merge
         sl = pkv.slot_mapping_step(gst.allocator, bt_np, s.BS, starts, n_new, out=slots_np)
+        if w.kv_fp8:
+            pkv.write_kv_attention_fp8(gst.q, gst.k_new, gst.v_new, sl, gst.k_cache, gst.v_cache,
+                                       gst.block_tables_dev, ctx_np, cu_np, w.scale, s.k_scale,
+                                       s.v_scale, out=out, workspace=workspace,
+                                       kv_split=s.kv_split)
+            return
         pkv.write_kv_attention(gst.q, gst.k_new, gst.v_new, sl, gst.k_cache, gst.v_cache,
                                gst.block_tables_dev, ctx_np, cu_np, w.scale, out=out,
                                workspace=workspace, kv_split=s.kv_split,
@@ -136,7 +150,8 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
     # record costs the stream a few microseconds, so bracketing every launch of every kernel
     # would stretch the step it times). Every kernel's time is then taken in a second, untimed
     # pass of the same steps with all launches bracketed.
-    dominant = "decode" if (w.q_lens == 1).any() and not phase_consistent else "prefill"
+    dominant = "decode" if (w.kv_fp8 or (w.q_lens == 1).any()) and not phase_consistent \
+        else "prefill"
     gc.callbacks.append(on_gc)
     if kernel_events == "timed":
         pkv.profile_set_kinds([])
@@ -171,12 +186,13 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
 
     ms_step = dt / steps * 1e3
     kv = _kv_bytes(w)
-    app = acc.append_bytes(w.T, s.Hkv, s.D, w.elem_bytes)
+    app = acc.append_bytes(w.T, s.Hkv, s.D, w.elem_bytes, w.kv_elem_bytes)
     decode_rows = w.q_lens == 1
-    dec_kv = acc.decode_kv_bytes(w.ctx_lens[decode_rows], s.Hkv, s.D, w.elem_bytes)
+    dec_kv = acc.decode_kv_bytes(w.ctx_lens[decode_rows], s.Hkv, s.D, w.kv_elem_bytes)
     flops = acc.attention_flops(w.ctx_lens[~decode_rows], w.q_lens[~decode_rows], s.Hq, s.D)
     res = {
         "workload": name, "phase_consistent": phase_consistent, "B": w.B, "T": w.T,
+        "kv_dtype": s.kv_dtype or s.dtype,
         "ms_per_step": ms_step,
         "step_gbs": (kv + app) / (ms_step * 1e-3) / 1e9, "tokens_per_s": w.T / (ms_step * 1e-3),
         "kv_bytes": kv, "append_bytes": app, "decode_kv_bytes": dec_kv, "prefill_flops": flops,

@@ -328,6 +328,71 @@ int32_t pkv_write_kv_attention(const void* q, const void* k_new, const void* v_n
                                int32_t kv_split, int32_t dtype, uint32_t flags, float* out,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- FP8 (OCP E4M3) KV pools with per-tensor scales [BC section 4.2: the KV cache kept in
+ *      FP8, about 57 % of the BF16 bytes, one write path; P3 "Design > paged.py" and its
+ *      single-device notes: a K/V dtype other than the model's is dequantised on read, and
+ *      FP8 without per-tensor scales is visibly lossy] -------------------------------------
+ * A pool element is one byte, an E4M3 code (bias 7, largest finite 448, S.1111.111 NaN, no
+ * infinities); the value it stands for is decode(code) * scale, with one float32 scale for
+ * the whole K pool (k_scale) and one for the V pool (v_scale), both finite and > 0.
+ *
+ * pkv_write_kv_fp8: quantises and scatters. For row t and element e, with x the bfloat16
+ * input, the code stored is E4M3(clamp(float32(x) * float32(1 / scale), -448, 448)) rounded to
+ * nearest, ties to even (saturating; -0 keeps its sign). NaN inputs are not supported.
+ *   k_new, v_new: device bfloat16 [n_rows, num_kv_heads, head_dim] contiguous.
+ *   slots_dev, k_cache, v_cache: as pkv_write_kv, the pools uint8 [num_blocks, block_size,
+ *                 num_kv_heads, head_dim]. num_kv_heads * head_dim a multiple of 16.
+ * Errors: PKV_ERR_INVALID (sizes, NULL pointers, scales), PKV_ERR_UNSUPPORTED (row width),
+ * PKV_ERR_HIP. n_rows == 0 is a no-op.
+ *
+ * pkv_attention_fp8: pkv_attention over E4M3 pools, q bfloat16, out float32, every row (decode
+ * and prefill) on the split decode pass: same splits, tiles, wave order and merge order, hence
+ * the same batch invariance as pkv_attention's decode rows. K codes widen exactly to bfloat16
+ * and meet q in float32 products; k_scale folds into the score scale; V codes widen exactly to
+ * float32 and v_scale multiplies each split's numerator once. head_dim 64 or 128,
+ * num_q_heads / num_kv_heads in {1, 2, 4}. Workspace from pkv_attention_fp8_workspace_size,
+ * same ownership rules as pkv_attention. Errors: as pkv_attention, plus PKV_ERR_INVALID for
+ * scales that are not finite and > 0. */
+int32_t pkv_write_kv_fp8(const void* k_new, const void* v_new, const int32_t* slots_dev,
+                         int32_t n_rows, void* k_cache, void* v_cache, int32_t num_blocks,
+                         int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                         float k_scale, float v_scale, void* stream);
+
+int32_t pkv_attention_fp8_workspace_size(const int32_t* ctx_lens_host,
+                                         const int32_t* cu_seqlens_q_host, int32_t B,
+                                         int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t kv_split, size_t* bytes);
+
+int32_t pkv_attention_fp8(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables_dev, int32_t max_blocks,
+                          const int32_t* ctx_lens_host, const int32_t* cu_seqlens_q_host,
+                          int32_t B, int32_t T, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                          float k_scale, float v_scale, int32_t kv_split, float* out,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Fused E4M3 step: pkv_write_kv_fp8 of k_new / v_new through host slots followed by
+ * pkv_attention_fp8, with the slots in the same host-to-device copy as the work lists, as
+ * pkv_write_kv_attention does for bfloat16 / float32 pools (same slot rules: negative skips,
+ * >= num_blocks * block_size is PKV_ERR_INVALID). Workspace from
+ * pkv_write_kv_attention_fp8_workspace_size (n_rows >= 0). Errors: as pkv_write_kv_fp8 and
+ * pkv_attention_fp8. */
+int32_t pkv_write_kv_attention_fp8_workspace_size(const int32_t* ctx_lens_host,
+                                                  const int32_t* cu_seqlens_q_host, int32_t B,
+                                                  int32_t num_q_heads, int32_t num_kv_heads,
+                                                  int32_t head_dim, int32_t kv_split,
+                                                  int32_t n_rows, size_t* bytes);
+
+int32_t pkv_write_kv_attention_fp8(const void* q, const void* k_new, const void* v_new,
+                                   const int32_t* slots_host, int32_t n_rows, void* k_cache,
+                                   void* v_cache, const int32_t* block_tables_dev,
+                                   int32_t max_blocks, const int32_t* ctx_lens_host,
+                                   const int32_t* cu_seqlens_q_host, int32_t B, int32_t T,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t num_blocks, float scale,
+                                   float k_scale, float v_scale, int32_t kv_split, float* out,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- diagnostics: per-kernel device time ------------------------------------------------
  * While enabled, every kernel launched by pkv_write_kv / pkv_attention is bracketed by two HIP
  * events recorded on its launch stream (the library owns the events). pkv_profile_read waits

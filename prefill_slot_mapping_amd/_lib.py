@@ -131,6 +131,20 @@ _SIGS = {
     "pkv_write_kv_attention": ([_vp, _vp, _vp, _pi32, _i32, _vp, _vp, _vp, _i32, _pi32, _pi32,
                                 _i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32,
                                 _i32, ctypes.c_uint32, _vp, _vp, ctypes.c_size_t, _vp], _i32),
+    "pkv_write_kv_fp8": ([_vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
+                          ctypes.c_float, ctypes.c_float, _vp], _i32),
+    "pkv_attention_fp8_workspace_size": ([_pi32, _pi32, _i32, _i32, _i32, _i32, _i32,
+                                          ctypes.POINTER(ctypes.c_size_t)], _i32),
+    "pkv_attention_fp8": ([_vp, _vp, _vp, _vp, _i32, _pi32, _pi32, _i32, _i32, _i32, _i32,
+                           _i32, _i32, _i32, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                           _i32, _vp, _vp, ctypes.c_size_t, _vp], _i32),
+    "pkv_write_kv_attention_fp8_workspace_size": ([_pi32, _pi32, _i32, _i32, _i32, _i32, _i32,
+                                                   _i32, ctypes.POINTER(ctypes.c_size_t)],
+                                                  _i32),
+    "pkv_write_kv_attention_fp8": ([_vp, _vp, _vp, _pi32, _i32, _vp, _vp, _vp, _i32, _pi32,
+                                    _pi32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                    ctypes.c_float, ctypes.c_float, ctypes.c_float, _i32, _vp,
+                                    _vp, ctypes.c_size_t, _vp], _i32),
     "pkv_profile_set_kinds": ([ctypes.c_uint32], _i32),
     "pkv_profile_enable": ([_i32], _i32),
     "pkv_profile_read": ([_i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)], _i32),
@@ -554,6 +568,141 @@ def write_kv_attention(q, k_new, v_new, slots, k_cache, v_cache, block_tables, c
         v_cache.data_ptr(), block_tables.data_ptr(), int(block_tables.shape[1]), _ptr(ctx),
         _ptr(cu), B, T, hq, hkv, d, bs, nb, float(scale), int(kv_split), dt, flags,
         out.data_ptr(), workspace.data_ptr(), ws_have, _stream_ptr(q, stream)))
+    return out
+
+
+# ---- FP8 (E4M3) pools with per-tensor scales ----------------------------------------------
+
+def _need_fp8_pools(k_cache, v_cache):
+    import torch
+    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+        raise ValueError("E4M3 pools are uint8 tensors of codes")
+    if v_cache.shape != k_cache.shape or k_cache.dim() != 4:
+        raise ValueError("pools must both be [num_blocks, block_size, num_kv_heads, head_dim]")
+
+
+def write_kv_fp8(k_new, v_new, slots, k_cache, v_cache, k_scale: float, v_scale: float,
+                 stream=None) -> None:
+    """pkv_write_kv_fp8: quantise bfloat16 rows of k_new / v_new [T_w, Hkv, D] to E4M3 codes
+    (value / scale, saturating, ties to even) and scatter them into the uint8 pools."""
+    import torch
+    _need_cuda(k_new, v_new, k_cache, v_cache)
+    _need_fp8_pools(k_cache, v_cache)
+    if k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16:
+        raise ValueError("k_new / v_new must be bfloat16")
+    nb, bs, hkv, d = k_cache.shape
+    if hasattr(slots, "is_cuda") and slots.is_cuda:
+        sl = slots
+    else:
+        host = _host_i32(slots)
+        validate_slots(host, nb * bs)
+        sl = torch.from_numpy(host).to(k_cache.device)
+    if sl.dtype != torch.int32 or not sl.is_contiguous():
+        raise ValueError("slots must be a contiguous int32 tensor")
+    _check(lib().pkv_write_kv_fp8(k_new.data_ptr(), v_new.data_ptr(), sl.data_ptr(),
+                                  int(k_new.shape[0]), k_cache.data_ptr(), v_cache.data_ptr(),
+                                  nb, bs, hkv, d, float(k_scale), float(v_scale),
+                                  _stream_ptr(k_cache, stream)))
+
+
+def attention_fp8_workspace_size(ctx_lens, cu_seqlens_q, num_q_heads: int, num_kv_heads: int,
+                                 head_dim: int, kv_split: int = 512) -> int:
+    ctx = _host_i32(ctx_lens)
+    cu = _host_i32(cu_seqlens_q)
+    out = ctypes.c_size_t(0)
+    _check(lib().pkv_attention_fp8_workspace_size(_ptr(ctx), _ptr(cu), ctx.size,
+                                                  int(num_q_heads), int(num_kv_heads),
+                                                  int(head_dim), int(kv_split),
+                                                  ctypes.byref(out)))
+    return int(out.value)
+
+
+def attention_fp8(q, k_cache, v_cache, block_tables, ctx_lens, cu_seqlens_q, scale: float,
+                  k_scale: float, v_scale: float, out=None, workspace=None,
+                  kv_split: int = 512, stream=None):
+    """pkv_attention_fp8: the ragged step over E4M3 pools (uint8 [NB, BS, Hkv, D]) with
+    per-tensor scales; q bfloat16 [T, Hq, D]; returns out (float32 [T, Hq, D])."""
+    import torch
+    _need_cuda(q, k_cache, v_cache, block_tables)
+    _need_fp8_pools(k_cache, v_cache)
+    if block_tables.dtype != torch.int32:
+        raise ValueError("block_tables must be int32")
+    if q.dtype != torch.bfloat16:
+        raise ValueError("q must be bfloat16")
+    ctx = _host_i32(ctx_lens)
+    cu = _host_i32(cu_seqlens_q)
+    T, hq, d = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    if d2 != d:
+        raise ValueError("q / pool head_dim mismatch")
+    B = ctx.size
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B, max_blocks]")
+    if out is None:
+        out = torch.empty((T, hq, d), dtype=torch.float32, device=q.device)
+    _need_cuda(out)
+    need = attention_fp8_workspace_size(ctx, cu, hq, hkv, d, kv_split)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().pkv_attention_fp8(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+        int(block_tables.shape[1]), _ptr(ctx), _ptr(cu), B, T, hq, hkv, d, bs, nb, float(scale),
+        float(k_scale), float(v_scale), int(kv_split), out.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream_ptr(q, stream)))
+    return out
+
+
+def write_kv_attention_fp8_workspace_size(ctx_lens, cu_seqlens_q, num_q_heads: int,
+                                         num_kv_heads: int, head_dim: int, n_rows: int,
+                                         kv_split: int = 512) -> int:
+    ctx = _host_i32(ctx_lens)
+    cu = _host_i32(cu_seqlens_q)
+    out = ctypes.c_size_t(0)
+    _check(lib().pkv_write_kv_attention_fp8_workspace_size(
+        _ptr(ctx), _ptr(cu), ctx.size, int(num_q_heads), int(num_kv_heads), int(head_dim),
+        int(kv_split), int(n_rows), ctypes.byref(out)))
+    return int(out.value)
+
+
+def write_kv_attention_fp8(q, k_new, v_new, slots, k_cache, v_cache, block_tables, ctx_lens,
+                           cu_seqlens_q, scale: float, k_scale: float, v_scale: float, out=None,
+                           workspace=None, kv_split: int = 512, stream=None):
+    """pkv_write_kv_attention_fp8: the E4M3 append of bfloat16 k_new / v_new [T_w, Hkv, D]
+    through host slots [T_w] and the attention over the step in one call; returns out."""
+    import torch
+    _need_cuda(q, k_new, v_new, k_cache, v_cache, block_tables)
+    _need_fp8_pools(k_cache, v_cache)
+    if block_tables.dtype != torch.int32:
+        raise ValueError("block_tables must be int32")
+    if q.dtype != torch.bfloat16 or k_new.dtype != torch.bfloat16 or \
+            v_new.dtype != torch.bfloat16:
+        raise ValueError("q, k_new and v_new must be bfloat16")
+    sl = slots if isinstance(slots, np.ndarray) and slots.dtype == np.int32 and \
+        slots.flags.c_contiguous else _host_i32(slots)
+    ctx = _host_i32(ctx_lens)
+    cu = _host_i32(cu_seqlens_q)
+    T, hq, d = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    if d2 != d:
+        raise ValueError("q / pool head_dim mismatch")
+    n_rows = int(k_new.shape[0])
+    if sl.size != n_rows or v_new.shape != k_new.shape:
+        raise ValueError("slots / k_new / v_new row counts differ")
+    B = ctx.size
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B, max_blocks]")
+    if out is None:
+        out = torch.empty((T, hq, d), dtype=torch.float32, device=q.device)
+    _need_cuda(out)
+    if workspace is None:
+        need = write_kv_attention_fp8_workspace_size(ctx, cu, hq, hkv, d, n_rows, kv_split)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().pkv_write_kv_attention_fp8(
+        q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), _ptr(sl), n_rows, k_cache.data_ptr(),
+        v_cache.data_ptr(), block_tables.data_ptr(), int(block_tables.shape[1]), _ptr(ctx),
+        _ptr(cu), B, T, hq, hkv, d, bs, nb, float(scale), float(k_scale), float(v_scale),
+        int(kv_split), out.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream_ptr(q, stream)))
     return out
 
 

@@ -37,9 +37,13 @@ def kv_read_time_ms(batch: int, ctx: int, bytes_per_token: int, hbm_bytes_per_s:
     return batch * ctx * bytes_per_token / hbm_bytes_per_s * 1e3
 
 
-def append_bytes(n_rows: int, kv_heads: int, head_dim: int, elem_bytes: int) -> int:
-    """Bytes the KV append moves: read and write K and V of every new row."""
-    return 2 * 2 * n_rows * kv_heads * head_dim * elem_bytes
+def append_bytes(n_rows: int, kv_heads: int, head_dim: int, elem_bytes: int,
+                 pool_elem_bytes: int = 0) -> int:
+    """Bytes the KV append moves: read K and V of every new row (elem_bytes per element) and
+    write them into the pools (pool_elem_bytes per element; 0 means the same type, 1 for E4M3
+    codes)."""
+    out_b = pool_elem_bytes or elem_bytes
+    return 2 * n_rows * kv_heads * head_dim * (elem_bytes + out_b)
 
 
 def visible_pairs(ctx: int, q_len: int) -> int:

@@ -21,16 +21,16 @@ LIB_PATH = os.path.join(PKG_DIR, "libpkv.so")
 ARCH = "gfx950"
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
-DEVICE_SOURCES = ["write_kv.hip", "decode.hip", "merge.hip", "prefill.hip"]
+DEVICE_SOURCES = ["write_kv.hip", "decode.hip", "decode_fp8.hip", "merge.hip", "prefill.hip"]
 HOST_SOURCES = ["allocator.cpp", "api.cpp", "scheduler.cpp"]
 
 # Packed-FP32 instructions are disabled for all device code: the compiler may not form
 # v_pk_{add,mul,fma}_f32 from ordinary float code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-# Per-source extras. decode.hip: no floating-point operation there sees a NaN (bad rows are
+# Per-source extras. decode.hip, decode_fp8.hip: no floating-point operation there sees a NaN (bad rows are
 # written as a NaN bit pattern through an integer select), which lets maxima fuse with their
 # DPP lane permutes.
-SOURCE_FLAGS = {"decode.hip": ["-fno-honor-nans"]}
+SOURCE_FLAGS = {"decode.hip": ["-fno-honor-nans"], "decode_fp8.hip": ["-fno-honor-nans"]}
 
 
 def hipcc() -> str:

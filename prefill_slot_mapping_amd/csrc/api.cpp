@@ -30,6 +30,9 @@ namespace {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// The kernels move 16-byte vectors through q, the new rows, the pools and the workspace.
+bool misaligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
 bool valid_dtype(int32_t dt) { return dt == PKV_F32 || dt == PKV_BF16; }
 int elem_bytes(int32_t dt) { return dt == PKV_BF16 ? 2 : 4; }
 
@@ -379,6 +382,9 @@ int32_t check_write(const void* k_new, const void* v_new, int32_t n_rows, const 
   if (n_rows > 0 && (k_new == nullptr || v_new == nullptr || k_cache == nullptr ||
                      v_cache == nullptr))
     return fail(PKV_ERR_INVALID, "write_kv: NULL pointer");
+  if (n_rows > 0 && (misaligned16(k_new) || misaligned16(v_new) || misaligned16(k_cache) ||
+                     misaligned16(v_cache)))
+    return fail(PKV_ERR_INVALID, "write_kv: device pointers must be 16-byte aligned");
   if (static_cast<int64_t>(n_rows) * (row_bytes / 16) > 0xffffffffLL)
     return fail(PKV_ERR_UNSUPPORTED, "write_kv: too many rows in one call");
   a->k_new = k_new;
@@ -400,6 +406,50 @@ int32_t launch_write(const pkv::WriteArgs& a, hipStream_t strm) {
   return PKV_OK;
 }
 
+// Validated arguments of an E4M3 append (pkv_write_kv_fp8 or the append of
+// pkv_write_kv_attention_fp8).
+int32_t check_write_fp8(const void* k_new, const void* v_new, int32_t n_rows,
+                        const void* k_cache, const void* v_cache, int32_t num_blocks,
+                        int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                        float k_scale, float v_scale, pkv::WriteFp8Args* a) {
+  if (n_rows < 0 || num_blocks < 0 || block_size <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+    return fail(PKV_ERR_INVALID, "write_kv_fp8: bad sizes");
+  if (!(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
+    return fail(PKV_ERR_INVALID, "write_kv_fp8: scales must be finite and > 0");
+  const int64_t row_codes = static_cast<int64_t>(num_kv_heads) * head_dim;
+  if (row_codes % 16 != 0)
+    return fail(PKV_ERR_UNSUPPORTED, "write_kv_fp8: num_kv_heads * head_dim must be a multiple "
+                                     "of 16");
+  if (n_rows > 0 && (k_new == nullptr || v_new == nullptr || k_cache == nullptr ||
+                     v_cache == nullptr))
+    return fail(PKV_ERR_INVALID, "write_kv_fp8: NULL pointer");
+  if (n_rows > 0 && (misaligned16(k_new) || misaligned16(v_new) || misaligned16(k_cache) ||
+                     misaligned16(v_cache)))
+    return fail(PKV_ERR_INVALID, "write_kv_fp8: device pointers must be 16-byte aligned");
+  if (static_cast<int64_t>(n_rows) * (row_codes / 16) > 0x7fffffffLL)
+    return fail(PKV_ERR_UNSUPPORTED, "write_kv_fp8: too many rows in one call");
+  a->k_new = k_new;
+  a->v_new = v_new;
+  a->slots = nullptr;
+  a->n_rows = n_rows;
+  a->chunks_per_row = static_cast<int32_t>(row_codes / 16);
+  a->n_slots = static_cast<int64_t>(num_blocks) * block_size;
+  a->k_inv_scale = 1.0f / k_scale;
+  a->v_inv_scale = 1.0f / v_scale;
+  a->k_cache = const_cast<void*>(k_cache);
+  a->v_cache = const_cast<void*>(v_cache);
+  return PKV_OK;
+}
+
+int32_t launch_write_fp8(const pkv::WriteFp8Args& a, hipStream_t strm) {
+  const int pr = prof_begin(0, strm);
+  hipError_t e = pkv::launch_write_kv_fp8(a, strm);
+  prof_end(pr, strm);
+  if (e != hipSuccess)
+    return fail(PKV_ERR_HIP, std::string("write_kv_fp8 launch: ") + hipGetErrorString(e));
+  return PKV_OK;
+}
+
 // One attention call, optionally preceded by a KV append whose slots come from host memory
 // (wr != nullptr): the slots travel in the same host-to-device copy as the work lists.
 int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
@@ -409,11 +459,24 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
                        int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
                        int32_t kv_split, int32_t dtype, uint32_t flags, float* out,
                        void* workspace, size_t workspace_bytes, void* stream,
-                       pkv::WriteArgs* wr, const int32_t* slots_host) {
+                       pkv::WriteArgs* wr, const int32_t* slots_host,
+                       const float* fp8_scales = nullptr, pkv::WriteFp8Args* wr8 = nullptr) {
+  // fp8_scales != nullptr: q is bfloat16 and the pools hold E4M3 codes with per-tensor scales
+  // {k_scale, v_scale}; every row runs on the split decode pass over those pools
   int32_t st = check_heads(num_q_heads, num_kv_heads, head_dim, kv_split, dtype);
   if (st != PKV_OK) return st;
   st = check_flags(flags, num_q_heads, num_kv_heads, head_dim, dtype);
   if (st != PKV_OK) return st;
+  if (fp8_scales != nullptr) {
+    if (dtype != PKV_BF16 || flags != 0)
+      return fail(PKV_ERR_INVALID, "attention_fp8: q must be bfloat16 and flags 0");
+    if (!pkv::decode_fp8_supported(head_dim, num_q_heads / num_kv_heads))
+      return fail(PKV_ERR_UNSUPPORTED, "attention_fp8: head_dim 64 or 128 and num_q_heads / "
+                                       "num_kv_heads one of 1, 2, 4");
+    for (int i = 0; i < 2; ++i)
+      if (!(std::isfinite(fp8_scales[i]) && fp8_scales[i] > 0.f))
+        return fail(PKV_ERR_INVALID, "attention_fp8: scales must be finite and > 0");
+  }
   if (block_size <= 0 || num_blocks <= 0 || max_blocks < 0)
     return fail(PKV_ERR_INVALID, "block_size, num_blocks must be > 0 and max_blocks >= 0");
   if (static_cast<int64_t>(num_blocks) * block_size > INT32_MAX)
@@ -422,11 +485,12 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
   st = check_step(ctx_lens_host, cu_seqlens_q_host, B, T,
                   static_cast<int64_t>(max_blocks) * block_size);
   if (st != PKV_OK) return st;
-  const int32_t n_write = wr != nullptr ? wr->n_rows : 0;
+  const int32_t n_write = wr != nullptr ? wr->n_rows : (wr8 != nullptr ? wr8->n_rows : 0);
+  const int64_t n_slots = wr != nullptr ? wr->n_slots : (wr8 != nullptr ? wr8->n_slots : 0);
   if (n_write > 0) {
     if (slots_host == nullptr) return fail(PKV_ERR_INVALID, "write_kv_attention: slots_host is NULL");
     for (int32_t i = 0; i < n_write; ++i)
-      if (slots_host[i] >= wr->n_slots)
+      if (slots_host[i] >= n_slots)
         return fail(PKV_ERR_INVALID, "write_kv_attention: slot " + std::to_string(slots_host[i]) +
                                          " outside the pool");
   }
@@ -434,9 +498,15 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
   if (T > 0 && (q == nullptr || k_cache == nullptr || v_cache == nullptr ||
                 block_tables_dev == nullptr || out == nullptr))
     return fail(PKV_ERR_INVALID, "attention: NULL device pointer");
+  if (T > 0 && (misaligned16(q) || misaligned16(k_cache) || misaligned16(v_cache) ||
+                misaligned16(workspace) || (reinterpret_cast<uintptr_t>(out) & 3u) != 0 ||
+                (reinterpret_cast<uintptr_t>(block_tables_dev) & 3u) != 0))
+    return fail(PKV_ERR_INVALID, "attention: q, pools and workspace must be 16-byte aligned, "
+                                 "out and block_tables 4-byte aligned");
 
-  const StepShape s = shape_for(ctx_lens_host, cu_seqlens_q_host, B, num_q_heads, num_kv_heads,
-                                head_dim, kv_split, dtype, flags);
+  StepShape s = shape_for(ctx_lens_host, cu_seqlens_q_host, B, num_q_heads, num_kv_heads,
+                          head_dim, kv_split, dtype, flags);
+  if (fp8_scales != nullptr) s.prefill_on_mfma = false;
   const pkv::WorkspaceLayout L = layout_for(s, num_q_heads, head_dim, n_write);
   if (workspace_bytes < L.total || (L.total > 0 && workspace == nullptr))
     return fail(PKV_ERR_INVALID, "attention: workspace smaller than the workspace-size query (" +
@@ -457,8 +527,14 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
     if (st != PKV_OK) return st;
   }
   if (n_write > 0) {
-    wr->slots = reinterpret_cast<const int32_t*>(ws + L.slots_off);
-    st = launch_write(*wr, strm);
+    const int32_t* slots_dev = reinterpret_cast<const int32_t*>(ws + L.slots_off);
+    if (wr != nullptr) {
+      wr->slots = slots_dev;
+      st = launch_write(*wr, strm);
+    } else {
+      wr8->slots = slots_dev;
+      st = launch_write_fp8(*wr8, strm);
+    }
     if (st != PKV_OK) return st;
   }
   if (T == 0) return ok();
@@ -508,6 +584,12 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
     d.hkv = num_kv_heads;
     d.kv_split = kv_split;
     d.scale_log2e = scale_log2e;
+    d.v_scale = 1.f;
+    if (fp8_scales != nullptr) {
+      d.scale_log2e = static_cast<float>(static_cast<double>(scale) * fp8_scales[0] *
+                                         1.4426950408889634);
+      d.v_scale = fp8_scales[1];
+    }
     d.items = reinterpret_cast<const pkv::DecodeItem*>(ws + L.decode_off);
     d.group = group;
     d.out = out;
@@ -515,7 +597,9 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
     d.part_l = part_l;
     d.part_acc = part_acc;
     const int pr = prof_begin(2, strm);
-    hipError_t e = pkv::launch_decode(d, L.n_decode, head_dim, group, dtype == PKV_BF16, strm);
+    hipError_t e = fp8_scales != nullptr
+                       ? pkv::launch_decode_fp8(d, L.n_decode, head_dim, group, strm)
+                       : pkv::launch_decode(d, L.n_decode, head_dim, group, dtype == PKV_BF16, strm);
     prof_end(pr, strm);
     if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("decode launch: ") + hipGetErrorString(e));
   }
@@ -539,7 +623,7 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
 int32_t workspace_size_impl(const int32_t* ctx_lens_host, const int32_t* cu_seqlens_q_host,
                             int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
                             int32_t head_dim, int32_t kv_split, int32_t dtype, uint32_t flags,
-                            int32_t n_write_rows, size_t* bytes) {
+                            int32_t n_write_rows, size_t* bytes, bool fp8 = false) {
   if (bytes == nullptr) return fail(PKV_ERR_INVALID, "workspace_size: bytes is NULL");
   *bytes = 0;
   if (n_write_rows < 0) return fail(PKV_ERR_INVALID, "workspace_size: n_rows must be >= 0");
@@ -552,6 +636,12 @@ int32_t workspace_size_impl(const int32_t* ctx_lens_host, const int32_t* cu_seql
   if (st != PKV_OK) return st;
   StepShape s = shape_for(ctx_lens_host, cu_seqlens_q_host, B, num_q_heads, num_kv_heads,
                           head_dim, kv_split, dtype, flags);
+  if (fp8) {
+    if (!pkv::decode_fp8_supported(head_dim, num_q_heads / num_kv_heads))
+      return fail(PKV_ERR_UNSUPPORTED, "attention_fp8: head_dim 64 or 128 and num_q_heads / "
+                                       "num_kv_heads one of 1, 2, 4");
+    s.prefill_on_mfma = false;
+  }
   *bytes = layout_for(s, num_q_heads, head_dim, n_write_rows).total;
   return ok();
 }
@@ -588,6 +678,8 @@ extern "C" int32_t pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* 
   if (n_pairs == 0) return ok();
   if (pairs_host == nullptr || k_cache == nullptr || v_cache == nullptr)
     return fail(PKV_ERR_INVALID, "copy_blocks: NULL pointer");
+  if (misaligned16(k_cache) || misaligned16(v_cache) || misaligned16(workspace))
+    return fail(PKV_ERR_INVALID, "copy_blocks: pools and workspace must be 16-byte aligned");
   if (static_cast<int64_t>(n_pairs) * (block_bytes / 16) > 0xffffffffLL)
     return fail(PKV_ERR_UNSUPPORTED, "copy_blocks: too many chunks in one call");
   const size_t need = align_up(sizeof(int32_t) * 2 * static_cast<size_t>(n_pairs));
@@ -692,6 +784,74 @@ extern "C" int32_t pkv_write_kv_attention(
                         cu_seqlens_q_host, B, T, num_q_heads, num_kv_heads, head_dim, block_size,
                         num_blocks, scale, kv_split, dtype, flags, out, workspace,
                         workspace_bytes, stream, &a, slots_host);
+}
+
+extern "C" int32_t pkv_write_kv_fp8(const void* k_new, const void* v_new,
+                                    const int32_t* slots_dev, int32_t n_rows, void* k_cache,
+                                    void* v_cache, int32_t num_blocks, int32_t block_size,
+                                    int32_t num_kv_heads, int32_t head_dim, float k_scale,
+                                    float v_scale, void* stream) {
+  pkv::WriteFp8Args a;
+  int32_t st = check_write_fp8(k_new, v_new, n_rows, k_cache, v_cache, num_blocks, block_size,
+                               num_kv_heads, head_dim, k_scale, v_scale, &a);
+  if (st != PKV_OK) return st;
+  if (n_rows == 0) return ok();
+  if (slots_dev == nullptr) return fail(PKV_ERR_INVALID, "write_kv_fp8: NULL pointer");
+  a.slots = slots_dev;
+  st = launch_write_fp8(a, static_cast<hipStream_t>(stream));
+  if (st != PKV_OK) return st;
+  return ok();
+}
+
+extern "C" int32_t pkv_attention_fp8_workspace_size(const int32_t* ctx_lens_host,
+                                                    const int32_t* cu_seqlens_q_host,
+                                                    int32_t B, int32_t num_q_heads,
+                                                    int32_t num_kv_heads, int32_t head_dim,
+                                                    int32_t kv_split, size_t* bytes) {
+  return workspace_size_impl(ctx_lens_host, cu_seqlens_q_host, B, num_q_heads, num_kv_heads,
+                             head_dim, kv_split, PKV_BF16, 0u, 0, bytes, true);
+}
+
+extern "C" int32_t pkv_attention_fp8(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* block_tables_dev, int32_t max_blocks,
+                                     const int32_t* ctx_lens_host,
+                                     const int32_t* cu_seqlens_q_host, int32_t B, int32_t T,
+                                     int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                     float scale, float k_scale, float v_scale,
+                                     int32_t kv_split, float* out, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  const float scales[2] = {k_scale, v_scale};
+  return attention_impl(q, k_cache, v_cache, block_tables_dev, max_blocks, ctx_lens_host,
+                        cu_seqlens_q_host, B, T, num_q_heads, num_kv_heads, head_dim, block_size,
+                        num_blocks, scale, kv_split, PKV_BF16, 0u, out, workspace,
+                        workspace_bytes, stream, nullptr, nullptr, scales);
+}
+
+extern "C" int32_t pkv_write_kv_attention_fp8_workspace_size(
+    const int32_t* ctx_lens_host, const int32_t* cu_seqlens_q_host, int32_t B,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t kv_split,
+    int32_t n_rows, size_t* bytes) {
+  return workspace_size_impl(ctx_lens_host, cu_seqlens_q_host, B, num_q_heads, num_kv_heads,
+                             head_dim, kv_split, PKV_BF16, 0u, n_rows, bytes, true);
+}
+
+extern "C" int32_t pkv_write_kv_attention_fp8(
+    const void* q, const void* k_new, const void* v_new, const int32_t* slots_host,
+    int32_t n_rows, void* k_cache, void* v_cache, const int32_t* block_tables_dev,
+    int32_t max_blocks, const int32_t* ctx_lens_host, const int32_t* cu_seqlens_q_host,
+    int32_t B, int32_t T, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t num_blocks, float scale, float k_scale, float v_scale,
+    int32_t kv_split, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  pkv::WriteFp8Args a;
+  int32_t st = check_write_fp8(k_new, v_new, n_rows, k_cache, v_cache, num_blocks, block_size,
+                               num_kv_heads, head_dim, k_scale, v_scale, &a);
+  if (st != PKV_OK) return st;
+  const float scales[2] = {k_scale, v_scale};
+  return attention_impl(q, k_cache, v_cache, block_tables_dev, max_blocks, ctx_lens_host,
+                        cu_seqlens_q_host, B, T, num_q_heads, num_kv_heads, head_dim, block_size,
+                        num_blocks, scale, kv_split, PKV_BF16, 0u, out, workspace,
+                        workspace_bytes, stream, nullptr, slots_host, scales, &a);
 }
 
 extern "C" int32_t pkv_profile_set_kinds(uint32_t kinds) {

@@ -43,11 +43,26 @@ struct DecodeArgs {
   int32_t group;      // hq / hkv
   int32_t kv_split;
   float scale_log2e;  // softmax scale times log2(e): scores live in the base-2 domain
+                      // (E4M3 pools: times the K scale as well)
+  float v_scale;      // E4M3 pools: the V scale (1 otherwise)
   const DecodeItem* items;
   float* out;
   float* part_m;
   float* part_l;
   float* part_acc;
+};
+
+struct WriteFp8Args {
+  const void* k_new;       // bfloat16 [n_rows, Hkv, D]
+  const void* v_new;
+  const int32_t* slots;
+  int32_t n_rows;
+  int32_t chunks_per_row;  // num_kv_heads * head_dim / 16 (16-byte chunks of a pool row)
+  int64_t n_slots;
+  float k_inv_scale;       // float32(1 / k_scale)
+  float v_inv_scale;
+  void* k_cache;           // E4M3 codes [NB, BS, Hkv, D]
+  void* v_cache;
 };
 
 struct MergeArgs {
@@ -81,6 +96,9 @@ struct PrefillArgs {
 // Each launcher enqueues one kernel on `stream` and returns hipSuccess or the launch error.
 hipError_t launch_write_kv(const WriteArgs& a, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
+hipError_t launch_write_kv_fp8(const WriteFp8Args& a, hipStream_t stream);
+hipError_t launch_decode_fp8(const DecodeArgs& a, int64_t n_items, int head_dim, int group,
+                             hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int64_t n_items, int head_dim, int group,
                          bool bf16, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int64_t n_items, int head_dim, hipStream_t stream);
@@ -89,6 +107,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int64_t n_items, int head_dim, i
 
 // Whether a (head_dim, group, dtype) combination has a built decode / prefill kernel.
 bool decode_supported(int head_dim, int group);
+bool decode_fp8_supported(int head_dim, int group);
 bool prefill_supported(int head_dim, int group, bool bf16);
 
 }  // namespace pkv

@@ -45,6 +45,55 @@ hipError_t launch_write_kv(const WriteArgs& a, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------------------
+// KV append into E4M3 pools: each bfloat16 element x of a new row is stored as the E4M3 code
+// of float32(x * inv_scale) (one float32 multiply), clamped to +-448 before the hardware
+// conversion (round to nearest, ties to even), so magnitudes beyond the E4M3 range saturate.
+// A thread writes 16 codes (one 16-byte chunk of a pool row) from 32 bytes of the new row.
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t quant4(uint32_t b01, uint32_t b23, float inv) {
+  const float x0 = fminf(fmaxf(__uint_as_float(b01 << 16) * inv, -448.f), 448.f);
+  const float x1 = fminf(fmaxf(__uint_as_float(b01 & 0xffff0000u) * inv, -448.f), 448.f);
+  const float x2 = fminf(fmaxf(__uint_as_float(b23 << 16) * inv, -448.f), 448.f);
+  const float x3 = fminf(fmaxf(__uint_as_float(b23 & 0xffff0000u) * inv, -448.f), 448.f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
+  return static_cast<uint32_t>(w);
+}
+
+__device__ __forceinline__ uint4 quant16(uint4 lo, uint4 hi, float inv) {
+  return make_uint4(quant4(lo.x, lo.y, inv), quant4(lo.z, lo.w, inv), quant4(hi.x, hi.y, inv),
+                    quant4(hi.z, hi.w, inv));
+}
+
+__global__ void __launch_bounds__(256) write_kv_fp8_kernel(WriteFp8Args a) {
+  const uint4* __restrict__ kn = static_cast<const uint4*>(a.k_new);
+  const uint4* __restrict__ vn = static_cast<const uint4*>(a.v_new);
+  uint4* __restrict__ kc = static_cast<uint4*>(a.k_cache);
+  uint4* __restrict__ vc = static_cast<uint4*>(a.v_cache);
+  const uint32_t chunks = static_cast<uint32_t>(a.chunks_per_row);
+  const uint32_t total = static_cast<uint32_t>(a.n_rows) * chunks;
+  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < total; i += gridDim.x * 256u) {
+    const uint32_t row = i / chunks;
+    const uint32_t c = i - row * chunks;
+    const int32_t s = a.slots[row];
+    if (s < 0 || s >= a.n_slots) continue;
+    const int64_t dst = static_cast<int64_t>(s) * chunks + c;
+    kc[dst] = quant16(kn[2 * i], kn[2 * i + 1], a.k_inv_scale);
+    vc[dst] = quant16(vn[2 * i], vn[2 * i + 1], a.v_inv_scale);
+  }
+}
+
+hipError_t launch_write_kv_fp8(const WriteFp8Args& a, hipStream_t stream) {
+  const int64_t total = static_cast<int64_t>(a.n_rows) * a.chunks_per_row;
+  if (total == 0) return hipSuccess;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(write_kv_fp8_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
 // Block copy (copy-on-write): block pairs[2i + 1] of both pools becomes a byte copy of block
 // pairs[2i]. A block is chunks_per_block contiguous 16-byte chunks in either pool.
 // ---------------------------------------------------------------------------------------

@@ -6,7 +6,9 @@ allocated pool is freed in the workload's seeded order so that the LIFO list hol
 permutation (non-contiguous block tables), sequences are admitted in order (a group member
 adopts its leader's full prompt blocks with an incref), each sequence's prior context is
 written with pkv_write_kv through pkv_slot_mapping slots, and the step's new rows are written
-the same way before attention. Pools start filled with NaN so that a stray read shows.
+the same way before attention. Pools start filled with NaN (the E4M3 NaN code for FP8 pools)
+so that a stray read shows. FP8 pools are written with pkv_write_kv_fp8 and read with
+pkv_attention_fp8, with the workload's per-tensor scales.
 
 Every method step here is a library call; torch only allocates device memory.
 """
@@ -51,9 +53,8 @@ class GpuStep:
     workspace: object = None
 
     def write_new(self, stream=None):
-        w = self.workload
-        L.write_kv(self.k_new, self.v_new, self.new_slots_dev, self.k_cache, self.v_cache,
-                   stream=stream)
+        _write(self.workload, self.k_new, self.v_new, self.new_slots_dev, self.k_cache,
+               self.v_cache, stream)
 
     def attention(self, kv_split: Optional[int] = None, stream=None,
                   phase_consistent: bool = False):
@@ -63,6 +64,18 @@ class GpuStep:
         if self.out is None:
             self.out = torch.empty((w.T, w.spec.Hq, w.spec.D), dtype=torch.float32,
                                    device=self.q.device)
+        if w.kv_fp8:
+            if phase_consistent:
+                raise ValueError("E4M3 pools have no phase-consistent tile path")
+            need = L.attention_fp8_workspace_size(w.ctx_lens, w.cu_seqlens_q, w.spec.Hq,
+                                                  w.spec.Hkv, w.spec.D, split)
+            if self.workspace is None or self.workspace.numel() < need:
+                self.workspace = torch.empty(max(need, 1), dtype=torch.uint8,
+                                             device=self.q.device)
+            return L.attention_fp8(self.q, self.k_cache, self.v_cache, self.block_tables_dev,
+                                   w.ctx_lens, w.cu_seqlens_q, w.scale, w.spec.k_scale,
+                                   w.spec.v_scale, out=self.out, workspace=self.workspace,
+                                   kv_split=split, stream=stream)
         need = L.attention_workspace_size(w.ctx_lens, w.cu_seqlens_q, w.spec.Hq, w.spec.Hkv,
                                           w.spec.D, split,
                                           L.PKV_BF16 if w.spec.dtype == "bf16" else L.PKV_F32,
@@ -77,10 +90,28 @@ class GpuStep:
 
     def fused_step(self, kv_split: Optional[int] = None, stream=None,
                    phase_consistent: bool = False):
-        """The step's KV append and attention in one pkv_write_kv_attention call."""
+        """The step's KV append and attention in one pkv_write_kv_attention call
+        (pkv_write_kv_attention_fp8 for E4M3 pools)."""
         import torch
         w = self.workload
         split = w.spec.kv_split if kv_split is None else kv_split
+        if w.kv_fp8:
+            if phase_consistent:
+                raise ValueError("E4M3 pools have no phase-consistent tile path")
+            if self.out is None:
+                self.out = torch.empty((w.T, w.spec.Hq, w.spec.D), dtype=torch.float32,
+                                       device=self.q.device)
+            need = L.write_kv_attention_fp8_workspace_size(w.ctx_lens, w.cu_seqlens_q, w.spec.Hq,
+                                                           w.spec.Hkv, w.spec.D, w.T, split)
+            if self.workspace is None or self.workspace.numel() < need:
+                self.workspace = torch.empty(max(need, 1), dtype=torch.uint8,
+                                             device=self.q.device)
+            return L.write_kv_attention_fp8(self.q, self.k_new, self.v_new, self.new_slots,
+                                            self.k_cache, self.v_cache, self.block_tables_dev,
+                                            w.ctx_lens, w.cu_seqlens_q, w.scale, w.spec.k_scale,
+                                            w.spec.v_scale, out=self.out,
+                                            workspace=self.workspace, kv_split=split,
+                                            stream=stream)
         if self.out is None:
             self.out = torch.empty((w.T, w.spec.Hq, w.spec.D), dtype=torch.float32,
                                    device=self.q.device)
@@ -96,6 +127,14 @@ class GpuStep:
                                     phase_consistent=phase_consistent)
 
 
+def _write(w, k_rows, v_rows, slots, k_cache, v_cache, stream=None):
+    if w.kv_fp8:
+        L.write_kv_fp8(k_rows, v_rows, slots, k_cache, v_cache, w.spec.k_scale, w.spec.v_scale,
+                       stream=stream)
+    else:
+        L.write_kv(k_rows, v_rows, slots, k_cache, v_cache, stream=stream)
+
+
 def build_gpu_step(w, device="cuda", write_new: bool = True, workers: int = 8) -> GpuStep:
     import torch
     s = w.spec
@@ -106,8 +145,12 @@ def build_gpu_step(w, device="cuda", write_new: bool = True, workers: int = 8) -
     alloc.free(w.free_order.tolist())
 
     dt = torch_dtype(w)
-    k_cache = torch.full((NB, BS, s.Hkv, s.D), float("nan"), dtype=dt, device=device)
-    v_cache = torch.full((NB, BS, s.Hkv, s.D), float("nan"), dtype=dt, device=device)
+    if w.kv_fp8:
+        k_cache = torch.full((NB, BS, s.Hkv, s.D), 0x7F, dtype=torch.uint8, device=device)
+        v_cache = torch.full((NB, BS, s.Hkv, s.D), 0x7F, dtype=torch.uint8, device=device)
+    else:
+        k_cache = torch.full((NB, BS, s.Hkv, s.D), float("nan"), dtype=dt, device=device)
+        v_cache = torch.full((NB, BS, s.Hkv, s.D), float("nan"), dtype=dt, device=device)
     tables = np.full((B, w.max_blocks), -1, dtype=np.int32)
 
     # admissions in order; each sequence writes its prior context right after its admission,
@@ -131,8 +174,8 @@ def build_gpu_step(w, device="cuda", write_new: bool = True, workers: int = 8) -
         vd = to_device(vv, device)
         if prior > start:
             sl = alloc.slots(tables[b], start, prior - start, BS)
-            L.write_kv(kd[start:prior].contiguous(), vd[start:prior].contiguous(), sl, k_cache,
-                       v_cache)
+            _write(w, kd[start:prior].contiguous(), vd[start:prior].contiguous(), sl, k_cache,
+                   v_cache)
         del kd, vd
         lo, hi = int(w.cu_seqlens_q[b]), int(w.cu_seqlens_q[b + 1])
         if hi > lo:

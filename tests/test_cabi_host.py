@@ -16,6 +16,9 @@ import oracle
 
 pytestmark = []
 
+# a fake device address, 256-byte aligned: validation never dereferences it
+F = 0x1000
+
 
 def test_library_exports_every_header_function():
     lib = pkv.lib()
@@ -157,8 +160,8 @@ def test_validate_slots():
 def _attn(**kw):
     """Raw pkv_attention call with fake device pointers: only validation may run."""
     lib = pkv.lib()
-    a = dict(q=1, k=1, v=1, bt=1, mb=8, ctx=[5, 9], cu=[0, 1, 3], T=3, hq=8, hkv=2, d=128,
-             bs=16, nb=4, scale=0.1, split=512, dt=L.PKV_BF16, out=1, ws=1, wsb=1 << 30)
+    a = dict(q=F, k=F, v=F, bt=F, mb=8, ctx=[5, 9], cu=[0, 1, 3], T=3, hq=8, hkv=2, d=128,
+             bs=16, nb=4, scale=0.1, split=512, dt=L.PKV_BF16, out=F, ws=F, wsb=1 << 30)
     a.update(kw)
     ctx = np.asarray(a["ctx"], np.int32)
     cu = np.asarray(a["cu"], np.int32)
@@ -206,18 +209,18 @@ def test_workspace_size_counts_splits():
 
 def test_write_kv_validation():
     lib = pkv.lib()
-    assert lib.pkv_write_kv(1, 1, 1, 4, 1, 1, 4, 16, 2, 128, 9, None) == L.PKV_ERR_INVALID
-    assert lib.pkv_write_kv(1, 1, 1, -1, 1, 1, 4, 16, 2, 128, 1, None) == L.PKV_ERR_INVALID
-    assert lib.pkv_write_kv(0, 1, 1, 4, 1, 1, 4, 16, 2, 128, 1, None) == L.PKV_ERR_INVALID
-    assert lib.pkv_write_kv(1, 1, 1, 0, 1, 1, 4, 16, 2, 128, 1, None) == L.PKV_OK
-    assert lib.pkv_write_kv(1, 1, 1, 4, 1, 1, 4, 16, 1, 4, 1, None) == L.PKV_ERR_UNSUPPORTED
+    assert lib.pkv_write_kv(F, F, F, 4, F, F, 4, 16, 2, 128, 9, None) == L.PKV_ERR_INVALID
+    assert lib.pkv_write_kv(F, F, F, -1, F, F, 4, 16, 2, 128, 1, None) == L.PKV_ERR_INVALID
+    assert lib.pkv_write_kv(0, F, F, 4, F, F, 4, 16, 2, 128, 1, None) == L.PKV_ERR_INVALID
+    assert lib.pkv_write_kv(F, F, F, 0, F, F, 4, 16, 2, 128, 1, None) == L.PKV_OK
+    assert lib.pkv_write_kv(F, F, F, 4, F, F, 4, 16, 1, 4, 1, None) == L.PKV_ERR_UNSUPPORTED
 
 
 def _attn_ex(flags, **kw):
     """Raw pkv_attention_ex call with fake device pointers: only validation may run."""
     lib = pkv.lib()
-    a = dict(q=1, k=1, v=1, bt=1, mb=8, ctx=[5, 9], cu=[0, 1, 3], T=3, hq=8, hkv=2, d=128,
-             bs=16, nb=4, scale=0.1, split=512, dt=L.PKV_BF16, out=1, ws=1, wsb=16)
+    a = dict(q=F, k=F, v=F, bt=F, mb=8, ctx=[5, 9], cu=[0, 1, 3], T=3, hq=8, hkv=2, d=128,
+             bs=16, nb=4, scale=0.1, split=512, dt=L.PKV_BF16, out=F, ws=F, wsb=16)
     a.update(kw)
     ctx = np.asarray(a["ctx"], np.int32)
     cu = np.asarray(a["cu"], np.int32)
@@ -251,9 +254,9 @@ def test_phase_consistent_workspace_has_no_split_partials():
 def _fused(**kw):
     """Raw pkv_write_kv_attention call with fake device pointers: only validation may run."""
     lib = pkv.lib()
-    a = dict(q=1, kn=1, vn=1, slots=[3, -1, 60], n=3, k=1, v=1, bt=1, mb=8, ctx=[5, 9],
+    a = dict(q=F, kn=F, vn=F, slots=[3, -1, 60], n=3, k=F, v=F, bt=F, mb=8, ctx=[5, 9],
              cu=[0, 1, 3], T=3, hq=8, hkv=2, d=128, bs=16, nb=4, scale=0.1, split=512,
-             dt=L.PKV_BF16, flags=0, out=1, ws=1, wsb=1 << 30)
+             dt=L.PKV_BF16, flags=0, out=F, ws=F, wsb=1 << 30)
     a.update(kw)
     ctx = np.asarray(a["ctx"], np.int32)
     cu = np.asarray(a["cu"], np.int32)
@@ -304,12 +307,101 @@ def test_copy_blocks_validation():
     lib = pkv.lib()
     pairs = np.asarray([1, 2, 3, 4], np.int32)
     call = lambda pr, n=2, nb=8, dt=L.PKV_BF16, wsb=256: lib.pkv_copy_blocks(
-        1, 1, L._ptr(np.asarray(pr, np.int32)), n, nb, 16, 2, 128, dt, 1, wsb, None)
+        F, F, L._ptr(np.asarray(pr, np.int32)), n, nb, 16, 2, 128, dt, F, wsb, None)
     assert call([1, 2, 3, 8]) == L.PKV_ERR_INVALID          # id outside the pool
     assert call([1, 2, 3, 2]) == L.PKV_ERR_INVALID          # destination twice
     assert call([1, 2, 2, 4]) == L.PKV_ERR_INVALID          # destination is also a source
     assert call([1, 2, 3, 4], wsb=8) == L.PKV_ERR_INVALID   # workspace too small
     assert call([1, 2, 3, 4], dt=3) == L.PKV_ERR_INVALID
     assert call([1, 2], n=0) == L.PKV_OK                    # nothing to copy
-    assert lib.pkv_copy_blocks(1, 1, L._ptr(pairs), 1, 8, 1, 1, 4, L.PKV_BF16, 1, 256,
+    assert lib.pkv_copy_blocks(F, F, L._ptr(pairs), 1, 8, 1, 1, 4, L.PKV_BF16, F, 256,
                                None) == L.PKV_ERR_UNSUPPORTED   # 8-byte blocks
+
+
+def test_write_kv_fp8_validation():
+    lib = pkv.lib()
+    call = lambda n=4, hkv=2, d=128, ks=0.5, vs=0.5, k=F: lib.pkv_write_kv_fp8(
+        k, F, F, n, F, F, 4, 16, hkv, d, ks, vs, None)
+    assert call(n=0) == L.PKV_OK                               # nothing to write
+    assert call(n=-1) == L.PKV_ERR_INVALID
+    assert call(k=0) == L.PKV_ERR_INVALID                      # NULL k_new
+    assert call(ks=0.0) == L.PKV_ERR_INVALID
+    assert call(vs=-1.0) == L.PKV_ERR_INVALID
+    assert call(ks=float("inf")) == L.PKV_ERR_INVALID
+    assert call(vs=float("nan")) == L.PKV_ERR_INVALID
+    assert call(hkv=1, d=8) == L.PKV_ERR_UNSUPPORTED           # 8-byte pool rows
+    assert pkv.lib().pkv_last_error() != b""
+
+
+def _attn_fp8(**kw):
+    """Raw pkv_attention_fp8 call with fake device pointers: only validation may run."""
+    lib = pkv.lib()
+    a = dict(q=F, k=F, v=F, bt=F, mb=8, ctx=[5, 9], cu=[0, 1, 3], T=3, hq=8, hkv=2, d=128,
+             bs=16, nb=4, scale=0.1, ks=0.5, vs=0.5, split=512, out=F, ws=F, wsb=16)
+    a.update(kw)
+    ctx = np.asarray(a["ctx"], np.int32)
+    cu = np.asarray(a["cu"], np.int32)
+    return lib.pkv_attention_fp8(a["q"], a["k"], a["v"], a["bt"], a["mb"], L._ptr(ctx),
+                                 L._ptr(cu), ctx.size, a["T"], a["hq"], a["hkv"], a["d"],
+                                 a["bs"], a["nb"], a["scale"], a["ks"], a["vs"], a["split"],
+                                 a["out"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hq=16, hkv=2), L.PKV_ERR_UNSUPPORTED),            # group 8 has no E4M3 instance
+    (dict(d=96), L.PKV_ERR_UNSUPPORTED),
+    (dict(ks=0.0), L.PKV_ERR_INVALID),
+    (dict(vs=float("nan")), L.PKV_ERR_INVALID),
+    (dict(ks=float("inf")), L.PKV_ERR_INVALID),
+    (dict(split=100), L.PKV_ERR_INVALID),
+    (dict(ctx=[5, 1]), L.PKV_ERR_INVALID),                  # q_len > ctx
+])
+def test_attention_fp8_validation_refuses_before_any_launch(kw, status):
+    assert _attn_fp8(**kw) == status
+    assert pkv.lib().pkv_last_error() != b""
+
+
+def test_attention_fp8_reaches_the_workspace_check_and_sizes_all_rows_as_decode():
+    assert _attn_fp8() == L.PKV_ERR_INVALID                 # 16-byte workspace
+    assert b"workspace" in pkv.lib().pkv_last_error()
+    assert _attn_fp8(ctx=[], cu=[0], T=0) == L.PKV_OK
+    # a 300-row prefill chunk: split partials per row on the E4M3 path, none on the tile path
+    f8 = pkv.attention_fp8_workspace_size([2000], [0, 300], 8, 2, 128, 512)
+    bf = pkv.attention_workspace_size([2000], [0, 300], 8, 2, 128, 512)
+    assert f8 > bf
+    with pytest.raises(pkv.Unsupported):
+        pkv.attention_fp8_workspace_size([5], [0, 1], 16, 2, 128, 512)
+
+
+def test_misaligned_device_pointers_are_refused():
+    assert _attn(q=F + 2) == L.PKV_ERR_INVALID
+    assert b"aligned" in pkv.lib().pkv_last_error()
+    assert _attn(ws=F + 8) == L.PKV_ERR_INVALID
+    assert _attn(out=F + 2) == L.PKV_ERR_INVALID
+    lib = pkv.lib()
+    assert lib.pkv_write_kv(F + 4, F, F, 4, F, F, 4, 16, 2, 128, 1, None) == L.PKV_ERR_INVALID
+    assert b"aligned" in pkv.lib().pkv_last_error()
+    assert lib.pkv_write_kv_fp8(F, F, F, 4, F + 8, F, 4, 16, 2, 128, 0.5, 0.5,
+                                None) == L.PKV_ERR_INVALID
+    assert b"aligned" in pkv.lib().pkv_last_error()
+
+
+def test_fused_fp8_step_validation():
+    lib = pkv.lib()
+    ctx = np.asarray([5, 9], np.int32)
+    cu = np.asarray([0, 1, 3], np.int32)
+
+    def call(slots=(3, -1, 60), ks=0.5, hq=8, wsb=1 << 30):
+        sl = np.asarray(slots, np.int32)
+        return lib.pkv_write_kv_attention_fp8(F, F, F, L._ptr(sl), sl.size, F, F, F, 8,
+                                              L._ptr(ctx), L._ptr(cu), 2, 3, hq, 2, 128, 16, 4,
+                                              0.1, ks, 0.5, 512, F, F, wsb, None)
+    assert call(slots=(3, -1, 64)) == L.PKV_ERR_INVALID       # slot outside the pool
+    assert b"outside" in pkv.lib().pkv_last_error()
+    assert call(ks=-1.0) == L.PKV_ERR_INVALID
+    assert call(hq=16) == L.PKV_ERR_UNSUPPORTED
+    assert call(wsb=16) == L.PKV_ERR_INVALID
+    assert b"workspace" in pkv.lib().pkv_last_error()
+    a = pkv.attention_fp8_workspace_size([5, 9], [0, 1, 3], 8, 2, 128, 512)
+    b = pkv.write_kv_attention_fp8_workspace_size([5, 9], [0, 1, 3], 8, 2, 128, 1000, 512)
+    assert b >= a + 4 * 1000

@@ -1,0 +1,200 @@
+"""GPU parity of the FP8 (OCP E4M3) pools with per-tensor scales, through the C ABI.
+
+Bars: every stored code bit-exact against the oracle's encoder (all finite bfloat16 inputs,
+several scales); attention within max abs error 2e-3 of the float64 oracle over the
+dequantised pools; a sequence's rows bitwise identical alone and inside the batch, and run to
+run; a bad block id gives NaN rows, never a fault.
+"""
+import numpy as np
+import pytest
+
+import prefill_slot_mapping_amd as pkv
+from oracle import build_oracle_step
+from oracle.fp8 import quantize_rows
+from workloads import FP8_CONFIGS, FP8_SMALL_CONFIGS, explicit_spec, make_workload
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+DEV = "cuda:0"
+
+
+def _harness():
+    from prefill_slot_mapping_amd.harness import build_gpu_step
+    return build_gpu_step
+
+
+def _codes(t):
+    return t.detach().cpu().numpy()
+
+
+def _finite_bf16_bits():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    exp = (bits >> 7) & 0xFF
+    return bits[exp != 0xFF]                       # drop infinities and NaNs
+
+
+@pytest.mark.parametrize("scale", [1.0, 1 / 64, 0.015, 3.0])
+def test_write_codes_bit_exact_over_all_finite_bf16(scale):
+    """Every finite bfloat16 value, times float32(1 / scale), rounded to E4M3 (saturating)."""
+    bits = _finite_bf16_bits()
+    hkv, d = 2, 64
+    row = hkv * d
+    n = (bits.size + row - 1) // row
+    pad = np.zeros(n * row, dtype=np.uint16)
+    pad[:bits.size] = bits
+    vals = pad.reshape(n, hkv, d)
+    rev = np.ascontiguousarray(vals[::-1])            # V gets the values in another order
+    print(f"[fp8-write] scale={scale} rows={n}", flush=True)
+    kn = torch.from_numpy(vals.view(np.int16)).to(DEV).view(torch.bfloat16)
+    vn = torch.from_numpy(rev.view(np.int16)).to(DEV).view(torch.bfloat16)
+    bs = 16
+    nb = (n + bs - 1) // bs + 1
+    kc = torch.full((nb, bs, hkv, d), 0x7F, dtype=torch.uint8, device=DEV)
+    vc = torch.full_like(kc, 0x7F)
+    slots = np.random.default_rng(5).permutation(nb * bs)[:n].astype(np.int32)
+    pkv.write_kv_fp8(kn, vn, slots, kc, vc, scale, scale)
+    torch.cuda.synchronize()
+    f32 = (pad.astype(np.uint32) << 16).view(np.float32).reshape(n, hkv, d)
+    want_k = quantize_rows(f32, scale)
+    want_v = quantize_rows(np.ascontiguousarray(f32[::-1]), scale)
+    got_k = _codes(kc).reshape(nb * bs, hkv, d)[slots]
+    got_v = _codes(vc).reshape(nb * bs, hkv, d)[slots]
+    bad = np.flatnonzero(got_k.reshape(-1) != want_k.reshape(-1))
+    assert bad.size == 0, (f"{bad.size} codes differ, first input bits "
+                           f"{pad[bad[:4]]} got {got_k.reshape(-1)[bad[:4]]} "
+                           f"want {want_k.reshape(-1)[bad[:4]]}")
+    assert np.array_equal(got_v, want_v)
+    # slots never named stay untouched
+    untouched = np.setdiff1d(np.arange(nb * bs), slots)
+    assert (_codes(kc).reshape(nb * bs, -1)[untouched] == 0x7F).all()
+
+
+def test_write_fp8_skips_negative_and_out_of_range_slots():
+    nb, bs, hkv, d = 4, 16, 2, 64
+    kc = torch.zeros((nb, bs, hkv, d), dtype=torch.uint8, device=DEV)
+    vc = torch.zeros_like(kc)
+    kn = torch.randn((3, hkv, d), device=DEV).to(torch.bfloat16)
+    vn = torch.randn((3, hkv, d), device=DEV).to(torch.bfloat16)
+    slots = torch.tensor([5, -1, nb * bs + 3], dtype=torch.int32, device=DEV)
+    pkv.write_kv_fp8(kn, vn, slots, kc, vc, 0.5, 0.25)
+    torch.cuda.synchronize()
+    flat = _codes(kc).reshape(nb * bs, hkv, d)
+    f32 = kn[0].float().cpu().numpy()
+    assert np.array_equal(flat[5], quantize_rows(f32, 0.5))
+    assert int((flat.reshape(nb * bs, -1) != 0).any(axis=1).sum()) == 1
+
+
+def check_step(w, rows=None, seqs=None):
+    print(f"[fp8-parity] {w.spec.name} B={w.B} T={w.T} NB={w.num_blocks}", flush=True)
+    gst = _harness()(w, device=DEV)
+    ost = build_oracle_step(w, seqs=seqs, poison=seqs is None)
+    assert np.array_equal(gst.block_tables, ost.block_tables)
+    assert np.array_equal(gst.new_slots, ost.new_slots)
+    got = gst.attention()
+    torch.cuda.synchronize()
+    got = got.cpu().numpy().astype(np.float64)
+    ref = ost.attention(rows)
+    sel = np.arange(w.T) if rows is None else np.asarray(sorted(rows))
+    assert np.isfinite(got[sel]).all()
+    err = float(np.abs(got[sel] - ref[sel]).max()) if sel.size else 0.0
+    print(f"[fp8-parity] {w.spec.name} max abs err {err:.3e}", flush=True)
+    assert err <= TOL
+    return gst, ost, got
+
+
+@pytest.mark.parametrize("name", list(FP8_SMALL_CONFIGS))
+def test_small_fp8_configs_match_oracle_and_codes_are_bit_exact(name):
+    w = make_workload(FP8_SMALL_CONFIGS[name])
+    gst, ost, _ = check_step(w)
+    assert np.array_equal(_codes(gst.k_cache), ost.k_pool)
+    assert np.array_equal(_codes(gst.v_cache), ost.v_pool)
+
+
+EDGE = [
+    # (Hq, Hkv, D, BS, sequences (ctx, q_len)[, spec keywords]); every kernel instance
+    (8, 8, 128, 16, [(1, 1), (2, 2), (16, 1), (17, 17), (513, 1), (1025, 1), (700, 130)]),
+    (8, 4, 128, 5, [(7, 1), (129, 1), (642, 1), (88, 20)]),
+    (16, 4, 128, 16, [(1, 1), (64, 1), (65, 1), (3000, 1), (90, 31)], {"kv_split": 64}),
+    (4, 4, 64, 1, [(1, 1), (5, 5), (300, 1), (70, 3)]),
+    (16, 8, 64, 32, [(3, 1), (100, 100), (1300, 1), (97, 33)]),
+    (16, 4, 64, 64, [(128, 1), (129, 2), (1, 1), (4097, 1)], {"kv_split": 2048}),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[f"G{c[0] // c[1]}-D{c[2]}-BS{c[3]}"
+                                            + (f"-split{c[5]['kv_split']}" if len(c) > 5 else "")
+                                            for c in EDGE])
+def test_fp8_edge_cases_match_oracle(case):
+    hq, hkv, d, bs, seqs = case[:5]
+    kw = case[5] if len(case) > 5 else {}
+    w = make_workload(explicit_spec(f"edge-fp8-{hq}-{hkv}-{d}-{bs}", "bf16", hq, hkv, d, bs, seqs,
+                                    kv_dtype="fp8", k_scale=1 / 32, v_scale=1 / 48, **kw))
+    check_step(w)
+
+
+def test_fp8_alone_equals_batched_bitwise_and_run_to_run():
+    w = make_workload(FP8_SMALL_CONFIGS["mixed-fp8-step"])
+    gst = _harness()(w, device=DEV)
+    batched = gst.attention().cpu().numpy().copy()
+    s = w.spec
+    for b in range(w.B):
+        lo, hi = int(w.cu_seqlens_q[b]), int(w.cu_seqlens_q[b + 1])
+        if hi == lo:
+            continue
+        out = pkv.attention_fp8(gst.q[lo:hi].contiguous(), gst.k_cache, gst.v_cache,
+                                gst.block_tables_dev[b:b + 1].contiguous(),
+                                [int(w.ctx_lens[b])], [0, hi - lo], w.scale, s.k_scale,
+                                s.v_scale, kv_split=s.kv_split)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), batched[lo:hi]), f"sequence {b}"
+    for _ in range(2):
+        assert np.array_equal(gst.attention().cpu().numpy(), batched)
+
+
+def test_fp8_out_of_range_block_id_gives_nan_not_a_fault():
+    w = make_workload(explicit_spec("badblock-fp8", "bf16", 8, 2, 128, 16, [(40, 1), (40, 1)],
+                                    kv_dtype="fp8", k_scale=0.05, v_scale=0.05))
+    gst = _harness()(w, device=DEV)
+    good = gst.attention().cpu().numpy().copy()
+    t = gst.block_tables.copy()
+    t[0, 1] = w.num_blocks + 1000
+    out = pkv.attention_fp8(gst.q, gst.k_cache, gst.v_cache, torch.from_numpy(t).to(DEV),
+                            w.ctx_lens, w.cu_seqlens_q, w.scale, w.spec.k_scale, w.spec.v_scale)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.isnan(o[0]).all()
+    assert np.array_equal(o[1], good[1])
+
+
+@pytest.mark.parametrize("name", list(FP8_CONFIGS))
+def test_full_size_fp8_configs_on_sampled_rows(name):
+    w = make_workload(FP8_CONFIGS[name])
+    rng = np.random.default_rng(13)
+    dec = [b for b in range(w.B) if w.q_lens[b] == 1]
+    pre = [b for b in range(w.B) if w.q_lens[b] > 1]
+    seqs = sorted(set(rng.choice(dec, size=min(4, len(dec)), replace=False).tolist()))
+    seqs.append(int(np.argmax(w.ctx_lens)))
+    if pre:
+        seqs += rng.choice(pre, size=2, replace=False).tolist()
+    seqs = sorted(set(seqs))
+    rows = []
+    for b in seqs:
+        lo, hi = int(w.cu_seqlens_q[b]), int(w.cu_seqlens_q[b + 1])
+        rows += sorted(set([lo, hi - 1, (lo + hi) // 2] +
+                           rng.integers(lo, hi, size=min(3, hi - lo)).tolist()))
+    check_step(w, rows=rows, seqs=seqs)
+
+
+def test_fused_fp8_step_equals_separate_calls_bitwise():
+    w = make_workload(FP8_SMALL_CONFIGS["mixed-fp8-step"])
+    a = _harness()(w, device=DEV, write_new=False)
+    b = _harness()(w, device=DEV, write_new=False)
+    fused = a.fused_step().cpu().numpy().copy()
+    b.write_new()
+    sep = b.attention().cpu().numpy()
+    torch.cuda.synchronize()
+    assert np.array_equal(_codes(a.k_cache), _codes(b.k_cache))
+    assert np.array_equal(_codes(a.v_cache), _codes(b.v_cache))
+    assert np.array_equal(fused, sep)
