@@ -261,21 +261,36 @@ def cpu_baseline(w, budget_s):
             "affinity_cores": len(os.sched_getaffinity(0))}
 
 
-def _traffic_for(kernel_file, workload):
-    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, each scaled by what the counter reads for a
-    plain copy of known size) from the committed rocprofv3 PMC summary, or None when the kernel
-    source has changed since the counters were taken."""
+def _traffic_for(workload):
+    """HBM bytes per launch of the workload's decode kernel (FETCH_SIZE + WRITE_SIZE, each
+    scaled by what the counter reads for a plain copy of known size) from the committed
+    rocprofv3 PMC summary, or None when that kernel's source has changed since the counters
+    were taken."""
     path = os.path.join(ROOT, "profiles", "decode_traffic.json")
     if not os.path.exists(path):
         return None
     try:
         rec = json.load(open(path))
-        src = open(os.path.join(ROOT, "prefill_slot_mapping_amd", "csrc", kernel_file), "rb").read()
-        if rec.get("kernel_sha256") != hashlib.sha256(src).hexdigest():
+        ent = rec[workload]
+        src_path = ent.get("kernel_source", rec["kernel_source"])
+        sha = ent.get("kernel_sha256", rec["kernel_sha256"])
+        src = open(os.path.join(ROOT, src_path), "rb").read()
+        if sha != hashlib.sha256(src).hexdigest():
             return None
-        return rec[workload]["hbm_bytes"]
+        return ent["hbm_bytes"]
     except (OSError, KeyError, ValueError):
         return None
+
+
+def _decode_roofline(res, name, kernel):
+    """Roofline object of a result's decode kernel: algorithmic KV bytes / its average launch."""
+    tr = res["timed_region_kernel"]
+    ms = tr.get("avg_ms") if tr.get("kernel") == "decode" else res["kernels_ms"]["decode"]
+    achieved = res["decode_kv_bytes"] / (ms * 1e-3) / 1e9 if ms else None
+    return {"bound": "hbm", "kernel": kernel, "achieved": achieved, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS if achieved else None,
+            "traffic": _traffic_for(name), "bytes_per_launch": res["decode_kv_bytes"],
+            "avg_launch_ms": ms}
 
 
 def main():
@@ -301,6 +316,9 @@ def main():
     extra = {}
     for name in [n for n in args.extra.split(",") if n and n != args.workload]:
         r = time_workload(name, args.steps, args.warmup, kernel_events=args.kernel_events)
+        if r["decode_kv_bytes"] and not (r["_w"].q_lens > 1).any():
+            r["roofline"] = _decode_roofline(r, name, "decode_fp8_kernel" if r["_w"].kv_fp8
+                                             else "decode_split_kernel")
         r.pop("_gst"); r.pop("_w")
         extra[name] = r
         torch.cuda.empty_cache()
@@ -312,14 +330,8 @@ def main():
         extra[name + "/phase-consistent"] = r
         torch.cuda.empty_cache()
 
-    tr = main_res["timed_region_kernel"]
-    dec_ms = tr.get("avg_ms") if tr.get("kernel") == "decode" else main_res["kernels_ms"]["decode"]
-    achieved = main_res["decode_kv_bytes"] / (dec_ms * 1e-3) / 1e9 if dec_ms else None
-    roofline = {"bound": "hbm", "kernel": "decode_split_kernel", "achieved": achieved,
-                "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS if achieved else None,
-                "traffic": _traffic_for("decode.hip", args.workload),
-                "bytes_per_launch": main_res["decode_kv_bytes"], "avg_launch_ms": dec_ms}
+    roofline = _decode_roofline(main_res, args.workload,
+                                "decode_fp8_kernel" if w.kv_fp8 else "decode_split_kernel")
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_seconds)
@@ -330,9 +342,9 @@ def main():
         "metric": "paged decode KV GB/s (% HBM peak); mixed ragged step tokens/s",
         "value": main_res["step_gbs"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": main_res["ms_per_step"], "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": s.dtype, "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": ("e4m3 KV, bf16 q" if w.kv_fp8 else s.dtype), "data": "synthetic",
         "config": {"workload": args.workload, "B": w.B, "Hq": s.Hq, "Hkv": s.Hkv, "D": s.D,
-                   "block_size": s.BS, "kv_split": s.kv_split,
+                   "block_size": s.BS, "kv_split": s.kv_split, "kv_dtype": s.kv_dtype or s.dtype,
                    "cached_tokens": int(w.ctx_lens.sum()), "parallelism": "single-gpu"},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -83,7 +83,10 @@ decode_split_kernel(DecodeArgs a) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int f = xcd_remap(blockIdx.x, gridDim.x);
+  // Items in grid order: the host lists them longest first and the hardware deals consecutive
+  // workgroups to the 8 XCDs in turn, so every XCD gets its share of full and short splits
+  // (contiguous per-XCD ranges of that list would leave the XCD holding the short ones idle).
+  const int f = blockIdx.x;
   const int item_idx = f / a.hkv;
   const int g = f - item_idx * a.hkv;        // the kv head of this work item
   const int hq0 = g * G;                     // its first query head
@@ -409,7 +412,7 @@ decode_pair_kernel(DecodeArgs a) {
   const int lane = tid & 63;
   const int pair = wave >> 1;
   const int half = wave & 1;                 // 0: loads K, 1: loads V; heads half*4 .. +3
-  const int f = xcd_remap(blockIdx.x, gridDim.x);
+  const int f = blockIdx.x;                  // grid order, as decode_split_kernel
   const int item_idx = f / a.hkv;
   const int g = f - item_idx * a.hkv;
   const int hq0 = g * G;

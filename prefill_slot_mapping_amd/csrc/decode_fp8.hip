@@ -53,9 +53,11 @@ __device__ __forceinline__ uint2 load_nt8(const uint2* p) {
 // Workgroup = 4 waves = one (query row, split, kv head) item serving the G query heads of the
 // kv head. K rows (D bytes) are loaded 16 bytes per lane (LPTK lanes per row) and staged in
 // LDS for the score stage (SPL lanes per key); V rows are loaded 8 bytes per lane (LPTV lanes
-// per row), so that P.V keeps 8 accumulators per head per lane.
+// per row), so that P.V keeps 8 accumulators per head per lane. A tile carries half the bytes
+// of a bfloat16 tile, so each wave keeps NBUF - 1 tiles in flight in a register ring while it
+// computes one (a tile's registers are few: 16 per 16 keys at head_dim 128).
 // ---------------------------------------------------------------------------------------
-template <int D, int G, int HT, int W>
+template <int D, int G, int HT, int W, int NBUF>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(W, W)))
 decode_fp8_kernel(DecodeArgs a) {
   constexpr int QROWB = D * 2;                // bytes of one bfloat16 q row
@@ -84,7 +86,10 @@ decode_fp8_kernel(DecodeArgs a) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int f = xcd_remap(blockIdx.x, gridDim.x);
+  // Items in grid order: the host lists them longest first and the hardware deals consecutive
+  // workgroups to the 8 XCDs in turn, so every XCD gets its share of full and short splits.
+  // (The heads of one item read disjoint cache lines, so keeping them on one XCD buys nothing.)
+  const int f = blockIdx.x;
   const int item_idx = f / a.hkv;
   const int g = f - item_idx * a.hkv;
   const int hq0 = g * G;
@@ -241,20 +246,28 @@ decode_fp8_kernel(DecodeArgs a) {
     }
   };
 
+  // tiles hs, hs + kStep, ... of this wave, ascending; tile i lives in ring buffer i % NBUF
   constexpr int kStep = kDecodeWaves * HT;
-  uint4 ka[NIK], kb2[NIK];
-  uint2 va[NIV], vb[NIV];
+  uint4 kbuf[NBUF][NIK];
+  uint2 vbuf[NBUF][NIV];
   int hs = t0 + wave * HT;
-  if (hs < t1) load(ka, va, hs);
-  while (hs < t1) {
-    const int hs1 = hs + kStep;
-    if (hs1 < t1) load(kb2, vb, hs1);
-    compute(ka, va, hs);
-    if (hs1 >= t1) break;
-    const int hs2 = hs1 + kStep;
-    if (hs2 < t1) load(ka, va, hs2);
-    compute(kb2, vb, hs1);
-    hs = hs2;
+#pragma unroll
+  for (int b = 0; b < NBUF - 1; ++b)
+    if (hs + b * kStep < t1) load(kbuf[b], vbuf[b], hs + b * kStep);
+  for (bool more = hs < t1; more;) {
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b) {
+      const int cur = hs + b * kStep;
+      if (more && cur < t1) {
+        const int nxt = cur + (NBUF - 1) * kStep;
+        if (nxt < t1) load(kbuf[(b + NBUF - 1) % NBUF], vbuf[(b + NBUF - 1) % NBUF], nxt);
+        compute(kbuf[b], vbuf[b], cur);
+      } else {
+        more = false;
+      }
+    }
+    hs += NBUF * kStep;
+    more = more && hs < t1;
   }
 
 #pragma unroll
@@ -318,13 +331,15 @@ bool decode_fp8_supported(int head_dim, int group) {
   return (head_dim == 64 || head_dim == 128) && (group == 1 || group == 2 || group == 4);
 }
 
+// Instances (keys per tile, waves-per-SIMD register budget, ring depth), measured on the
+// batched 64-sequence step (groups of 4) and 32-sequence steps with groups of 1 and 2.
 template <int D>
 static hipError_t launch_fp8_d(const DecodeArgs& a, uint32_t grid, int group,
                                hipStream_t stream) {
   switch (group) {
-    case 1: hipLaunchKernelGGL((decode_fp8_kernel<D, 1, 32, 2>), dim3(grid), dim3(256), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((decode_fp8_kernel<D, 2, 32, 2>), dim3(grid), dim3(256), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((decode_fp8_kernel<D, 4, 16, 3>), dim3(grid), dim3(256), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((decode_fp8_kernel<D, 1, 32, 3, 2>), dim3(grid), dim3(256), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((decode_fp8_kernel<D, 2, 32, 3, 2>), dim3(grid), dim3(256), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((decode_fp8_kernel<D, 4, 16, 3, 3>), dim3(grid), dim3(256), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
