@@ -198,3 +198,22 @@ def test_fused_fp8_step_equals_separate_calls_bitwise():
     assert np.array_equal(_codes(a.k_cache), _codes(b.k_cache))
     assert np.array_equal(_codes(a.v_cache), _codes(b.v_cache))
     assert np.array_equal(fused, sep)
+
+
+def test_fp8_rows_are_bitwise_the_same_as_decode_rows_and_in_any_chunking():
+    """Every row of an E4M3 step runs on the split decode pass, so a token's bits do not depend
+    on its segment's kind or chunking: one 300-row chunk, the same rows re-cut into chunks
+    (1-row segments are decode rows), and a decode row at the same position all agree."""
+    w = make_workload(explicit_spec("fp8-phase", "bf16", 16, 4, 128, 16,
+                                    [(700, 300), (90, 2), (300, 1)], kv_dtype="fp8",
+                                    k_scale=1 / 32, v_scale=1 / 40))
+    gst = _harness()(w, device=DEV)
+    s = w.spec
+    full = gst.attention().cpu().numpy().copy()
+    rows = full[0:300]
+    bt = gst.block_tables_dev[0:1].contiguous()
+    for lo, hi in [(0, 37), (37, 101), (101, 102), (102, 103), (103, 299), (299, 300)]:
+        out = pkv.attention_fp8(gst.q[lo:hi].contiguous(), gst.k_cache, gst.v_cache, bt,
+                                [400 + hi], [0, hi - lo], w.scale, s.k_scale, s.v_scale)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), rows[lo:hi]), (lo, hi)
