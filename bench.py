@@ -39,7 +39,7 @@ def _parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="batched-bf16-decode")
-    ap.add_argument("--extra", default="mixed-ragged-step,batched-fp8-decode",
+    ap.add_argument("--extra", default="mixed-ragged-step,batched-fp8-decode,mixed-fp8-step",
                     help="comma-separated workloads timed the same way, reported under 'extra'")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline sample")
@@ -94,8 +94,6 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
     from workloads import ALL_CONFIGS, make_workload
 
     w = make_workload(ALL_CONFIGS[name])
-    if w.kv_fp8 and phase_consistent:
-        raise ValueError("E4M3 pools have no phase-consistent tile path")
     t_build = time.time()
     gst = build_gpu_step(w, device=device)
     t_build = time.time() - t_build
@@ -107,7 +105,7 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
     bt_np = np.ascontiguousarray(gst.block_tables, dtype=np.int32)
     if w.kv_fp8:
         ws_bytes = pkv.write_kv_attention_fp8_workspace_size(ctx_np, cu_np, s.Hq, s.Hkv, s.D,
-                                                             w.T, s.kv_split)
+                                                             w.T, s.kv_split, phase_consistent)
     else:
         ws_bytes = pkv.write_kv_attention_workspace_size(
             ctx_np, cu_np, s.Hq, s.Hkv, s.D, w.T, s.kv_split,
@@ -123,7 +121,7 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
             pkv.write_kv_attention_fp8(gst.q, gst.k_new, gst.v_new, sl, gst.k_cache, gst.v_cache,
                                        gst.block_tables_dev, ctx_np, cu_np, w.scale, s.k_scale,
                                        s.v_scale, out=out, workspace=workspace,
-                                       kv_split=s.kv_split)
+                                       kv_split=s.kv_split, phase_consistent=phase_consistent)
             return
         pkv.write_kv_attention(gst.q, gst.k_new, gst.v_new, sl, gst.k_cache, gst.v_cache,
                                gst.block_tables_dev, ctx_np, cu_np, w.scale, out=out,
@@ -150,8 +148,7 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
     # record costs the stream a few microseconds, so bracketing every launch of every kernel
     # would stretch the step it times). Every kernel's time is then taken in a second, untimed
     # pass of the same steps with all launches bracketed.
-    dominant = "decode" if (w.kv_fp8 or (w.q_lens == 1).any()) and not phase_consistent \
-        else "prefill"
+    dominant = "decode" if (w.q_lens == 1).any() and not phase_consistent else "prefill"
     gc.callbacks.append(on_gc)
     if kernel_events == "timed":
         pkv.profile_set_kinds([])

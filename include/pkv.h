@@ -345,14 +345,15 @@ int32_t pkv_write_kv_attention(const void* q, const void* k_new, const void* v_n
  * Errors: PKV_ERR_INVALID (sizes, NULL pointers, scales), PKV_ERR_UNSUPPORTED (row width),
  * PKV_ERR_HIP. n_rows == 0 is a no-op.
  *
- * pkv_attention_fp8: pkv_attention over E4M3 pools, q bfloat16, out float32, every row (decode
- * and prefill) on the split decode pass: same splits, tiles, wave order and merge order, hence
- * the same batch invariance as pkv_attention's decode rows. K codes widen exactly to bfloat16
- * and meet q in float32 products; k_scale folds into the score scale; V codes widen exactly to
- * float32 and v_scale multiplies each split's numerator once. head_dim 64 or 128,
- * num_q_heads / num_kv_heads in {1, 2, 4}. Workspace from pkv_attention_fp8_workspace_size,
- * same ownership rules as pkv_attention. Errors: as pkv_attention, plus PKV_ERR_INVALID for
- * scales that are not finite and > 0. */
+ * pkv_attention_fp8: pkv_attention_ex over E4M3 pools, q bfloat16, out float32, with the same
+ * routing, splits, tiles and merge order, hence the same batch invariance: decode rows on the
+ * split decode pass over the codes, prefill rows (and with PKV_ATTN_PHASE_CONSISTENT every
+ * row) on the MFMA tile path, which widens each tile's codes to bfloat16 in LDS. Codes widen
+ * exactly (every E4M3 value is a bfloat16 value); k_scale folds into the score scale, v_scale
+ * multiplies each split numerator (decode) or output (tiles) once. head_dim 64 or 128,
+ * num_q_heads / num_kv_heads in {1, 2, 4}; flags as pkv_attention_ex. Workspace from
+ * pkv_attention_fp8_workspace_size (same flags), same ownership rules as pkv_attention.
+ * Errors: as pkv_attention_ex, plus PKV_ERR_INVALID for scales that are not finite and > 0. */
 int32_t pkv_write_kv_fp8(const void* k_new, const void* v_new, const int32_t* slots_dev,
                          int32_t n_rows, void* k_cache, void* v_cache, int32_t num_blocks,
                          int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
@@ -361,27 +362,29 @@ int32_t pkv_write_kv_fp8(const void* k_new, const void* v_new, const int32_t* sl
 int32_t pkv_attention_fp8_workspace_size(const int32_t* ctx_lens_host,
                                          const int32_t* cu_seqlens_q_host, int32_t B,
                                          int32_t num_q_heads, int32_t num_kv_heads,
-                                         int32_t head_dim, int32_t kv_split, size_t* bytes);
+                                         int32_t head_dim, int32_t kv_split, uint32_t flags,
+                                         size_t* bytes);
 
 int32_t pkv_attention_fp8(const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* block_tables_dev, int32_t max_blocks,
                           const int32_t* ctx_lens_host, const int32_t* cu_seqlens_q_host,
                           int32_t B, int32_t T, int32_t num_q_heads, int32_t num_kv_heads,
                           int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
-                          float k_scale, float v_scale, int32_t kv_split, float* out,
-                          void* workspace, size_t workspace_bytes, void* stream);
+                          float k_scale, float v_scale, int32_t kv_split, uint32_t flags,
+                          float* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Fused E4M3 step: pkv_write_kv_fp8 of k_new / v_new through host slots followed by
  * pkv_attention_fp8, with the slots in the same host-to-device copy as the work lists, as
  * pkv_write_kv_attention does for bfloat16 / float32 pools (same slot rules: negative skips,
  * >= num_blocks * block_size is PKV_ERR_INVALID). Workspace from
- * pkv_write_kv_attention_fp8_workspace_size (n_rows >= 0). Errors: as pkv_write_kv_fp8 and
- * pkv_attention_fp8. */
+ * pkv_write_kv_attention_fp8_workspace_size (same flags, n_rows >= 0). Errors: as
+ * pkv_write_kv_fp8 and pkv_attention_fp8. */
 int32_t pkv_write_kv_attention_fp8_workspace_size(const int32_t* ctx_lens_host,
                                                   const int32_t* cu_seqlens_q_host, int32_t B,
                                                   int32_t num_q_heads, int32_t num_kv_heads,
                                                   int32_t head_dim, int32_t kv_split,
-                                                  int32_t n_rows, size_t* bytes);
+                                                  uint32_t flags, int32_t n_rows,
+                                                  size_t* bytes);
 
 int32_t pkv_write_kv_attention_fp8(const void* q, const void* k_new, const void* v_new,
                                    const int32_t* slots_host, int32_t n_rows, void* k_cache,
@@ -390,8 +393,9 @@ int32_t pkv_write_kv_attention_fp8(const void* q, const void* k_new, const void*
                                    const int32_t* cu_seqlens_q_host, int32_t B, int32_t T,
                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                    int32_t block_size, int32_t num_blocks, float scale,
-                                   float k_scale, float v_scale, int32_t kv_split, float* out,
-                                   void* workspace, size_t workspace_bytes, void* stream);
+                                   float k_scale, float v_scale, int32_t kv_split,
+                                   uint32_t flags, float* out, void* workspace,
+                                   size_t workspace_bytes, void* stream);
 
 /* ---- diagnostics: per-kernel device time ------------------------------------------------
  * While enabled, every kernel launched by pkv_write_kv / pkv_attention is bracketed by two HIP

@@ -134,17 +134,18 @@ _SIGS = {
     "pkv_write_kv_fp8": ([_vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
                           ctypes.c_float, ctypes.c_float, _vp], _i32),
     "pkv_attention_fp8_workspace_size": ([_pi32, _pi32, _i32, _i32, _i32, _i32, _i32,
-                                          ctypes.POINTER(ctypes.c_size_t)], _i32),
+                                          ctypes.c_uint32, ctypes.POINTER(ctypes.c_size_t)],
+                                         _i32),
     "pkv_attention_fp8": ([_vp, _vp, _vp, _vp, _i32, _pi32, _pi32, _i32, _i32, _i32, _i32,
                            _i32, _i32, _i32, ctypes.c_float, ctypes.c_float, ctypes.c_float,
-                           _i32, _vp, _vp, ctypes.c_size_t, _vp], _i32),
+                           _i32, ctypes.c_uint32, _vp, _vp, ctypes.c_size_t, _vp], _i32),
     "pkv_write_kv_attention_fp8_workspace_size": ([_pi32, _pi32, _i32, _i32, _i32, _i32, _i32,
-                                                   _i32, ctypes.POINTER(ctypes.c_size_t)],
-                                                  _i32),
+                                                   ctypes.c_uint32, _i32,
+                                                   ctypes.POINTER(ctypes.c_size_t)], _i32),
     "pkv_write_kv_attention_fp8": ([_vp, _vp, _vp, _pi32, _i32, _vp, _vp, _vp, _i32, _pi32,
                                     _pi32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
-                                    ctypes.c_float, ctypes.c_float, ctypes.c_float, _i32, _vp,
-                                    _vp, ctypes.c_size_t, _vp], _i32),
+                                    ctypes.c_float, ctypes.c_float, ctypes.c_float, _i32,
+                                    ctypes.c_uint32, _vp, _vp, ctypes.c_size_t, _vp], _i32),
     "pkv_profile_set_kinds": ([ctypes.c_uint32], _i32),
     "pkv_profile_enable": ([_i32], _i32),
     "pkv_profile_read": ([_i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)], _i32),
@@ -606,22 +607,25 @@ def write_kv_fp8(k_new, v_new, slots, k_cache, v_cache, k_scale: float, v_scale:
 
 
 def attention_fp8_workspace_size(ctx_lens, cu_seqlens_q, num_q_heads: int, num_kv_heads: int,
-                                 head_dim: int, kv_split: int = 512) -> int:
+                                 head_dim: int, kv_split: int = 512,
+                                 phase_consistent: bool = False) -> int:
     ctx = _host_i32(ctx_lens)
     cu = _host_i32(cu_seqlens_q)
     out = ctypes.c_size_t(0)
+    flags = PKV_ATTN_PHASE_CONSISTENT if phase_consistent else 0
     _check(lib().pkv_attention_fp8_workspace_size(_ptr(ctx), _ptr(cu), ctx.size,
                                                   int(num_q_heads), int(num_kv_heads),
-                                                  int(head_dim), int(kv_split),
+                                                  int(head_dim), int(kv_split), flags,
                                                   ctypes.byref(out)))
     return int(out.value)
 
 
 def attention_fp8(q, k_cache, v_cache, block_tables, ctx_lens, cu_seqlens_q, scale: float,
                   k_scale: float, v_scale: float, out=None, workspace=None,
-                  kv_split: int = 512, stream=None):
+                  kv_split: int = 512, stream=None, phase_consistent: bool = False):
     """pkv_attention_fp8: the ragged step over E4M3 pools (uint8 [NB, BS, Hkv, D]) with
-    per-tensor scales; q bfloat16 [T, Hq, D]; returns out (float32 [T, Hq, D])."""
+    per-tensor scales; q bfloat16 [T, Hq, D]; returns out (float32 [T, Hq, D]).
+    phase_consistent=True sets PKV_ATTN_PHASE_CONSISTENT (every row on the tile path)."""
     import torch
     _need_cuda(q, k_cache, v_cache, block_tables)
     _need_fp8_pools(k_cache, v_cache)
@@ -641,32 +645,37 @@ def attention_fp8(q, k_cache, v_cache, block_tables, ctx_lens, cu_seqlens_q, sca
     if out is None:
         out = torch.empty((T, hq, d), dtype=torch.float32, device=q.device)
     _need_cuda(out)
-    need = attention_fp8_workspace_size(ctx, cu, hq, hkv, d, kv_split)
+    need = attention_fp8_workspace_size(ctx, cu, hq, hkv, d, kv_split, phase_consistent)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    flags = PKV_ATTN_PHASE_CONSISTENT if phase_consistent else 0
     _check(lib().pkv_attention_fp8(
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
         int(block_tables.shape[1]), _ptr(ctx), _ptr(cu), B, T, hq, hkv, d, bs, nb, float(scale),
-        float(k_scale), float(v_scale), int(kv_split), out.data_ptr(), workspace.data_ptr(),
+        float(k_scale), float(v_scale), int(kv_split), flags, out.data_ptr(),
+        workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream_ptr(q, stream)))
     return out
 
 
 def write_kv_attention_fp8_workspace_size(ctx_lens, cu_seqlens_q, num_q_heads: int,
                                          num_kv_heads: int, head_dim: int, n_rows: int,
-                                         kv_split: int = 512) -> int:
+                                         kv_split: int = 512,
+                                         phase_consistent: bool = False) -> int:
     ctx = _host_i32(ctx_lens)
     cu = _host_i32(cu_seqlens_q)
     out = ctypes.c_size_t(0)
+    flags = PKV_ATTN_PHASE_CONSISTENT if phase_consistent else 0
     _check(lib().pkv_write_kv_attention_fp8_workspace_size(
         _ptr(ctx), _ptr(cu), ctx.size, int(num_q_heads), int(num_kv_heads), int(head_dim),
-        int(kv_split), int(n_rows), ctypes.byref(out)))
+        int(kv_split), flags, int(n_rows), ctypes.byref(out)))
     return int(out.value)
 
 
 def write_kv_attention_fp8(q, k_new, v_new, slots, k_cache, v_cache, block_tables, ctx_lens,
                            cu_seqlens_q, scale: float, k_scale: float, v_scale: float, out=None,
-                           workspace=None, kv_split: int = 512, stream=None):
+                           workspace=None, kv_split: int = 512, stream=None,
+                           phase_consistent: bool = False):
     """pkv_write_kv_attention_fp8: the E4M3 append of bfloat16 k_new / v_new [T_w, Hkv, D]
     through host slots [T_w] and the attention over the step in one call; returns out."""
     import torch
@@ -695,13 +704,15 @@ def write_kv_attention_fp8(q, k_new, v_new, slots, k_cache, v_cache, block_table
         out = torch.empty((T, hq, d), dtype=torch.float32, device=q.device)
     _need_cuda(out)
     if workspace is None:
-        need = write_kv_attention_fp8_workspace_size(ctx, cu, hq, hkv, d, n_rows, kv_split)
+        need = write_kv_attention_fp8_workspace_size(ctx, cu, hq, hkv, d, n_rows, kv_split,
+                                                     phase_consistent)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    flags = PKV_ATTN_PHASE_CONSISTENT if phase_consistent else 0
     _check(lib().pkv_write_kv_attention_fp8(
         q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), _ptr(sl), n_rows, k_cache.data_ptr(),
         v_cache.data_ptr(), block_tables.data_ptr(), int(block_tables.shape[1]), _ptr(ctx),
         _ptr(cu), B, T, hq, hkv, d, bs, nb, float(scale), float(k_scale), float(v_scale),
-        int(kv_split), out.data_ptr(), workspace.data_ptr(),
+        int(kv_split), flags, out.data_ptr(), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream_ptr(q, stream)))
     return out
 

@@ -462,14 +462,13 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
                        pkv::WriteArgs* wr, const int32_t* slots_host,
                        const float* fp8_scales = nullptr, pkv::WriteFp8Args* wr8 = nullptr) {
   // fp8_scales != nullptr: q is bfloat16 and the pools hold E4M3 codes with per-tensor scales
-  // {k_scale, v_scale}; every row runs on the split decode pass over those pools
+  // {k_scale, v_scale}; rows are routed as for bfloat16 pools, onto the E4M3 kernels
   int32_t st = check_heads(num_q_heads, num_kv_heads, head_dim, kv_split, dtype);
   if (st != PKV_OK) return st;
   st = check_flags(flags, num_q_heads, num_kv_heads, head_dim, dtype);
   if (st != PKV_OK) return st;
   if (fp8_scales != nullptr) {
-    if (dtype != PKV_BF16 || flags != 0)
-      return fail(PKV_ERR_INVALID, "attention_fp8: q must be bfloat16 and flags 0");
+    if (dtype != PKV_BF16) return fail(PKV_ERR_INVALID, "attention_fp8: q must be bfloat16");
     if (!pkv::decode_fp8_supported(head_dim, num_q_heads / num_kv_heads))
       return fail(PKV_ERR_UNSUPPORTED, "attention_fp8: head_dim 64 or 128 and num_q_heads / "
                                        "num_kv_heads one of 1, 2, 4");
@@ -504,9 +503,8 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
     return fail(PKV_ERR_INVALID, "attention: q, pools and workspace must be 16-byte aligned, "
                                  "out and block_tables 4-byte aligned");
 
-  StepShape s = shape_for(ctx_lens_host, cu_seqlens_q_host, B, num_q_heads, num_kv_heads,
-                          head_dim, kv_split, dtype, flags);
-  if (fp8_scales != nullptr) s.prefill_on_mfma = false;
+  const StepShape s = shape_for(ctx_lens_host, cu_seqlens_q_host, B, num_q_heads, num_kv_heads,
+                                head_dim, kv_split, dtype, flags);
   const pkv::WorkspaceLayout L = layout_for(s, num_q_heads, head_dim, n_write);
   if (workspace_bytes < L.total || (L.total > 0 && workspace == nullptr))
     return fail(PKV_ERR_INVALID, "attention: workspace smaller than the workspace-size query (" +
@@ -539,7 +537,11 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
   }
   if (T == 0) return ok();
 
-  const float scale_log2e = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  // scores in the base-2 domain: scale * log2(e), times the K scale for E4M3 pools
+  const double k_scale = fp8_scales != nullptr ? static_cast<double>(fp8_scales[0]) : 1.0;
+  const float scale_log2e =
+      static_cast<float>(static_cast<double>(scale) * k_scale * 1.4426950408889634);
+  const float v_scale = fp8_scales != nullptr ? fp8_scales[1] : 1.f;
   int32_t bs_log2 = -1;
   for (int sh = 0; sh < 31; ++sh)
     if ((1 << sh) == block_size) bs_log2 = sh;
@@ -563,10 +565,12 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
     p.hkv = num_kv_heads;
     p.scale_log2e = std::fabs(scale_log2e);
     p.negate_q = scale < 0.f ? 1 : 0;
+    p.v_scale = v_scale;
     p.items = reinterpret_cast<const pkv::PrefillItem*>(ws + L.prefill_off);
     p.out = out;
     const int pr = prof_begin(1, strm);
-    hipError_t e = pkv::launch_prefill(p, L.n_prefill, head_dim, group, strm);
+    hipError_t e = pkv::launch_prefill(p, L.n_prefill, head_dim, group, fp8_scales != nullptr,
+                                       strm);
     prof_end(pr, strm);
     if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("prefill launch: ") + hipGetErrorString(e));
   }
@@ -584,12 +588,7 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
     d.hkv = num_kv_heads;
     d.kv_split = kv_split;
     d.scale_log2e = scale_log2e;
-    d.v_scale = 1.f;
-    if (fp8_scales != nullptr) {
-      d.scale_log2e = static_cast<float>(static_cast<double>(scale) * fp8_scales[0] *
-                                         1.4426950408889634);
-      d.v_scale = fp8_scales[1];
-    }
+    d.v_scale = v_scale;
     d.items = reinterpret_cast<const pkv::DecodeItem*>(ws + L.decode_off);
     d.group = group;
     d.out = out;
@@ -636,12 +635,9 @@ int32_t workspace_size_impl(const int32_t* ctx_lens_host, const int32_t* cu_seql
   if (st != PKV_OK) return st;
   StepShape s = shape_for(ctx_lens_host, cu_seqlens_q_host, B, num_q_heads, num_kv_heads,
                           head_dim, kv_split, dtype, flags);
-  if (fp8) {
-    if (!pkv::decode_fp8_supported(head_dim, num_q_heads / num_kv_heads))
-      return fail(PKV_ERR_UNSUPPORTED, "attention_fp8: head_dim 64 or 128 and num_q_heads / "
-                                       "num_kv_heads one of 1, 2, 4");
-    s.prefill_on_mfma = false;
-  }
+  if (fp8 && !pkv::decode_fp8_supported(head_dim, num_q_heads / num_kv_heads))
+    return fail(PKV_ERR_UNSUPPORTED, "attention_fp8: head_dim 64 or 128 and num_q_heads / "
+                                     "num_kv_heads one of 1, 2, 4");
   *bytes = layout_for(s, num_q_heads, head_dim, n_write_rows).total;
   return ok();
 }
@@ -807,9 +803,10 @@ extern "C" int32_t pkv_attention_fp8_workspace_size(const int32_t* ctx_lens_host
                                                     const int32_t* cu_seqlens_q_host,
                                                     int32_t B, int32_t num_q_heads,
                                                     int32_t num_kv_heads, int32_t head_dim,
-                                                    int32_t kv_split, size_t* bytes) {
+                                                    int32_t kv_split, uint32_t flags,
+                                                    size_t* bytes) {
   return workspace_size_impl(ctx_lens_host, cu_seqlens_q_host, B, num_q_heads, num_kv_heads,
-                             head_dim, kv_split, PKV_BF16, 0u, 0, bytes, true);
+                             head_dim, kv_split, PKV_BF16, flags, 0, bytes, true);
 }
 
 extern "C" int32_t pkv_attention_fp8(const void* q, const void* k_cache, const void* v_cache,
@@ -819,21 +816,21 @@ extern "C" int32_t pkv_attention_fp8(const void* q, const void* k_cache, const v
                                      int32_t num_q_heads, int32_t num_kv_heads,
                                      int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                      float scale, float k_scale, float v_scale,
-                                     int32_t kv_split, float* out, void* workspace,
-                                     size_t workspace_bytes, void* stream) {
+                                     int32_t kv_split, uint32_t flags, float* out,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
   const float scales[2] = {k_scale, v_scale};
   return attention_impl(q, k_cache, v_cache, block_tables_dev, max_blocks, ctx_lens_host,
                         cu_seqlens_q_host, B, T, num_q_heads, num_kv_heads, head_dim, block_size,
-                        num_blocks, scale, kv_split, PKV_BF16, 0u, out, workspace,
+                        num_blocks, scale, kv_split, PKV_BF16, flags, out, workspace,
                         workspace_bytes, stream, nullptr, nullptr, scales);
 }
 
 extern "C" int32_t pkv_write_kv_attention_fp8_workspace_size(
     const int32_t* ctx_lens_host, const int32_t* cu_seqlens_q_host, int32_t B,
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t kv_split,
-    int32_t n_rows, size_t* bytes) {
+    uint32_t flags, int32_t n_rows, size_t* bytes) {
   return workspace_size_impl(ctx_lens_host, cu_seqlens_q_host, B, num_q_heads, num_kv_heads,
-                             head_dim, kv_split, PKV_BF16, 0u, n_rows, bytes, true);
+                             head_dim, kv_split, PKV_BF16, flags, n_rows, bytes, true);
 }
 
 extern "C" int32_t pkv_write_kv_attention_fp8(
@@ -842,7 +839,8 @@ extern "C" int32_t pkv_write_kv_attention_fp8(
     int32_t max_blocks, const int32_t* ctx_lens_host, const int32_t* cu_seqlens_q_host,
     int32_t B, int32_t T, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
     int32_t block_size, int32_t num_blocks, float scale, float k_scale, float v_scale,
-    int32_t kv_split, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+    int32_t kv_split, uint32_t flags, float* out, void* workspace, size_t workspace_bytes,
+    void* stream) {
   pkv::WriteFp8Args a;
   int32_t st = check_write_fp8(k_new, v_new, n_rows, k_cache, v_cache, num_blocks, block_size,
                                num_kv_heads, head_dim, k_scale, v_scale, &a);
@@ -850,7 +848,7 @@ extern "C" int32_t pkv_write_kv_attention_fp8(
   const float scales[2] = {k_scale, v_scale};
   return attention_impl(q, k_cache, v_cache, block_tables_dev, max_blocks, ctx_lens_host,
                         cu_seqlens_q_host, B, T, num_q_heads, num_kv_heads, head_dim, block_size,
-                        num_blocks, scale, kv_split, PKV_BF16, 0u, out, workspace,
+                        num_blocks, scale, kv_split, PKV_BF16, flags, out, workspace,
                         workspace_bytes, stream, nullptr, slots_host, scales, &a);
 }
 

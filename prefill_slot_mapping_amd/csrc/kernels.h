@@ -87,8 +87,9 @@ struct PrefillArgs {
   int32_t hq;
   int32_t hkv;
   int32_t n_items;
-  float scale_log2e;  // |scale| * log2(e)
+  float scale_log2e;  // |scale| * log2(e) (E4M3 pools: times the K scale as well)
   int32_t negate_q;   // scale < 0: the kernel flips the sign of q instead
+  float v_scale;      // E4M3 pools: the V scale (1 otherwise)
   const PrefillItem* items;
   float* out;
 };
@@ -103,7 +104,7 @@ hipError_t launch_decode(const DecodeArgs& a, int64_t n_items, int head_dim, int
                          bool bf16, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int64_t n_items, int head_dim, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int64_t n_items, int head_dim, int group,
-                          hipStream_t stream);
+                          bool fp8, hipStream_t stream);
 
 // Whether a (head_dim, group, dtype) combination has a built decode / prefill kernel.
 bool decode_supported(int head_dim, int group);

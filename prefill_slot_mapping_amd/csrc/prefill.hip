@@ -19,6 +19,13 @@
 // a tile that none of a wave's rows can see is skipped by that wave, which is bitwise the same
 // as processing it (max unchanged, alpha = 1, p = 0). Hence a row's bits depend only on its
 // own query, position and sequence K/V, never on how its segment was chunked or batched.
+//
+// E4M3 pools (the F8 instances; "Finish RL Training Faster: Bitwise-Consistent ...", section
+// 4.2, FP8 KV storage with one read path): a tile's codes (half the bytes) are copied global ->
+// LDS into a double-buffered staging area, then every wave widens its share of them exactly
+// to bfloat16 into the one bf16 tile buffer the MFMA operand reads use (every E4M3 value is a
+// bfloat16 value). The K scale is folded into the score scale by the host; the V scale
+// multiplies each output once. Everything else, and so the numeric contract, is as above.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -63,18 +70,43 @@ __device__ __forceinline__ void tile_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int D, int G>
+// 16 E4M3 codes -> 16 bfloat16 values (two 16-byte chunks), exactly
+__device__ __forceinline__ void e4m3x16_to_bf16(uint4 c, uint4& lo, uint4& hi) {
+  auto pk = [](uint32_t w, bool h) {
+    return __builtin_bit_cast(uint32_t, h ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                                          : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  };
+  lo = make_uint4(pk(c.x, false), pk(c.x, true), pk(c.y, false), pk(c.y, true));
+  hi = make_uint4(pk(c.z, false), pk(c.z, true), pk(c.w, false), pk(c.w, true));
+}
+
+// The LDS writes of this wave have completed, then the workgroup meets (tile DMAs in flight
+// stay in flight).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int D, int G, bool F8>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_kernel(PrefillArgs a) {
-  constexpr int CPR = D / 8;                 // 16-byte chunks per head row
+  constexpr int CPR = D / 8;                 // 16-byte bf16 chunks per head row
   constexpr int KS = D / 16;                 // k-steps of S^T = K Q^T
   constexpr int DB = D / 32;                 // 32-wide d blocks of O^T
   constexpr int TC = kPrefillKeyTile * CPR;  // chunks per tile and tensor
   constexpr int NJ = TC / 256;               // DMA instructions per wave per tensor per tile
+  constexpr int CPC = D / 16;                // 16-byte code chunks per E4M3 head row
+  constexpr int TCC = kPrefillKeyTile * CPC; // code chunks per tile and tensor
+  constexpr int NJC = TCC / 256;             // code DMA instructions per wave per tensor
   static_assert(NJ >= 1 && TC % 256 == 0, "tile must cover the workgroup");
+  static_assert(!F8 || (NJC >= 1 && TCC % 256 == 0), "code tile must cover the workgroup");
 
-  // [buffer][tensor: 0 = K, 1 = V][chunk]: tile kt lives in buffer kt % 2
-  __shared__ uint4 s_kv[2][2][TC];
+  // [buffer][tensor: 0 = K, 1 = V][chunk]: tile kt lives in buffer kt % 2 (bf16 pools), or in
+  // the one buffer after its codes are widened (E4M3 pools: codes of tile kt in s_code[kt % 2])
+  constexpr int NBK = F8 ? 1 : 2;
+  __shared__ uint4 s_kv[NBK][2][TC];
+  __shared__ uint4 s_code[F8 ? 2 : 1][2][F8 ? TCC : 1];
   // a window of the sequence's block-table entries (validated), starting at entry win0
   __shared__ int s_blk[kPrefillBlockWindow];
   __shared__ int s_bad;
@@ -150,6 +182,48 @@ prefill_kernel(PrefillArgs a) {
   // K and V of tile kt into LDS buffer buf. Chunk position P holds chunk (P % CPR) ^ swz(row)
   // of key row P / CPR, so the swizzled layout comes from the source addresses. Keys no row
   // needs re-read the item's last key (finite data whose p is exactly 0).
+  // E4M3 codes of tile kt into staging buffer buf, row-major (code chunk P = chunk P % CPC of
+  // key row P / CPC); keys no row needs re-read the item's last key.
+  auto dma_codes = [&](int kt, int buf) {
+    const uint4* __restrict__ kc = static_cast<const uint4*>(a.k_cache);
+    const uint4* __restrict__ vc = static_cast<const uint4*>(a.v_cache);
+    const uint32_t stride_c = static_cast<uint32_t>(a.hkv * CPC);
+    uint64_t off[NJC];
+#pragma unroll
+    for (int j = 0; j < NJC; ++j) {
+      const int P = (wave * NJC + j) * 64 + lane;
+      const int row = P / CPC;
+      const int key = min(kt * kPrefillKeyTile + row, key_limit - 1);
+      const int e = entry_of(key);
+      const int in_blk = key - e * a.block_size;
+      const uint32_t slot = static_cast<uint32_t>(s_blk[e - win0] * a.block_size + in_blk);
+      off[j] = static_cast<uint64_t>(slot) * stride_c + g * CPC + (P % CPC);
+    }
+#pragma unroll
+    for (int j = 0; j < NJC; ++j) {
+      const int base = (wave * NJC + j) * 64;
+      dma16(kc + off[j], lds_addr(&s_code[buf][0][base]));
+      dma16(vc + off[j], lds_addr(&s_code[buf][1][base]));
+    }
+  };
+
+  // codes of staging buffer buf -> bfloat16 in the swizzled layout of s_kv[0], all waves
+  auto widen = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < NJC; ++j) {
+      const int P = (wave * NJC + j) * 64 + lane;
+      const int row = P / CPC;
+      const int c = P % CPC;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        uint4 lo, hi;
+        e4m3x16_to_bf16(s_code[buf][t][P], lo, hi);
+        s_kv[0][t][row * CPR + ((2 * c) ^ swz<CPR>(row))] = lo;
+        s_kv[0][t][row * CPR + ((2 * c + 1) ^ swz<CPR>(row))] = hi;
+      }
+    }
+  };
+
   auto dma_tile = [&](int kt, int buf) {
     uint64_t off[NJ];
 #pragma unroll
@@ -182,10 +256,11 @@ prefill_kernel(PrefillArgs a) {
   if (tid == 0) s_bad = 0;
   load_window();
   __syncthreads();
-  dma_tile(0, 0);
+  if constexpr (F8) dma_codes(0, 0);
+  else dma_tile(0, 0);
 
   for (int kt = 0; kt < n_tiles; ++kt) {
-    const int buf = kt & 1;
+    const int buf = F8 ? 0 : (kt & 1);
     // tile kt has landed in LDS; every wave is done with tile kt - 1 and with the block window
     tile_barrier();
     if (kt + 1 < n_tiles) {
@@ -195,7 +270,15 @@ prefill_kernel(PrefillArgs a) {
         load_window();
         tile_barrier();
       }
-      dma_tile(kt + 1, buf ^ 1);                       // in flight while this tile is computed
+      // in flight while this tile is computed
+      if constexpr (F8) dma_codes(kt + 1, (kt + 1) & 1);
+      else dma_tile(kt + 1, buf ^ 1);
+    }
+    if constexpr (F8) {
+      // every wave widens its share of tile kt (its codes landed before the barrier above; the
+      // bf16 buffer is free: every wave has finished tile kt - 1), then the workgroup meets
+      widen(kt & 1);
+      lds_barrier();
     }
 
     if (kt * kPrefillKeyTile > wave_last_pos) continue;  // no row of this wave sees this tile
@@ -305,6 +388,7 @@ prefill_kernel(PrefillArgs a) {
   const bool bad_item = s_bad != 0;
   if (!real) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float vs = a.v_scale;
   float* dst = a.out + ((static_cast<int64_t>(it.row0) + qrow) * a.hq +
                         static_cast<int64_t>(g) * G + head) * D;
 #pragma unroll
@@ -312,10 +396,17 @@ prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
       float4 o;
-      o.x = acc[db][4 * rq + 0] / l_tot;
-      o.y = acc[db][4 * rq + 1] / l_tot;
-      o.z = acc[db][4 * rq + 2] / l_tot;
-      o.w = acc[db][4 * rq + 3] / l_tot;
+      if constexpr (F8) {
+        o.x = acc[db][4 * rq + 0] * vs / l_tot;
+        o.y = acc[db][4 * rq + 1] * vs / l_tot;
+        o.z = acc[db][4 * rq + 2] * vs / l_tot;
+        o.w = acc[db][4 * rq + 3] * vs / l_tot;
+      } else {
+        o.x = acc[db][4 * rq + 0] / l_tot;
+        o.y = acc[db][4 * rq + 1] / l_tot;
+        o.z = acc[db][4 * rq + 2] / l_tot;
+        o.w = acc[db][4 * rq + 3] / l_tot;
+      }
       if (bad_item) o = make_float4(__builtin_nanf(""), __builtin_nanf(""),
                                     __builtin_nanf(""), __builtin_nanf(""));
       *reinterpret_cast<float4*>(dst + 32 * db + 8 * rq + 4 * h32) = o;
@@ -328,26 +419,35 @@ bool prefill_supported(int head_dim, int group, bool bf16) {
 }
 
 template <int D>
-static hipError_t launch_prefill_d(const PrefillArgs& a, uint32_t grid, int group,
+static hipError_t launch_prefill_d(const PrefillArgs& a, uint32_t grid, int group, bool fp8,
                                    hipStream_t stream) {
+  if (fp8) {
+    switch (group) {   // E4M3 pools: the groups the E4M3 decode pass serves
+      case 1: hipLaunchKernelGGL((prefill_kernel<D, 1, true>), dim3(grid), dim3(256), 0, stream, a); break;
+      case 2: hipLaunchKernelGGL((prefill_kernel<D, 2, true>), dim3(grid), dim3(256), 0, stream, a); break;
+      case 4: hipLaunchKernelGGL((prefill_kernel<D, 4, true>), dim3(grid), dim3(256), 0, stream, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (group) {
-    case 1: hipLaunchKernelGGL((prefill_kernel<D, 1>), dim3(grid), dim3(256), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((prefill_kernel<D, 2>), dim3(grid), dim3(256), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((prefill_kernel<D, 4>), dim3(grid), dim3(256), 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((prefill_kernel<D, 8>), dim3(grid), dim3(256), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((prefill_kernel<D, 1, false>), dim3(grid), dim3(256), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((prefill_kernel<D, 2, false>), dim3(grid), dim3(256), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((prefill_kernel<D, 4, false>), dim3(grid), dim3(256), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((prefill_kernel<D, 8, false>), dim3(grid), dim3(256), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int64_t n_items, int head_dim, int group,
-                          hipStream_t stream) {
+                          bool fp8, hipStream_t stream) {
   const int64_t grid64 = n_items * a.hkv;
   if (grid64 == 0) return hipSuccess;
   if (grid64 > 0x7fffffffLL || n_items != a.n_items) return hipErrorInvalidValue;
   const uint32_t grid = static_cast<uint32_t>(grid64);
-  if (head_dim == 64) return launch_prefill_d<64>(a, grid, group, stream);
-  if (head_dim == 128) return launch_prefill_d<128>(a, grid, group, stream);
+  if (head_dim == 64) return launch_prefill_d<64>(a, grid, group, fp8, stream);
+  if (head_dim == 128) return launch_prefill_d<128>(a, grid, group, fp8, stream);
   return hipErrorInvalidValue;
 }
 

@@ -65,17 +65,16 @@ class GpuStep:
             self.out = torch.empty((w.T, w.spec.Hq, w.spec.D), dtype=torch.float32,
                                    device=self.q.device)
         if w.kv_fp8:
-            if phase_consistent:
-                raise ValueError("E4M3 pools have no phase-consistent tile path")
             need = L.attention_fp8_workspace_size(w.ctx_lens, w.cu_seqlens_q, w.spec.Hq,
-                                                  w.spec.Hkv, w.spec.D, split)
+                                                  w.spec.Hkv, w.spec.D, split, phase_consistent)
             if self.workspace is None or self.workspace.numel() < need:
                 self.workspace = torch.empty(max(need, 1), dtype=torch.uint8,
                                              device=self.q.device)
             return L.attention_fp8(self.q, self.k_cache, self.v_cache, self.block_tables_dev,
                                    w.ctx_lens, w.cu_seqlens_q, w.scale, w.spec.k_scale,
                                    w.spec.v_scale, out=self.out, workspace=self.workspace,
-                                   kv_split=split, stream=stream)
+                                   kv_split=split, stream=stream,
+                                   phase_consistent=phase_consistent)
         need = L.attention_workspace_size(w.ctx_lens, w.cu_seqlens_q, w.spec.Hq, w.spec.Hkv,
                                           w.spec.D, split,
                                           L.PKV_BF16 if w.spec.dtype == "bf16" else L.PKV_F32,
@@ -96,13 +95,12 @@ class GpuStep:
         w = self.workload
         split = w.spec.kv_split if kv_split is None else kv_split
         if w.kv_fp8:
-            if phase_consistent:
-                raise ValueError("E4M3 pools have no phase-consistent tile path")
             if self.out is None:
                 self.out = torch.empty((w.T, w.spec.Hq, w.spec.D), dtype=torch.float32,
                                        device=self.q.device)
             need = L.write_kv_attention_fp8_workspace_size(w.ctx_lens, w.cu_seqlens_q, w.spec.Hq,
-                                                           w.spec.Hkv, w.spec.D, w.T, split)
+                                                           w.spec.Hkv, w.spec.D, w.T, split,
+                                                           phase_consistent)
             if self.workspace is None or self.workspace.numel() < need:
                 self.workspace = torch.empty(max(need, 1), dtype=torch.uint8,
                                              device=self.q.device)
@@ -111,7 +109,7 @@ class GpuStep:
                                             w.ctx_lens, w.cu_seqlens_q, w.scale, w.spec.k_scale,
                                             w.spec.v_scale, out=self.out,
                                             workspace=self.workspace, kv_split=split,
-                                            stream=stream)
+                                            stream=stream, phase_consistent=phase_consistent)
         if self.out is None:
             self.out = torch.empty((w.T, w.spec.Hq, w.spec.D), dtype=torch.float32,
                                    device=self.q.device)

@@ -337,14 +337,14 @@ def _attn_fp8(**kw):
     """Raw pkv_attention_fp8 call with fake device pointers: only validation may run."""
     lib = pkv.lib()
     a = dict(q=F, k=F, v=F, bt=F, mb=8, ctx=[5, 9], cu=[0, 1, 3], T=3, hq=8, hkv=2, d=128,
-             bs=16, nb=4, scale=0.1, ks=0.5, vs=0.5, split=512, out=F, ws=F, wsb=16)
+             bs=16, nb=4, scale=0.1, ks=0.5, vs=0.5, split=512, flags=0, out=F, ws=F, wsb=16)
     a.update(kw)
     ctx = np.asarray(a["ctx"], np.int32)
     cu = np.asarray(a["cu"], np.int32)
     return lib.pkv_attention_fp8(a["q"], a["k"], a["v"], a["bt"], a["mb"], L._ptr(ctx),
                                  L._ptr(cu), ctx.size, a["T"], a["hq"], a["hkv"], a["d"],
                                  a["bs"], a["nb"], a["scale"], a["ks"], a["vs"], a["split"],
-                                 a["out"], a["ws"], a["wsb"], None)
+                                 a["flags"], a["out"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -355,20 +355,25 @@ def _attn_fp8(**kw):
     (dict(ks=float("inf")), L.PKV_ERR_INVALID),
     (dict(split=100), L.PKV_ERR_INVALID),
     (dict(ctx=[5, 1]), L.PKV_ERR_INVALID),                  # q_len > ctx
+    (dict(flags=2), L.PKV_ERR_INVALID),                     # unknown flag bits
 ])
 def test_attention_fp8_validation_refuses_before_any_launch(kw, status):
     assert _attn_fp8(**kw) == status
     assert pkv.lib().pkv_last_error() != b""
 
 
-def test_attention_fp8_reaches_the_workspace_check_and_sizes_all_rows_as_decode():
+def test_attention_fp8_reaches_the_workspace_check_and_routes_rows_as_bf16():
     assert _attn_fp8() == L.PKV_ERR_INVALID                 # 16-byte workspace
     assert b"workspace" in pkv.lib().pkv_last_error()
+    assert _attn_fp8(flags=L.PKV_ATTN_PHASE_CONSISTENT) == L.PKV_ERR_INVALID
+    assert b"workspace" in pkv.lib().pkv_last_error()
     assert _attn_fp8(ctx=[], cu=[0], T=0) == L.PKV_OK
-    # a 300-row prefill chunk: split partials per row on the E4M3 path, none on the tile path
-    f8 = pkv.attention_fp8_workspace_size([2000], [0, 300], 8, 2, 128, 512)
-    bf = pkv.attention_workspace_size([2000], [0, 300], 8, 2, 128, 512)
-    assert f8 > bf
+    # the same work lists as bfloat16 pools: a prefill chunk on tiles, decode rows split
+    for ctx, cu in (([2000], [0, 300]), ([2000, 700], [0, 1, 2])):
+        for pc in (False, True):
+            f8 = pkv.attention_fp8_workspace_size(ctx, cu, 8, 2, 128, 512, pc)
+            bf = pkv.attention_workspace_size(ctx, cu, 8, 2, 128, 512, phase_consistent=pc)
+            assert f8 == bf
     with pytest.raises(pkv.Unsupported):
         pkv.attention_fp8_workspace_size([5], [0, 1], 16, 2, 128, 512)
 
@@ -391,17 +396,18 @@ def test_fused_fp8_step_validation():
     ctx = np.asarray([5, 9], np.int32)
     cu = np.asarray([0, 1, 3], np.int32)
 
-    def call(slots=(3, -1, 60), ks=0.5, hq=8, wsb=1 << 30):
+    def call(slots=(3, -1, 60), ks=0.5, hq=8, wsb=1 << 30, flags=0):
         sl = np.asarray(slots, np.int32)
         return lib.pkv_write_kv_attention_fp8(F, F, F, L._ptr(sl), sl.size, F, F, F, 8,
                                               L._ptr(ctx), L._ptr(cu), 2, 3, hq, 2, 128, 16, 4,
-                                              0.1, ks, 0.5, 512, F, F, wsb, None)
+                                              0.1, ks, 0.5, 512, flags, F, F, wsb, None)
     assert call(slots=(3, -1, 64)) == L.PKV_ERR_INVALID       # slot outside the pool
     assert b"outside" in pkv.lib().pkv_last_error()
     assert call(ks=-1.0) == L.PKV_ERR_INVALID
     assert call(hq=16) == L.PKV_ERR_UNSUPPORTED
     assert call(wsb=16) == L.PKV_ERR_INVALID
     assert b"workspace" in pkv.lib().pkv_last_error()
+    assert call(flags=4) == L.PKV_ERR_INVALID
     a = pkv.attention_fp8_workspace_size([5, 9], [0, 1, 3], 8, 2, 128, 512)
     b = pkv.write_kv_attention_fp8_workspace_size([5, 9], [0, 1, 3], 8, 2, 128, 1000, 512)
     assert b >= a + 4 * 1000

@@ -86,13 +86,13 @@ def test_write_fp8_skips_negative_and_out_of_range_slots():
     assert int((flat.reshape(nb * bs, -1) != 0).any(axis=1).sum()) == 1
 
 
-def check_step(w, rows=None, seqs=None):
-    print(f"[fp8-parity] {w.spec.name} B={w.B} T={w.T} NB={w.num_blocks}", flush=True)
+def check_step(w, rows=None, seqs=None, pc=False):
+    print(f"[fp8-parity] {w.spec.name} B={w.B} T={w.T} NB={w.num_blocks} pc={pc}", flush=True)
     gst = _harness()(w, device=DEV)
     ost = build_oracle_step(w, seqs=seqs, poison=seqs is None)
     assert np.array_equal(gst.block_tables, ost.block_tables)
     assert np.array_equal(gst.new_slots, ost.new_slots)
-    got = gst.attention()
+    got = gst.attention(phase_consistent=pc)
     torch.cuda.synchronize()
     got = got.cpu().numpy().astype(np.float64)
     ref = ost.attention(rows)
@@ -113,7 +113,7 @@ def test_small_fp8_configs_match_oracle_and_codes_are_bit_exact(name):
 
 
 EDGE = [
-    # (Hq, Hkv, D, BS, sequences (ctx, q_len)[, spec keywords]); every kernel instance
+    # (Hq, Hkv, D, BS, sequences (ctx, q_len)[, spec keywords]); every decode and tile instance
     (8, 8, 128, 16, [(1, 1), (2, 2), (16, 1), (17, 17), (513, 1), (1025, 1), (700, 130)]),
     (8, 4, 128, 5, [(7, 1), (129, 1), (642, 1), (88, 20)]),
     (16, 4, 128, 16, [(1, 1), (64, 1), (65, 1), (3000, 1), (90, 31)], {"kv_split": 64}),
@@ -123,15 +123,16 @@ EDGE = [
 ]
 
 
+@pytest.mark.parametrize("pc", [False, True], ids=["default", "phase-consistent"])
 @pytest.mark.parametrize("case", EDGE, ids=[f"G{c[0] // c[1]}-D{c[2]}-BS{c[3]}"
                                             + (f"-split{c[5]['kv_split']}" if len(c) > 5 else "")
                                             for c in EDGE])
-def test_fp8_edge_cases_match_oracle(case):
+def test_fp8_edge_cases_match_oracle(case, pc):
     hq, hkv, d, bs, seqs = case[:5]
     kw = case[5] if len(case) > 5 else {}
     w = make_workload(explicit_spec(f"edge-fp8-{hq}-{hkv}-{d}-{bs}", "bf16", hq, hkv, d, bs, seqs,
                                     kv_dtype="fp8", k_scale=1 / 32, v_scale=1 / 48, **kw))
-    check_step(w)
+    check_step(w, pc=pc)
 
 
 def test_fp8_alone_equals_batched_bitwise_and_run_to_run():
@@ -200,20 +201,40 @@ def test_fused_fp8_step_equals_separate_calls_bitwise():
     assert np.array_equal(fused, sep)
 
 
-def test_fp8_rows_are_bitwise_the_same_as_decode_rows_and_in_any_chunking():
-    """Every row of an E4M3 step runs on the split decode pass, so a token's bits do not depend
-    on its segment's kind or chunking: one 300-row chunk, the same rows re-cut into chunks
-    (1-row segments are decode rows), and a decode row at the same position all agree."""
-    w = make_workload(explicit_spec("fp8-phase", "bf16", 16, 4, 128, 16,
-                                    [(700, 300), (90, 2), (300, 1)], kv_dtype="fp8",
-                                    k_scale=1 / 32, v_scale=1 / 40))
+def _fp8_phase_workload():
+    return make_workload(explicit_spec("fp8-phase", "bf16", 16, 4, 128, 16,
+                                       [(700, 300), (90, 2), (300, 1)], kv_dtype="fp8",
+                                       k_scale=1 / 32, v_scale=1 / 40))
+
+
+@pytest.mark.parametrize("pc", [False, True], ids=["default", "phase-consistent"])
+def test_fp8_rechunking_is_bitwise_invisible(pc):
+    """A prefill segment's rows give the same bits as one chunk and re-cut into chunks (each
+    over the cache as it stands after it); with PKV_ATTN_PHASE_CONSISTENT 1-row segments
+    (decode rows) agree too, since every row then runs on the tile path."""
+    w = _fp8_phase_workload()
     gst = _harness()(w, device=DEV)
     s = w.spec
-    full = gst.attention().cpu().numpy().copy()
+    full = gst.attention(phase_consistent=pc).cpu().numpy().copy()
     rows = full[0:300]
     bt = gst.block_tables_dev[0:1].contiguous()
-    for lo, hi in [(0, 37), (37, 101), (101, 102), (102, 103), (103, 299), (299, 300)]:
+    cuts = [(0, 37), (37, 101), (101, 102), (102, 103), (103, 299), (299, 300)]
+    for lo, hi in cuts:
+        if hi - lo == 1 and not pc:
+            continue                        # a 1-row segment is a decode row: another kind
         out = pkv.attention_fp8(gst.q[lo:hi].contiguous(), gst.k_cache, gst.v_cache, bt,
-                                [400 + hi], [0, hi - lo], w.scale, s.k_scale, s.v_scale)
+                                [400 + hi], [0, hi - lo], w.scale, s.k_scale, s.v_scale,
+                                phase_consistent=pc)
         torch.cuda.synchronize()
         assert np.array_equal(out.cpu().numpy(), rows[lo:hi]), (lo, hi)
+
+
+def test_fp8_phase_consistent_mode_matches_oracle():
+    for name in ("mixed-fp8-step", "batched-fp8-decode", "prefix-shared-fp8-decode"):
+        w = make_workload(FP8_SMALL_CONFIGS[name])
+        gst = _harness()(w, device=DEV)
+        got = gst.attention(phase_consistent=True).cpu().numpy().astype(np.float64)
+        ref = build_oracle_step(w).attention()
+        err = float(np.abs(got - ref).max())
+        print(f"[fp8-parity] {name} phase-consistent max abs err {err:.3e}", flush=True)
+        assert err <= TOL
