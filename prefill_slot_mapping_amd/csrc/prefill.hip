@@ -12,7 +12,8 @@
 // position 0 and visited in ascending order up to the tile holding the item's last row:
 //   S^T[key][mrow] = K Q^T     16 MFMAs (2 key blocks x D/16 k-steps; K from LDS, Q in VGPRs)
 //   masked online softmax per M-row in the base-2 domain (float32), one row per lane pair
-//   O^T[d][mrow] += V^T P^T    P split into bf16 hi + lo parts (two MFMAs, ~16-bit P)
+//   O^T[d][mrow] += V^T P^T    P split into bf16 hi + lo parts (two MFMAs, ~16-bit P): hi is
+//                              p with its low 16 bits cleared, lo the exact remainder rounded
 // K and V tiles are staged row-major in LDS with an XOR swizzle on 16-byte chunks; the V^T
 // operand is read with ds_read_b64_tr_b16 (the hardware transpose read), so no transposed
 // store is needed. Keys past the item's last row are not loaded (zero-filled, so 0 * V = 0);
@@ -284,19 +285,22 @@ prefill_kernel(PrefillArgs a) {
     if (kt * kPrefillKeyTile > wave_last_pos) continue;  // no row of this wave sees this tile
     const uint4* sk = s_kv[buf][0];
 
-    // ---- S^T = K Q^T: two 32-key blocks ----
+    // ---- S^T = K Q^T: two 32-key blocks; all K fragments of a block are read before its
+    //      MFMAs so that the LDS latency is paid once per block ----
     f32x16_t s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
       const int row = kb * 32 + l32;
+      uint4 kf[KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint4 kv = sk[row * CPR + ((2 * ks + h32) ^ swz<CPR>(row))];
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv), qf[ks],
-                                                        s[kb], 0, 0, 0);
-      }
+      for (int ks = 0; ks < KS; ++ks) kf[ks] = sk[row * CPR + ((2 * ks + h32) ^ swz<CPR>(row))];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[ks]),
+                                                        qf[ks], s[kb], 0, 0, 0);
     }
 
     // ---- online softmax for this lane's M-row (keys split with lane ^ 32), base 2 ----
@@ -347,20 +351,30 @@ prefill_kernel(PrefillArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        bf16x8_t phi, plo;
+        // P = hi + lo: hi = p with its low 16 bits cleared (a bfloat16 value), lo = the exact
+        // float32 remainder rounded to bfloat16, so hi + lo carries about 16 bits of p
+        uint32_t phw[4], plw[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          float p = fast_exp2(fmaf(s[kb][8 * m + j], sl2, neg_m));
+        for (int j = 0; j < 8; j += 2) {
+          float p0 = fast_exp2(fmaf(s[kb][8 * m + j], sl2, neg_m));
+          float p1 = fast_exp2(fmaf(s[kb][8 * m + j + 1], sl2, neg_m));
           if (diag) {
             const int r = 8 * m + j;
             const int key = kt * kPrefillKeyTile + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-            p = key <= pos ? p : 0.f;
+            p0 = key <= pos ? p0 : 0.f;
+            p1 = key + 1 <= pos ? p1 : 0.f;
           }
-          psum += p;
-          const __bf16 ph = static_cast<__bf16>(p);
-          phi[j] = ph;
-          plo[j] = static_cast<__bf16>(p - static_cast<float>(ph));
+          psum += p0;
+          psum += p1;
+          const uint32_t b0 = __float_as_uint(p0), b1 = __float_as_uint(p1);
+          phw[j / 2] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+          const float l0 = p0 - __uint_as_float(b0 & 0xffff0000u);
+          const float l1 = p1 - __uint_as_float(b1 & 0xffff0000u);
+          typedef float f32x2_t __attribute__((ext_vector_type(2)));
+          plw[j / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{l0, l1}, bf16x2_t));
         }
+        const bf16x8_t phi = __builtin_bit_cast(bf16x8_t, phw);
+        const bf16x8_t plo = __builtin_bit_cast(bf16x8_t, plw);
         const int r0 = kb * 32 + 16 * m + 4 * (grp16 >> 1) + rsub;   // slots 0..3
         const int r1 = r0 + 8;                                        // slots 4..7
 #pragma unroll
