@@ -47,7 +47,10 @@ enum {
   PKV_ERR_INCONSISTENT = -7     /* allocator books do not add up */
 };
 
-enum { PKV_F32 = 0, PKV_BF16 = 1 };
+/* Element types. PKV_E4M3 (one-byte E4M3 codes) names the pools of the _fp8 entry points and
+ * is accepted as a pool type by pkv_copy_blocks only; the other entry points take PKV_F32 or
+ * PKV_BF16. */
+enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_E4M3 = 2 };
 
 /* Flag bits of pkv_attention_ex / pkv_attention_workspace_size_ex. */
 enum { PKV_ATTN_PHASE_CONSISTENT = 1 };
@@ -209,7 +212,8 @@ int32_t pkv_write_kv(const void* k_new, const void* v_new, const int32_t* slots_
  * [0, num_blocks), no destination twice, no destination that is also a source
  * (PKV_ERR_INVALID). The pairs go to the device through the library's pinned staging into
  * workspace (device, >= 8 * n_pairs bytes rounded up to 256, caller-owned; untouched until the
- * copy has run). Pools as in pkv_write_kv. Enqueued on stream; n_pairs == 0 is a no-op. */
+ * copy has run). Pools as in pkv_write_kv, or E4M3 pools (dtype PKV_E4M3). Enqueued on stream;
+ * n_pairs == 0 is a no-op. */
 int32_t pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs_host,
                         int32_t n_pairs, int32_t num_blocks, int32_t block_size,
                         int32_t num_kv_heads, int32_t head_dim, int32_t dtype, void* workspace,

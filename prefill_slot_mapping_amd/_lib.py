@@ -30,6 +30,7 @@ PKV_ERR_HIP = -6
 PKV_ERR_INCONSISTENT = -7
 PKV_F32 = 0
 PKV_BF16 = 1
+PKV_E4M3 = 2
 PKV_ATTN_PHASE_CONSISTENT = 1
 
 
@@ -455,8 +456,9 @@ def copy_blocks(pairs, k_cache, v_cache, workspace=None, stream=None) -> None:
     need = (8 * n + 255) // 256 * 256
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=k_cache.device)
+    dt = PKV_E4M3 if k_cache.dtype == torch.uint8 else _dtype_code(k_cache)
     _check(lib().pkv_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), _ptr(pr), n, nb, bs, hkv,
-                                 d, _dtype_code(k_cache), workspace.data_ptr(),
+                                 d, dt, workspace.data_ptr(),
                                  workspace.numel() * workspace.element_size(),
                                  _stream_ptr(k_cache, stream)))
 

@@ -664,11 +664,13 @@ extern "C" int32_t pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* 
                                    int32_t n_pairs, int32_t num_blocks, int32_t block_size,
                                    int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
                                    void* workspace, size_t workspace_bytes, void* stream) {
-  if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID, "copy_blocks: bad dtype");
+  if (!valid_dtype(dtype) && dtype != PKV_E4M3)
+    return fail(PKV_ERR_INVALID, "copy_blocks: dtype must be PKV_F32, PKV_BF16 or PKV_E4M3");
   if (n_pairs < 0 || num_blocks < 0 || block_size <= 0 || num_kv_heads <= 0 || head_dim <= 0)
     return fail(PKV_ERR_INVALID, "copy_blocks: bad sizes");
   const int64_t block_bytes =
-      static_cast<int64_t>(block_size) * num_kv_heads * head_dim * elem_bytes(dtype);
+      static_cast<int64_t>(block_size) * num_kv_heads * head_dim *
+      (dtype == PKV_E4M3 ? 1 : elem_bytes(dtype));
   if (block_bytes % 16 != 0)
     return fail(PKV_ERR_UNSUPPORTED, "copy_blocks: block bytes must be a multiple of 16");
   if (n_pairs == 0) return ok();

@@ -316,6 +316,15 @@ def test_copy_blocks_validation():
     assert call([1, 2], n=0) == L.PKV_OK                    # nothing to copy
     assert lib.pkv_copy_blocks(F, F, L._ptr(pairs), 1, 8, 1, 1, 4, L.PKV_BF16, F, 256,
                                None) == L.PKV_ERR_UNSUPPORTED   # 8-byte blocks
+    # E4M3 pools: one-byte elements (a 4-code block is too small; a 16-code block passes the
+    # type and size checks and stops at the 8-byte workspace)
+    assert lib.pkv_copy_blocks(F, F, L._ptr(pairs), 1, 8, 1, 1, 4, L.PKV_E4M3, F, 256,
+                               None) == L.PKV_ERR_UNSUPPORTED
+    assert lib.pkv_copy_blocks(F, F, L._ptr(pairs), 1, 8, 1, 1, 16, L.PKV_E4M3, F, 4,
+                               None) == L.PKV_ERR_INVALID
+    assert b"workspace" in lib.pkv_last_error()
+    # the other entry points do not take PKV_E4M3
+    assert lib.pkv_write_kv(F, F, F, 4, F, F, 4, 16, 2, 128, L.PKV_E4M3, None) == L.PKV_ERR_INVALID
 
 
 def test_write_kv_fp8_validation():

@@ -11,14 +11,16 @@ import numpy as np
 import pytest
 
 import prefill_slot_mapping_amd as pkv
+from oracle.fp8 import dequantize, quantize_rows
 from oracle.paged import attend_rows
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-TOL = {"bf16": 2e-3, "f32": 1e-5}
+TOL = {"bf16": 2e-3, "f32": 1e-5, "e4m3": 2e-3}
 HQ, HKV, D, SCALE = 8, 2, 64, 0.125
+K_SCALE, V_SCALE = 1 / 40, 1 / 48      # E4M3 pools: the rows are bf16, the pools their codes
 
 
 def _bf16_round(a):
@@ -57,16 +59,24 @@ class Tokens:
 def _kv(key, dt):
     r = np.random.default_rng([*key, 1])
     k, v = r.standard_normal((HKV, D)).astype(np.float32), r.standard_normal((HKV, D)).astype(np.float32)
-    return (_bf16_round(k), _bf16_round(v)) if dt == "bf16" else (k, v)
+    return (_bf16_round(k), _bf16_round(v)) if dt != "f32" else (k, v)
+
+
+def _kv_stored(key, dt):
+    """The values a pool holds for a token: E4M3 pools hold codes of the bf16 rows."""
+    k, v = _kv(key, dt)
+    if dt == "e4m3":
+        return dequantize(quantize_rows(k, K_SCALE), K_SCALE), dequantize(quantize_rows(v, V_SCALE), V_SCALE)
+    return k, v
 
 
 def _q(sid, pos, dt):
     q = np.random.default_rng([sid, pos, 2]).standard_normal((HQ, D)).astype(np.float32)
-    return _bf16_round(q) if dt == "bf16" else q
+    return _bf16_round(q) if dt != "f32" else q
 
 
 def _dense(tok, sid, pos, dt):
-    kv = [_kv(tok.key(sid, j), dt) for j in range(pos + 1)]
+    kv = [_kv_stored(tok.key(sid, j), dt) for j in range(pos + 1)]
     kc = np.stack([x[0] for x in kv], axis=1)
     vc = np.stack([x[1] for x in kv], axis=1)
     return attend_rows(_q(sid, pos, dt)[None], kc, vc, np.array([pos]), SCALE)[0]
@@ -74,11 +84,15 @@ def _dense(tok, sid, pos, dt):
 
 def _engine(dt, bs, chunk, budget, nb, share, steps, seed):
     rng = np.random.default_rng(seed)
-    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
     mb = 64 // bs
     sched = pkv.Scheduler(nb, bs, chunk, budget, 6, mb, share)
-    kc = torch.full((nb, bs, HKV, D), float("nan"), dtype=tdt, device=DEV)
-    vc = torch.full((nb, bs, HKV, D), float("nan"), dtype=tdt, device=DEV)
+    if dt == "e4m3":
+        kc = torch.full((nb, bs, HKV, D), 0x7F, dtype=torch.uint8, device=DEV)
+        vc = torch.full((nb, bs, HKV, D), 0x7F, dtype=torch.uint8, device=DEV)
+    else:
+        kc = torch.full((nb, bs, HKV, D), float("nan"), dtype=tdt, device=DEV)
+        vc = torch.full((nb, bs, HKV, D), float("nan"), dtype=tdt, device=DEV)
     tok = Tokens()
     reqs = [(0, 11, 3), (1, 11, 3), (2, 7, -1), (3, 37, 3), (4, 2, -1), (5, 9, -1), (6, 37, 3)]
     for sid, plen, grp in reqs:
@@ -124,10 +138,13 @@ def _engine(dt, bs, chunk, budget, nb, share, steps, seed):
             bt = np.full((len(p.seq_ids), mb), -1, np.int32)
             for b, tab in enumerate(p.block_tables):
                 bt[b, :len(tab)] = tab
-            out = pkv.write_kv_attention(
-                torch.from_numpy(q).to(DEV, tdt), torch.from_numpy(kn).to(DEV, tdt),
-                torch.from_numpy(vn).to(DEV, tdt), np.asarray(p.slots, np.int32), kc, vc,
-                torch.from_numpy(bt).to(DEV), p.ctx_lens, p.cu_seqlens, SCALE, workspace=ws)
+            args = (torch.from_numpy(q).to(DEV, tdt), torch.from_numpy(kn).to(DEV, tdt),
+                    torch.from_numpy(vn).to(DEV, tdt), np.asarray(p.slots, np.int32), kc, vc,
+                    torch.from_numpy(bt).to(DEV), p.ctx_lens, p.cu_seqlens, SCALE)
+            if dt == "e4m3":
+                out = pkv.write_kv_attention_fp8(*args, K_SCALE, V_SCALE, workspace=ws)
+            else:
+                out = pkv.write_kv_attention(*args, workspace=ws)
             got = out.cpu().numpy().astype(np.float64)
             for t, (sid, pos, pre_row) in enumerate(rows):
                 err = float(np.abs(got[t] - _dense(tok, sid, pos, dt)).max())
@@ -141,7 +158,7 @@ def _engine(dt, bs, chunk, budget, nb, share, steps, seed):
     return st
 
 
-@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("dt", ["bf16", "f32", "e4m3"])
 @pytest.mark.parametrize("cfg", [dict(bs=4, chunk=16, budget=24, nb=30, share=True),
                                  dict(bs=16, chunk=40, budget=64, nb=9, share=True),
                                  dict(bs=1, chunk=5, budget=12, nb=120, share=False)],
