@@ -314,6 +314,21 @@ def _decode_roofline(res, name, kernel):
                            "achieved": res["decode_kv_bytes"] / (cms * 1e-3) / 1e9 if cms else None}}
 
 
+def _clocks():
+    """Current GPU clocks as rocm-smi reports them (a child process), or None."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
+                           text=True, timeout=30)
+        if r.returncode != 0:
+            return None
+        d = json.loads(r.stdout[r.stdout.index("{"):])
+        card = next(iter(d.values()))
+        return {k: v for k, v in card.items() if "clock" in k.lower() or "level" in k.lower()}
+    except (OSError, ValueError, StopIteration, subprocess.SubprocessError):
+        return None
+
+
 def main():
     args = _parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -353,6 +368,7 @@ def main():
 
     roofline = _decode_roofline(main_res, args.workload,
                                 "decode_fp8_kernel" if w.kv_fp8 else "decode_split_kernel")
+    clocks = _clocks()
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_seconds)
@@ -369,6 +385,7 @@ def main():
                    "cached_tokens": int(w.ctx_lens.sum()), "parallelism": "single-gpu"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "gpu_clocks_after_timing": clocks,
         "detail": main_res,
         "extra": extra,
     }
