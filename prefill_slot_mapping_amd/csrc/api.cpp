@@ -13,6 +13,7 @@
 #include <cmath>
 #include <cstring>
 #include <deque>
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <unordered_map>
@@ -169,8 +170,9 @@ struct ProfRecord {
   hipEvent_t a, b;
 };
 std::mutex g_prof_mu;
-bool g_prof_on = false;
-uint32_t g_prof_kinds = 0xFu;  // kernel kinds bracketed while profiling is on
+// read without the lock on every launch (the fast path when profiling is off)
+std::atomic<bool> g_prof_on{false};
+std::atomic<uint32_t> g_prof_kinds{0xFu};  // kernel kinds bracketed while profiling is on
 std::vector<ProfRecord> g_prof_pending;
 std::vector<hipEvent_t> g_prof_free;
 double g_prof_ms[4] = {0, 0, 0, 0};
@@ -189,7 +191,9 @@ hipEvent_t prof_event() {
 
 // Records the opening event of a launch of `kind`; returns the record index or -1.
 int prof_begin(int kind, hipStream_t s) {
-  if (!g_prof_on || ((g_prof_kinds >> kind) & 1u) == 0) return -1;
+  if (!g_prof_on.load(std::memory_order_relaxed) ||
+      ((g_prof_kinds.load(std::memory_order_relaxed) >> kind) & 1u) == 0)
+    return -1;
   std::lock_guard<std::mutex> lk(g_prof_mu);
   ProfRecord r{kind, prof_event(), prof_event()};
   if (r.a == nullptr || r.b == nullptr) return -1;
@@ -857,7 +861,7 @@ extern "C" int32_t pkv_write_kv_attention_fp8(
 extern "C" int32_t pkv_profile_set_kinds(uint32_t kinds) {
   if ((kinds & ~0xFu) != 0) return fail(PKV_ERR_INVALID, "profile_set_kinds: unknown kind bits");
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  g_prof_kinds = kinds;
+  g_prof_kinds.store(kinds, std::memory_order_relaxed);
   return ok();
 }
 
@@ -875,7 +879,7 @@ extern "C" int32_t pkv_profile_enable(int32_t enable) {
       g_prof_n[k] = 0;
     }
   }
-  g_prof_on = enable != 0;
+  g_prof_on.store(enable != 0, std::memory_order_relaxed);
   return ok();
 }
 
