@@ -303,8 +303,9 @@ int32_t pkv_attention_ex(const void* q, const void* k_cache, const void* v_cache
  *      [T, H, D]] -----------------------------------------------------------------------
  * Same result as pkv_write_kv(k_new, v_new, <slots>, n_rows, k_cache, v_cache, ...) followed
  * by pkv_attention_ex(..., flags, ...) on the same stream, but the slots are read from host
- * memory and travel to the device in the same host-to-device copy as the attention work lists
- * (one copy per step instead of two).
+ * memory: they are staged with the attention work lists in the library's pinned buffer, and
+ * one launch copies the lists to the workspace and appends the rows, reading the slots from
+ * the pinned buffer in place (no separate host-to-device copy).
  *   slots_host:   host int32 [n_rows]; row t of k_new / v_new ([n_rows, num_kv_heads,
  *                 head_dim], device, dtype) goes to slot slots_host[t]. A negative slot skips
  *                 its row; a slot >= num_blocks * block_size is PKV_ERR_INVALID (checked before

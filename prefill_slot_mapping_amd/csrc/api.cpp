@@ -37,18 +37,20 @@ bool misaligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u)
 bool valid_dtype(int32_t dt) { return dt == PKV_F32 || dt == PKV_BF16; }
 int elem_bytes(int32_t dt) { return dt == PKV_BF16 ? 2 : 4; }
 
-// ---- pinned staging ring: work lists are built on the host and copied asynchronously ----
-// A ring of pinned buffers per device. Slot n % kRingSlots holds the data of call n until its
-// host-to-device copy has run; before the host rewrites a slot it waits for a fence (an event
-// recorded on the stream of the slot's previous copy) that covers that copy. Fences are
-// recorded every kFenceEvery calls, not every call: each event record costs the stream a few
-// microseconds. A copy left uncovered because its stream was not used again before the slot
-// came round is waited for with a device synchronisation.
+// ---- pinned staging ring: work lists are built on the host and read by the device ----------
+// A ring of pinned buffers per device. Slot n % kRingSlots holds the data of call n until the
+// device work that reads it (a host-to-device copy, or the fused append launch, which reads the
+// buffer in place through its device mapping) has run; before the host rewrites a slot it
+// waits for a fence (an event recorded on the stream of the slot's previous reader) that
+// covers that work. Fences are recorded every kFenceEvery calls, not every call: each event
+// record costs the stream a few microseconds. A reader left uncovered because its stream was
+// not used again before the slot came round is waited for with a device synchronisation.
 constexpr int kRingSlots = 16;
 constexpr int kFenceEvery = 4;
 
 struct StagingSlot {
   void* host = nullptr;
+  void* dev = nullptr;          // device mapping of host (kernels read it in place)
   size_t cap = 0;
   int64_t call = -1;            // call whose copy last read this slot (-1: none)
   hipStream_t stream = nullptr; // the stream of that copy
@@ -129,8 +131,11 @@ hipError_t record_fence(DeviceRing* r, hipStream_t stream, int64_t covers) {
 
 // Copies `bytes` of host-built data to device memory dst on stream strm through the current
 // device's staging ring; fill(host) writes the data into the staging buffer.
-template <typename Fill>
-int32_t stage_and_copy(void* dst, size_t bytes, hipStream_t strm, const char* what, Fill fill) {
+// Stages `bytes` of host-built data in the current device's ring (fill(host) writes them) and
+// enqueues run(dev) on strm, the device work that reads them (through the device mapping dev of
+// the staging buffer, or with a copy); run returns a status.
+template <typename Fill, typename Run>
+int32_t stage_and_run(size_t bytes, hipStream_t strm, const char* what, Fill fill, Run run) {
   int dev = 0;
   DeviceRing* ring = ring_for_current_device(&dev);
   if (ring == nullptr) return fail(PKV_ERR_HIP, std::string(what) + ": hipGetDevice failed");
@@ -149,19 +154,37 @@ int32_t stage_and_copy(void* dst, size_t bytes, hipStream_t strm, const char* wh
     const size_t want = std::max<size_t>(bytes, 1 << 16);
     hipError_t e = hipHostMalloc(&slot.host, want, hipHostMallocDefault);
     if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string(what) + ": pinned staging: " + hipGetErrorString(e));
+    e = hipHostGetDevicePointer(&slot.dev, slot.host, 0);
+    if (e != hipSuccess) {
+      (void)hipHostFree(slot.host);
+      slot.host = nullptr;
+      slot.dev = nullptr;
+      return fail(PKV_ERR_HIP, std::string(what) + ": staging mapping: " + hipGetErrorString(e));
+    }
     slot.cap = want;
   }
   fill(static_cast<char*>(slot.host));
-  hipError_t e = hipMemcpyAsync(dst, slot.host, bytes, hipMemcpyHostToDevice, strm);
-  if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string(what) + ": list copy: " + hipGetErrorString(e));
+  const int32_t rs = run(static_cast<const char*>(slot.host), static_cast<const char*>(slot.dev));
+  if (rs != PKV_OK) return rs;
   ring->calls = call + 1;
   slot.call = call;
   slot.stream = strm;
   if (call % kFenceEvery == kFenceEvery - 1) {
-    e = record_fence(ring, strm, call);
+    const hipError_t e = record_fence(ring, strm, call);
     if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string(what) + ": fence: " + hipGetErrorString(e));
   }
   return PKV_OK;
+}
+
+// Copies `bytes` of host-built data to device memory dst on stream strm through the current
+// device's staging ring; fill(host) writes the data into the staging buffer.
+template <typename Fill>
+int32_t stage_and_copy(void* dst, size_t bytes, hipStream_t strm, const char* what, Fill fill) {
+  return stage_and_run(bytes, strm, what, fill, [&](const char* host, const char*) -> int32_t {
+    hipError_t e = hipMemcpyAsync(dst, host, bytes, hipMemcpyHostToDevice, strm);
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string(what) + ": list copy: " + hipGetErrorString(e));
+    return PKV_OK;
+  });
 }
 
 // ---- diagnostics: event pairs around launches -------------------------------------------
@@ -521,22 +544,38 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
 
   // work lists (and fused-append slots) -> pinned staging -> workspace, one async copy ordered
   // before the kernels
-  if (L.list_bytes > 0) {
-    st = stage_and_copy(ws, L.list_bytes, strm, "attention", [&](char* host) {
-      build_lists(s, L, host);
-      if (n_write > 0) std::memcpy(host + L.slots_off, slots_host, sizeof(int32_t) * n_write);
+  const auto fill = [&](char* host) {
+    build_lists(s, L, host);
+    if (n_write > 0) std::memcpy(host + L.slots_off, slots_host, sizeof(int32_t) * n_write);
+  };
+  if (n_write > 0) {
+    // one launch copies the work lists (bytes [0, slots_off) of the staging buffer) to the
+    // workspace and appends the rows, reading their slots from the staging buffer in place
+    st = stage_and_run(L.list_bytes, strm, "write_kv_attention", fill,
+                       [&](const char*, const char* dev) -> int32_t {
+      pkv::StageArgs sa;
+      sa.src = reinterpret_cast<const uint4*>(dev);
+      sa.dst = reinterpret_cast<uint4*>(ws);
+      sa.n_u4 = static_cast<int32_t>(L.slots_off / 16);
+      sa.copy_blocks = static_cast<int32_t>(std::min<size_t>((L.slots_off / 16 + 255) / 256, 64));
+      const int32_t* slots_staged = reinterpret_cast<const int32_t*>(dev + L.slots_off);
+      const int pr = prof_begin(0, strm);
+      hipError_t e;
+      if (wr != nullptr) {
+        wr->slots = slots_staged;
+        e = pkv::launch_stage_write_kv(sa, *wr, strm);
+      } else {
+        wr8->slots = slots_staged;
+        e = pkv::launch_stage_write_kv_fp8(sa, *wr8, strm);
+      }
+      prof_end(pr, strm);
+      if (e != hipSuccess)
+        return fail(PKV_ERR_HIP, std::string("write_kv launch: ") + hipGetErrorString(e));
+      return PKV_OK;
     });
     if (st != PKV_OK) return st;
-  }
-  if (n_write > 0) {
-    const int32_t* slots_dev = reinterpret_cast<const int32_t*>(ws + L.slots_off);
-    if (wr != nullptr) {
-      wr->slots = slots_dev;
-      st = launch_write(*wr, strm);
-    } else {
-      wr8->slots = slots_dev;
-      st = launch_write_fp8(*wr8, strm);
-    }
+  } else if (L.list_bytes > 0) {
+    st = stage_and_copy(ws, L.list_bytes, strm, "attention", fill);
     if (st != PKV_OK) return st;
   }
   if (T == 0) return ok();

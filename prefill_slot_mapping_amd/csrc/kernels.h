@@ -21,6 +21,15 @@ struct WriteArgs {
   void* v_cache;
 };
 
+// Work lists staged in pinned host memory, copied to the workspace by the first blocks of a
+// fused append launch (src is the device mapping of the staging buffer).
+struct StageArgs {
+  const uint4* src;
+  uint4* dst;
+  int32_t n_u4;         // 16-byte chunks to copy
+  int32_t copy_blocks;  // blocks [0, copy_blocks) copy; the others append
+};
+
 struct CopyArgs {
   void* k_cache;
   void* v_cache;
@@ -98,6 +107,10 @@ struct PrefillArgs {
 hipError_t launch_write_kv(const WriteArgs& a, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
 hipError_t launch_write_kv_fp8(const WriteFp8Args& a, hipStream_t stream);
+// The copy of st and the append of a in one launch; a.slots may point into st.src's memory.
+hipError_t launch_stage_write_kv(const StageArgs& st, const WriteArgs& a, hipStream_t stream);
+hipError_t launch_stage_write_kv_fp8(const StageArgs& st, const WriteFp8Args& a,
+                                     hipStream_t stream);
 hipError_t launch_decode_fp8(const DecodeArgs& a, int64_t n_items, int head_dim, int group,
                              hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int64_t n_items, int head_dim, int group,

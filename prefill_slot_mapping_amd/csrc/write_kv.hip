@@ -16,14 +16,15 @@ namespace pkv {
 // KV append: row t of k_new / v_new goes to slot slots[t]; a slot row is contiguous in the
 // [num_blocks, block_size, Hkv, D] pool at byte offset slot * Hkv * D * elem_bytes.
 // ---------------------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) write_kv_kernel(WriteArgs a) {
+__device__ __forceinline__ void write_kv_chunks(const WriteArgs& a, uint32_t first,
+                                                uint32_t stride) {
   const uint4* __restrict__ kn = static_cast<const uint4*>(a.k_new);
   const uint4* __restrict__ vn = static_cast<const uint4*>(a.v_new);
   uint4* __restrict__ kc = static_cast<uint4*>(a.k_cache);
   uint4* __restrict__ vc = static_cast<uint4*>(a.v_cache);
   const uint32_t chunks = static_cast<uint32_t>(a.chunks_per_row);
   const uint32_t total = static_cast<uint32_t>(a.n_rows) * chunks;
-  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < total; i += gridDim.x * 256u) {
+  for (uint32_t i = first; i < total; i += stride) {
     const uint32_t row = i / chunks;
     const uint32_t c = i - row * chunks;
     const int32_t s = a.slots[row];
@@ -32,6 +33,10 @@ __global__ void __launch_bounds__(256) write_kv_kernel(WriteArgs a) {
     kc[dst] = kn[i];
     vc[dst] = vn[i];
   }
+}
+
+__global__ void __launch_bounds__(256) write_kv_kernel(WriteArgs a) {
+  write_kv_chunks(a, blockIdx.x * 256u + threadIdx.x, gridDim.x * 256u);
 }
 
 hipError_t launch_write_kv(const WriteArgs& a, hipStream_t stream) {
@@ -65,14 +70,15 @@ __device__ __forceinline__ uint4 quant16(uint4 lo, uint4 hi, float inv) {
                     quant4(hi.z, hi.w, inv));
 }
 
-__global__ void __launch_bounds__(256) write_kv_fp8_kernel(WriteFp8Args a) {
+__device__ __forceinline__ void write_kv_fp8_chunks(const WriteFp8Args& a, uint32_t first,
+                                                    uint32_t stride) {
   const uint4* __restrict__ kn = static_cast<const uint4*>(a.k_new);
   const uint4* __restrict__ vn = static_cast<const uint4*>(a.v_new);
   uint4* __restrict__ kc = static_cast<uint4*>(a.k_cache);
   uint4* __restrict__ vc = static_cast<uint4*>(a.v_cache);
   const uint32_t chunks = static_cast<uint32_t>(a.chunks_per_row);
   const uint32_t total = static_cast<uint32_t>(a.n_rows) * chunks;
-  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < total; i += gridDim.x * 256u) {
+  for (uint32_t i = first; i < total; i += stride) {
     const uint32_t row = i / chunks;
     const uint32_t c = i - row * chunks;
     const int32_t s = a.slots[row];
@@ -81,6 +87,58 @@ __global__ void __launch_bounds__(256) write_kv_fp8_kernel(WriteFp8Args a) {
     kc[dst] = quant16(kn[2 * i], kn[2 * i + 1], a.k_inv_scale);
     vc[dst] = quant16(vn[2 * i], vn[2 * i + 1], a.v_inv_scale);
   }
+}
+
+__global__ void __launch_bounds__(256) write_kv_fp8_kernel(WriteFp8Args a) {
+  write_kv_fp8_chunks(a, blockIdx.x * 256u + threadIdx.x, gridDim.x * 256u);
+}
+
+// ---------------------------------------------------------------------------------------
+// Fused staging + append: blocks [0, copy_blocks) copy the step's work lists from the pinned
+// staging buffer (read through its device mapping) into the workspace; the other blocks
+// scatter the new rows, reading each row's slot from the same staging buffer. One launch
+// instead of a host-to-device copy followed by the append.
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ bool stage_copy(const StageArgs& st) {
+  if (static_cast<int32_t>(blockIdx.x) >= st.copy_blocks) return false;
+  const uint32_t stride = static_cast<uint32_t>(st.copy_blocks) * 256u;
+  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < static_cast<uint32_t>(st.n_u4);
+       i += stride)
+    st.dst[i] = st.src[i];
+  return true;
+}
+
+__global__ void __launch_bounds__(256) stage_write_kv_kernel(StageArgs st, WriteArgs a) {
+  if (stage_copy(st)) return;
+  const uint32_t b = blockIdx.x - static_cast<uint32_t>(st.copy_blocks);
+  write_kv_chunks(a, b * 256u + threadIdx.x, (gridDim.x - st.copy_blocks) * 256u);
+}
+
+__global__ void __launch_bounds__(256) stage_write_kv_fp8_kernel(StageArgs st, WriteFp8Args a) {
+  if (stage_copy(st)) return;
+  const uint32_t b = blockIdx.x - static_cast<uint32_t>(st.copy_blocks);
+  write_kv_fp8_chunks(a, b * 256u + threadIdx.x, (gridDim.x - st.copy_blocks) * 256u);
+}
+
+static uint32_t append_blocks(int64_t total) {
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  return static_cast<uint32_t>(blocks < 1 ? 1 : blocks);
+}
+
+hipError_t launch_stage_write_kv(const StageArgs& st, const WriteArgs& a, hipStream_t stream) {
+  const uint32_t nb = append_blocks(static_cast<int64_t>(a.n_rows) * a.chunks_per_row);
+  hipLaunchKernelGGL(stage_write_kv_kernel, dim3(st.copy_blocks + nb), dim3(256), 0, stream, st,
+                     a);
+  return hipGetLastError();
+}
+
+hipError_t launch_stage_write_kv_fp8(const StageArgs& st, const WriteFp8Args& a,
+                                     hipStream_t stream) {
+  const uint32_t nb = append_blocks(static_cast<int64_t>(a.n_rows) * a.chunks_per_row);
+  hipLaunchKernelGGL(stage_write_kv_fp8_kernel, dim3(st.copy_blocks + nb), dim3(256), 0, stream,
+                     st, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_write_kv_fp8(const WriteFp8Args& a, hipStream_t stream) {
