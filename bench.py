@@ -224,11 +224,13 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
     res["roofline_frac_step"] = t_roof / (ms_step * 1e-3)
     res["_gst"] = gst
     res["_w"] = w
+    res["_out"] = out
     return res
 
 
-def cpu_baseline(w, budget_s):
-    """The oracle as it stands, on a bounded sample of the same workload's decode rows."""
+def cpu_baseline(w, budget_s, gpu_out=None):
+    """The oracle as it stands, on a bounded sample of the same workload's rows; with gpu_out
+    (the last timed step's output) the sampled rows are also compared with the GPU's."""
     import numpy as np
     from oracle import build_oracle_step
     try:
@@ -262,7 +264,7 @@ def cpu_baseline(w, budget_s):
     reps = 0
     t = time.perf_counter()
     while True:
-        st.attention(rows=rows)
+        ref = st.attention(rows=rows)
         reps += 1
         spent = time.perf_counter() - t
         if spent >= 0.66 * budget_s or spent / reps * (reps + 1) > budget_s:
@@ -272,9 +274,14 @@ def cpu_baseline(w, budget_s):
     sample = f"{len(chosen)} of {w.B} sequences ({len(rows)} query rows, " \
              f"{int(w.ctx_lens[chosen].sum())} cached tokens) x {reps} passes, float64 " \
              f"per-row oracle"
+    parity = None
+    if gpu_out is not None:
+        got = gpu_out[rows].detach().cpu().numpy().astype(np.float64)
+        parity = {"rows": len(rows), "max_abs_err": float(np.abs(got - ref[rows]).max()),
+                  "tolerance": 2e-3 if w.spec.dtype == "bf16" else 1e-5}
     return {"value": kv_done / spent / 1e9, "unit": "GB/s", "cores": int(blas_threads),
             "kind": "oracle", "sample": sample, "seconds": spent,
-            "affinity_cores": len(os.sched_getaffinity(0))}
+            "affinity_cores": len(os.sched_getaffinity(0)), "parity_vs_gpu": parity}
 
 
 def _traffic_for(workload):
@@ -355,14 +362,14 @@ def main():
         if r["decode_kv_bytes"] and not (r["_w"].q_lens > 1).any():
             r["roofline"] = _decode_roofline(r, name, "decode_fp8_kernel" if r["_w"].kv_fp8
                                              else "decode_split_kernel")
-        r.pop("_gst"); r.pop("_w")
+        r.pop("_gst"); r.pop("_w"); r.pop("_out")
         extra[name] = r
         torch.cuda.empty_cache()
 
     for name in [n for n in args.consistent.split(",") if n]:
         r = time_workload(name, args.steps, args.warmup, phase_consistent=True,
                           kernel_events=args.kernel_events)
-        r.pop("_gst"); r.pop("_w")
+        r.pop("_gst"); r.pop("_w"); r.pop("_out")
         extra[name + "/phase-consistent"] = r
         torch.cuda.empty_cache()
 
@@ -371,9 +378,10 @@ def main():
     clocks = _clocks()
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, args.cpu_seconds)
+        cpu = cpu_baseline(w, args.cpu_seconds, main_res["_out"])
     main_res.pop("_gst")
     main_res.pop("_w")
+    main_res.pop("_out")
     s = w.spec
     line = {
         "metric": "paged decode KV GB/s (% HBM peak); mixed ragged step tokens/s",
