@@ -203,6 +203,8 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
     kv = _kv_bytes(w)
     app = acc.append_bytes(w.T, s.Hkv, s.D, w.elem_bytes, w.kv_elem_bytes)
     decode_rows = w.q_lens == 1
+    decode_only = bool((w.q_lens <= 1).all())
+    uq = acc.unique_kv_bytes(gst.block_tables, w.ctx_lens, s.BS, s.Hkv, s.D, w.kv_elem_bytes)
     dec_kv = acc.decode_kv_bytes(w.ctx_lens[decode_rows], s.Hkv, s.D, w.kv_elem_bytes)
     flops = acc.attention_flops(w.ctx_lens[~decode_rows], w.q_lens[~decode_rows], s.Hq, s.D)
     res = {
@@ -211,6 +213,11 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
         "ms_per_step": ms_step,
         "step_gbs": (kv + app) / (ms_step * 1e-3) / 1e9, "tokens_per_s": w.T / (ms_step * 1e-3),
         "kv_bytes": kv, "append_bytes": app, "decode_kv_bytes": dec_kv, "prefill_flops": flops,
+        # distinct cached bytes (a block shared by several sequences counted once) and, for
+        # decode-only steps, the rate they give over the decode kernel's time
+        "unique_kv_bytes": uq,
+        "decode_unique_gbs": (uq / (kern["decode"][0] / kern["decode"][1] * 1e-3) / 1e9
+                              if decode_only and kern["decode"][1] else None),
         "build_s": t_build,
         "host_enqueue_ms": {"median": float(np.median(host_ms)), "max": float(host_ms.max())},
         "gc_pauses_in_timed_region": {"count": len(gc_pauses),
