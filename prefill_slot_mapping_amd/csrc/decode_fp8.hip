@@ -339,7 +339,7 @@ static hipError_t launch_fp8_d(const DecodeArgs& a, uint32_t grid, int group,
   switch (group) {
     case 1: hipLaunchKernelGGL((decode_fp8_kernel<D, 1, 32, 3, 2>), dim3(grid), dim3(256), 0, stream, a); break;
     case 2: hipLaunchKernelGGL((decode_fp8_kernel<D, 2, 32, 3, 2>), dim3(grid), dim3(256), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((decode_fp8_kernel<D, 4, 16, 3, 3>), dim3(grid), dim3(256), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((decode_fp8_kernel<D, 4, 16, 4, 3>), dim3(grid), dim3(256), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
