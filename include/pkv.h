@@ -13,8 +13,9 @@
  *         batch independence).
  *
  * Conventions for every entry point
- *   - Returns PKV_OK (0) or a negative status; pkv_last_error() then gives a message (per
- *     thread, valid until the next failing call on that thread).
+ *   - Returns PKV_OK (0) or a negative status; pkv_last_error() then gives a message. The
+ *     message is kept per thread: the next call on that thread that fails replaces it and a
+ *     call that succeeds may clear it, so read (or copy) it right after the failure.
  *   - Arguments are validated on the host before anything happens: on any error nothing is
  *     launched, nothing is copied and no allocator state changes.
  *   - No exception crosses the ABI. No entry point allocates device memory: device buffers
