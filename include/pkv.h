@@ -19,10 +19,17 @@
  *   - Arguments are validated on the host before anything happens: on any error nothing is
  *     launched, nothing is copied and no allocator state changes.
  *   - No exception crosses the ABI. No entry point allocates device memory: device buffers
- *     are owned by the caller; the library owns only allocator handles and a small ring of
- *     pinned host staging buffers for work lists.
+ *     are owned by the caller; the library owns only allocator handles, a small ring of
+ *     pinned host staging buffers for work lists and, per device, one stream and two events.
  *   - Device work is enqueued on the caller's stream (a hipStream_t passed as void*; NULL is
- *     the default stream) and is asynchronous with respect to the host.
+ *     the default stream) and is asynchronous with respect to the host. An attention step with
+ *     a large prefill pass (over 512 workgroups: the segments' tiles of 128 / group query
+ *     rows, times num_kv_heads) and a large decode pass (at least 1024 workgroups: the decode
+ *     rows' KV splits, times num_kv_heads) enqueues its decode pass on the library's stream,
+ *     forked from the caller's stream after the step's append and joined back to it before
+ *     the call returns: work enqueued later on the caller's stream sees the whole result, and
+ *     the output bits are those of the unforked path. Such calls from several threads on one
+ *     device serialise their decode passes on that stream.
  *   - Element type codes: PKV_F32 (float32) and PKV_BF16 (bfloat16). q, k_new, v_new and both
  *     pools share one element type; attention output is always float32.
  */

@@ -187,6 +187,45 @@ int32_t stage_and_copy(void* dst, size_t bytes, hipStream_t strm, const char* wh
   });
 }
 
+// ---- second stream: a large mixed step's decode pass runs beside its prefill pass -------
+// Launched after the prefill pass on one stream, the decode pass cannot start until the last
+// prefill workgroup has ended, and the prefill grid leaves more and more compute units idle as
+// its shortest items finish. A mixed step with a large prefill grid (more than two workgroups
+// per compute unit, so that such a tail exists) and a large decode pass therefore forks: after
+// the append, the prefill pass is enqueued first on the caller's stream, then the decode pass
+// and its merge on a library-owned stream (one per device, default priority) that waits for
+// the caller's stream; the caller's stream waits for them before anything enqueued after the
+// call. The decode workgroups then fill compute units as prefill workgroups leave. Below the
+// thresholds the two event records and waits cost more than the overlap gains. Enqueueing the
+// fork and the join holds a per-device lock, so the events are never re-recorded in between.
+// Kernels, work lists and outputs are the same either way, so no output bit depends on it.
+constexpr int64_t kForkMinPrefillWgs = 512;
+constexpr int64_t kForkMinDecodeWgs = 1024;
+struct SideStream {
+  std::mutex mu;
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+std::unordered_map<int, SideStream*> g_side;
+
+SideStream* side_for_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  auto it = g_side.find(dev);
+  if (it != g_side.end()) return it->second;
+  SideStream* ss = new SideStream();
+  if (hipStreamCreateWithFlags(&ss->s, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&ss->fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&ss->join, hipEventDisableTiming) != hipSuccess) {
+    delete ss;
+    return nullptr;
+  }
+  g_side[dev] = ss;
+  return ss;
+}
+
 // ---- diagnostics: event pairs around launches -------------------------------------------
 struct ProfRecord {
   int kind;
@@ -593,6 +632,21 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
   float* part_l = reinterpret_cast<float*>(ws + L.part_l_off);
   float* part_acc = reinterpret_cast<float*>(ws + L.part_acc_off);
 
+  // a large mixed step forks its decode pass (and merge) onto the second stream
+  const bool fork = L.n_prefill * num_kv_heads > kForkMinPrefillWgs &&
+                    L.n_decode * num_kv_heads >= kForkMinDecodeWgs;
+  SideStream* side = nullptr;
+  std::unique_lock<std::mutex> side_lock;
+  hipStream_t dstrm = strm;
+  if (fork) {
+    side = side_for_current_device();
+    if (side == nullptr) return fail(PKV_ERR_HIP, "attention: second stream set-up failed");
+    side_lock = std::unique_lock<std::mutex>(side->mu);
+    hipError_t e = hipEventRecord(side->fork, strm);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("attention: fork: ") + hipGetErrorString(e));
+    dstrm = side->s;
+  }
   if (L.n_prefill > 0) {
     pkv::PrefillArgs p;
     p.q = q;
@@ -638,11 +692,11 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
     d.part_m = part_m;
     d.part_l = part_l;
     d.part_acc = part_acc;
-    const int pr = prof_begin(2, strm);
+    const int pr = prof_begin(2, dstrm);
     hipError_t e = fp8_scales != nullptr
-                       ? pkv::launch_decode_fp8(d, L.n_decode, head_dim, group, strm)
-                       : pkv::launch_decode(d, L.n_decode, head_dim, group, dtype == PKV_BF16, strm);
-    prof_end(pr, strm);
+                       ? pkv::launch_decode_fp8(d, L.n_decode, head_dim, group, dstrm)
+                       : pkv::launch_decode(d, L.n_decode, head_dim, group, dtype == PKV_BF16, dstrm);
+    prof_end(pr, dstrm);
     if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("decode launch: ") + hipGetErrorString(e));
   }
   if (L.n_merge > 0) {
@@ -654,10 +708,15 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
     mg.part_l = part_l;
     mg.part_acc = part_acc;
     mg.out = out;
-    const int pr = prof_begin(3, strm);
-    hipError_t e = pkv::launch_merge(mg, L.n_merge, head_dim, strm);
-    prof_end(pr, strm);
+    const int pr = prof_begin(3, dstrm);
+    hipError_t e = pkv::launch_merge(mg, L.n_merge, head_dim, dstrm);
+    prof_end(pr, dstrm);
     if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("merge launch: ") + hipGetErrorString(e));
+  }
+  if (fork) {
+    hipError_t e = hipEventRecord(side->join, dstrm);
+    if (e == hipSuccess) e = hipStreamWaitEvent(strm, side->join, 0);
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("attention: join: ") + hipGetErrorString(e));
   }
   return ok();
 }
