@@ -329,11 +329,17 @@ def _decode_roofline(res, name, kernel):
 
 
 def _clocks():
-    """Current GPU clocks as rocm-smi reports them (a child process), or None."""
+    """Current GPU clocks as rocm-smi reports them (a child process), or None. The script is
+    handed to this interpreter directly: its `#!/usr/bin/env` line would make the child replace
+    itself once more, which profilers that set up the GPU in every process do not allow."""
+    import shutil
     import subprocess
+    smi = shutil.which("rocm-smi")
+    if smi is None:
+        return None
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
-                           text=True, timeout=30)
+        r = subprocess.run([sys.executable, os.path.realpath(smi), "--showclocks", "--json"],
+                           capture_output=True, text=True, timeout=30)
         if r.returncode != 0:
             return None
         d = json.loads(r.stdout[r.stdout.index("{"):])

@@ -306,7 +306,11 @@ prefill_kernel(PrefillArgs a) {
     // ---- online softmax for this lane's M-row (keys split with lane ^ 32), base 2 ----
     // Exponents are taken against a reference m_ref that trails the running max by less than
     // kRescaleSlack (p <= 2^slack); O and l are rescaled only when the max rises past it.
-    const bool diag = (kt + 1) * kPrefillKeyTile > wave_first_pos + 1 || !real;
+    // Tiles that cross a row of the wave (and every tile of a wave with unused rows) take the
+    // masked path. The choice is made for the whole wave: on a tile that crosses none of its
+    // rows the mask keeps every key of a used row, so masking there changes no value.
+    const bool diag = __builtin_amdgcn_ballot_w64(
+        (kt + 1) * kPrefillKeyTile > wave_first_pos + 1 || !real) != 0;
     float tmax = -INFINITY;
     if (!diag) {
 #pragma unroll
