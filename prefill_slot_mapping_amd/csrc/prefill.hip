@@ -59,6 +59,12 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
                :: "v"(src), "s"(lds_base) : "memory", "m0");
 }
 
+// As dma16, from the wave-uniform base address sbase plus this lane's 32-bit byte offset voff.
+__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_base) : "memory", "m0");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p))));
@@ -113,7 +119,7 @@ prefill_kernel(PrefillArgs a) {
   __shared__ int s_bad;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int h32 = lane >> 5;
@@ -185,10 +191,32 @@ prefill_kernel(PrefillArgs a) {
   // needs re-read the item's last key (finite data whose p is exactly 0).
   // E4M3 codes of tile kt into staging buffer buf, row-major (code chunk P = chunk P % CPC of
   // key row P / CPC); keys no row needs re-read the item's last key.
+  const uint32_t stride_c = static_cast<uint32_t>(a.hkv * CPC);  // code chunks per slot
+  uint32_t lane_off_c[F8 ? NJC : 1];
+  if constexpr (F8) {
+    static_assert(NJC * 64 / CPC == 16, "a wave copies 16 keys of a tile");
+#pragma unroll
+    for (int j = 0; j < NJC; ++j)
+      lane_off_c[j] = (static_cast<uint32_t>((j * 64 + lane) / CPC) * stride_c + g * CPC +
+                       lane % CPC) * 16u;
+  }
   auto dma_codes = [&](int kt, int buf) {
     const uint4* __restrict__ kc = static_cast<const uint4*>(a.k_cache);
     const uint4* __restrict__ vc = static_cast<const uint4*>(a.v_cache);
-    const uint32_t stride_c = static_cast<uint32_t>(a.hkv * CPC);
+    const int key0 = kt * kPrefillKeyTile + wave * 16;
+    if (a.bs_log2 >= 4 && key0 + 15 <= key_limit - 1) {   // as in dma_tile
+      const int e = key0 >> a.bs_log2;
+      const int blk = __builtin_amdgcn_readfirstlane(s_blk[e - win0]);
+      const uint32_t slot0 = static_cast<uint32_t>(blk) * a.block_size + (key0 - (e << a.bs_log2));
+      const uint64_t base = static_cast<uint64_t>(slot0) * stride_c;
+#pragma unroll
+      for (int j = 0; j < NJC; ++j) {
+        const int cb = (wave * NJC + j) * 64;
+        dma16_s(kc + base, lane_off_c[j], lds_addr(&s_code[buf][0][cb]));
+        dma16_s(vc + base, lane_off_c[j], lds_addr(&s_code[buf][1][cb]));
+      }
+      return;
+    }
     uint64_t off[NJC];
 #pragma unroll
     for (int j = 0; j < NJC; ++j) {
@@ -225,7 +253,37 @@ prefill_kernel(PrefillArgs a) {
     }
   };
 
+  // Each wave copies 16 consecutive keys of a tile (NJ * 64 / CPR rows). With blocks of at
+  // least 16 keys (a power of two) those keys are consecutive slots of one block: one
+  // block-table lookup per tile, a wave-uniform base address and per-lane offsets fixed for the
+  // whole item (chunk position P of the wave's rows, swizzled as below).
+  static_assert(NJ * 64 / CPR == 16, "a wave copies 16 keys of a tile");
+  uint32_t lane_off[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int r = (j * 64 + lane) / CPR;          // key row within the wave's 16
+    const int row = wave * 16 + r;
+    lane_off[j] = (static_cast<uint32_t>(r) * slot_stride + head_off +
+                   ((lane % CPR) ^ swz<CPR>(row))) * 16u;
+  }
+  const bool one_block_rows = a.bs_log2 >= 4;
   auto dma_tile = [&](int kt, int buf) {
+    const int key0 = kt * kPrefillKeyTile + wave * 16;
+    if (one_block_rows && key0 + 15 <= key_limit - 1) {
+      const int e = key0 >> a.bs_log2;
+      const int blk = __builtin_amdgcn_readfirstlane(s_blk[e - win0]);
+      const uint32_t slot0 = static_cast<uint32_t>(blk) * a.block_size + (key0 - (e << a.bs_log2));
+      const uint64_t base = static_cast<uint64_t>(slot0) * slot_stride;
+      const uint4* kb = kp + base;
+      const uint4* vb = vp + base;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int cb = (wave * NJ + j) * 64;
+        dma16_s(kb, lane_off[j], lds_addr(&s_kv[buf][0][cb]));
+        dma16_s(vb, lane_off[j], lds_addr(&s_kv[buf][1][cb]));
+      }
+      return;
+    }
     uint64_t off[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
