@@ -647,78 +647,85 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
     if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("attention: fork: ") + hipGetErrorString(e));
     dstrm = side->s;
   }
-  if (L.n_prefill > 0) {
-    pkv::PrefillArgs p;
-    p.q = q;
-    p.k_cache = k_cache;
-    p.v_cache = v_cache;
-    p.block_tables = block_tables_dev;
-    p.max_blocks = max_blocks;
-    p.block_size = block_size;
-    p.bs_log2 = bs_log2;
-    p.num_blocks = num_blocks;
-    p.n_items = static_cast<int32_t>(L.n_prefill);
-    p.hq = num_q_heads;
-    p.hkv = num_kv_heads;
-    p.scale_log2e = std::fabs(scale_log2e);
-    p.negate_q = scale < 0.f ? 1 : 0;
-    p.v_scale = v_scale;
-    p.items = reinterpret_cast<const pkv::PrefillItem*>(ws + L.prefill_off);
-    p.out = out;
-    const int pr = prof_begin(1, strm);
-    hipError_t e = pkv::launch_prefill(p, L.n_prefill, head_dim, group, fp8_scales != nullptr,
-                                       strm);
-    prof_end(pr, strm);
-    if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("prefill launch: ") + hipGetErrorString(e));
-  }
-  if (L.n_decode > 0) {
-    pkv::DecodeArgs d;
-    d.q = q;
-    d.k_cache = k_cache;
-    d.v_cache = v_cache;
-    d.block_tables = block_tables_dev;
-    d.max_blocks = max_blocks;
-    d.block_size = block_size;
-    d.bs_log2 = bs_log2;
-    d.num_blocks = num_blocks;
-    d.hq = num_q_heads;
-    d.hkv = num_kv_heads;
-    d.kv_split = kv_split;
-    d.scale_log2e = scale_log2e;
-    d.v_scale = v_scale;
-    d.items = reinterpret_cast<const pkv::DecodeItem*>(ws + L.decode_off);
-    d.group = group;
-    d.out = out;
-    d.part_m = part_m;
-    d.part_l = part_l;
-    d.part_acc = part_acc;
-    const int pr = prof_begin(2, dstrm);
-    hipError_t e = fp8_scales != nullptr
-                       ? pkv::launch_decode_fp8(d, L.n_decode, head_dim, group, dstrm)
-                       : pkv::launch_decode(d, L.n_decode, head_dim, group, dtype == PKV_BF16, dstrm);
-    prof_end(pr, dstrm);
-    if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("decode launch: ") + hipGetErrorString(e));
-  }
-  if (L.n_merge > 0) {
-    pkv::MergeArgs mg;
-    mg.items = reinterpret_cast<const pkv::MergeItem*>(ws + L.merge_off);
-    mg.hq = num_q_heads;
-    mg.n_waves = static_cast<int32_t>(L.n_merge * num_q_heads);
-    mg.part_m = part_m;
-    mg.part_l = part_l;
-    mg.part_acc = part_acc;
-    mg.out = out;
-    const int pr = prof_begin(3, dstrm);
-    hipError_t e = pkv::launch_merge(mg, L.n_merge, head_dim, dstrm);
-    prof_end(pr, dstrm);
-    if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("merge launch: ") + hipGetErrorString(e));
-  }
+  // the passes; after a failed launch the join below still runs, so that the caller's stream
+  // never runs ahead of work already enqueued on the second stream
+  const auto launch_passes = [&]() -> int32_t {
+    if (L.n_prefill > 0) {
+      pkv::PrefillArgs p;
+      p.q = q;
+      p.k_cache = k_cache;
+      p.v_cache = v_cache;
+      p.block_tables = block_tables_dev;
+      p.max_blocks = max_blocks;
+      p.block_size = block_size;
+      p.bs_log2 = bs_log2;
+      p.num_blocks = num_blocks;
+      p.n_items = static_cast<int32_t>(L.n_prefill);
+      p.hq = num_q_heads;
+      p.hkv = num_kv_heads;
+      p.scale_log2e = std::fabs(scale_log2e);
+      p.negate_q = scale < 0.f ? 1 : 0;
+      p.v_scale = v_scale;
+      p.items = reinterpret_cast<const pkv::PrefillItem*>(ws + L.prefill_off);
+      p.out = out;
+      const int pr = prof_begin(1, strm);
+      hipError_t e = pkv::launch_prefill(p, L.n_prefill, head_dim, group, fp8_scales != nullptr,
+                                         strm);
+      prof_end(pr, strm);
+      if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("prefill launch: ") + hipGetErrorString(e));
+    }
+    if (L.n_decode > 0) {
+      pkv::DecodeArgs d;
+      d.q = q;
+      d.k_cache = k_cache;
+      d.v_cache = v_cache;
+      d.block_tables = block_tables_dev;
+      d.max_blocks = max_blocks;
+      d.block_size = block_size;
+      d.bs_log2 = bs_log2;
+      d.num_blocks = num_blocks;
+      d.hq = num_q_heads;
+      d.hkv = num_kv_heads;
+      d.kv_split = kv_split;
+      d.scale_log2e = scale_log2e;
+      d.v_scale = v_scale;
+      d.items = reinterpret_cast<const pkv::DecodeItem*>(ws + L.decode_off);
+      d.group = group;
+      d.out = out;
+      d.part_m = part_m;
+      d.part_l = part_l;
+      d.part_acc = part_acc;
+      const int pr = prof_begin(2, dstrm);
+      hipError_t e = fp8_scales != nullptr
+                         ? pkv::launch_decode_fp8(d, L.n_decode, head_dim, group, dstrm)
+                         : pkv::launch_decode(d, L.n_decode, head_dim, group, dtype == PKV_BF16, dstrm);
+      prof_end(pr, dstrm);
+      if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("decode launch: ") + hipGetErrorString(e));
+    }
+    if (L.n_merge > 0) {
+      pkv::MergeArgs mg;
+      mg.items = reinterpret_cast<const pkv::MergeItem*>(ws + L.merge_off);
+      mg.hq = num_q_heads;
+      mg.n_waves = static_cast<int32_t>(L.n_merge * num_q_heads);
+      mg.part_m = part_m;
+      mg.part_l = part_l;
+      mg.part_acc = part_acc;
+      mg.out = out;
+      const int pr = prof_begin(3, dstrm);
+      hipError_t e = pkv::launch_merge(mg, L.n_merge, head_dim, dstrm);
+      prof_end(pr, dstrm);
+      if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("merge launch: ") + hipGetErrorString(e));
+    }
+    return PKV_OK;
+  };
+  int32_t rc = launch_passes();
   if (fork) {
     hipError_t e = hipEventRecord(side->join, dstrm);
     if (e == hipSuccess) e = hipStreamWaitEvent(strm, side->join, 0);
-    if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("attention: join: ") + hipGetErrorString(e));
+    if (e != hipSuccess && rc == PKV_OK)
+      rc = fail(PKV_ERR_HIP, std::string("attention: join: ") + hipGetErrorString(e));
   }
-  return ok();
+  return rc == PKV_OK ? ok() : rc;
 }
 
 int32_t workspace_size_impl(const int32_t* ctx_lens_host, const int32_t* cu_seqlens_q_host,
