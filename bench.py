@@ -47,6 +47,8 @@ def _parse():
     ap.add_argument("--consistent", default="batched-bf16-decode,mixed-ragged-step",
                     help="comma-separated workloads also timed in the phase-consistent mode, "
                          "reported under 'extra' as '<name>/phase-consistent'")
+    ap.add_argument("--consistent-split", type=int, default=2048,
+                    help="kv_split of the phase-consistent runs (the tile path's KV split)")
     ap.add_argument("--kernel-events", choices=("timed", "separate"), default="timed",
                     help="take the per-kernel HIP-event times inside the timed steps (default) "
                          "or in a second pass of the same steps")
@@ -82,7 +84,7 @@ def _kv_bytes(w):
 
 
 def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
-                  kernel_events="timed", cold_steps=20):
+                  kernel_events="timed", cold_steps=20, kv_split=None):
     """Build the step, then time `steps` whole steps; returns a result dict. With
     phase_consistent the attention runs with PKV_ATTN_PHASE_CONSISTENT (decode rows on the
     prefill tile path, bitwise equal to the same tokens inside prefill chunks)."""
@@ -94,6 +96,7 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
     from workloads import ALL_CONFIGS, make_workload
 
     w = make_workload(ALL_CONFIGS[name])
+    split = w.spec.kv_split if kv_split is None else kv_split
     t_build = time.time()
     gst = build_gpu_step(w, device=device)
     t_build = time.time() - t_build
@@ -105,10 +108,10 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
     bt_np = np.ascontiguousarray(gst.block_tables, dtype=np.int32)
     if w.kv_fp8:
         ws_bytes = pkv.write_kv_attention_fp8_workspace_size(ctx_np, cu_np, s.Hq, s.Hkv, s.D,
-                                                             w.T, s.kv_split, phase_consistent)
+                                                             w.T, split, phase_consistent)
     else:
         ws_bytes = pkv.write_kv_attention_workspace_size(
-            ctx_np, cu_np, s.Hq, s.Hkv, s.D, w.T, s.kv_split,
+            ctx_np, cu_np, s.Hq, s.Hkv, s.D, w.T, split,
             pkv.PKV_BF16 if s.dtype == "bf16" else pkv.PKV_F32, phase_consistent)
     workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=device)
     out = torch.empty((w.T, s.Hq, s.D), dtype=torch.float32, device=device)
@@ -121,11 +124,11 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
             pkv.write_kv_attention_fp8(gst.q, gst.k_new, gst.v_new, sl, gst.k_cache, gst.v_cache,
                                        gst.block_tables_dev, ctx_np, cu_np, w.scale, s.k_scale,
                                        s.v_scale, out=out, workspace=workspace,
-                                       kv_split=s.kv_split, phase_consistent=phase_consistent)
+                                       kv_split=split, phase_consistent=phase_consistent)
             return
         pkv.write_kv_attention(gst.q, gst.k_new, gst.v_new, sl, gst.k_cache, gst.v_cache,
                                gst.block_tables_dev, ctx_np, cu_np, w.scale, out=out,
-                               workspace=workspace, kv_split=s.kv_split,
+                               workspace=workspace, kv_split=split,
                                phase_consistent=phase_consistent)
 
     for _ in range(warmup):
@@ -208,7 +211,8 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
     dec_kv = acc.decode_kv_bytes(w.ctx_lens[decode_rows], s.Hkv, s.D, w.kv_elem_bytes)
     flops = acc.attention_flops(w.ctx_lens[~decode_rows], w.q_lens[~decode_rows], s.Hq, s.D)
     res = {
-        "workload": name, "phase_consistent": phase_consistent, "B": w.B, "T": w.T,
+        "workload": name, "phase_consistent": phase_consistent, "kv_split": split,
+        "B": w.B, "T": w.T,
         "kv_dtype": s.kv_dtype or s.dtype,
         "ms_per_step": ms_step,
         "step_gbs": (kv + app) / (ms_step * 1e-3) / 1e9, "tokens_per_s": w.T / (ms_step * 1e-3),
@@ -381,7 +385,7 @@ def main():
 
     for name in [n for n in args.consistent.split(",") if n]:
         r = time_workload(name, args.steps, args.warmup, phase_consistent=True,
-                          kernel_events=args.kernel_events)
+                          kernel_events=args.kernel_events, kv_split=args.consistent_split)
         r.pop("_gst"); r.pop("_w"); r.pop("_out")
         extra[name + "/phase-consistent"] = r
         torch.cuda.empty_cache()

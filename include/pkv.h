@@ -257,7 +257,8 @@ int32_t pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs_host,
  *                  0 <= q_len <= ctx_len <= max_blocks * block_size.
  *   head_dim:      64 or 128. num_q_heads / num_kv_heads in {1, 2, 4, 8}.
  *   kv_split:      positive multiple of 64, at most 2048 (512 is the default; part of the
- *                  numeric contract, so keep it fixed for bitwise comparisons).
+ *                  numeric contract, so keep it fixed for bitwise comparisons). The
+ *                  phase-consistent mode below takes any positive multiple of 64.
  *   out:           device float32 [T, num_q_heads, head_dim].
  *   workspace:     device buffer of at least pkv_attention_workspace_size() bytes, owned by
  *                  the caller, not read by the caller; it must stay untouched until the
@@ -286,9 +287,14 @@ int32_t pkv_attention(const void* q, const void* k_cache, const void* v_cache,
  * ascending order, bf16 MFMA for both contractions), so a token's output bits are the same
  * whether it is computed inside a prefill chunk of any size or as a decode row (phase
  * consistency, [BC section 2]; the page names the shared path as the main cost of the
- * consistent version). Decode rows then give
- * up the KV split, so one workgroup streams a row's whole context per kv head; the extra cost
- * over the split decode pass is measured, not hidden.
+ * consistent version). In this mode every row, decode or prefill, has its keys cut into
+ * splits of kv_split keys on the tile path: a tile item covers one split of its rows, and a row
+ * whose keys reach past the first split writes one partial per split, which the merge combines
+ * in ascending split order, exactly as for the split decode pass. The same kv_split must be
+ * used for the calls whose rows are compared. Here kv_split has no upper bound: a split longer
+ * than every context gives each row one pass over its whole context (no partials, fewer
+ * workgroups for long decode rows). The extra cost over the split decode pass is measured, not
+ * hidden.
  * Errors: as pkv_attention, plus PKV_ERR_INVALID for unknown flag bits and PKV_ERR_UNSUPPORTED
  * when the flag is set for float32 inputs (the tile path is bf16 MFMA only). */
 int32_t pkv_attention_workspace_size_ex(const int32_t* ctx_lens_host,

@@ -279,6 +279,7 @@ struct StepShape {
   bool prefill_on_mfma;  // segments with q_len > 1 use the prefill kernel
   bool all_mfma;         // phase-consistent mode: every segment (decode rows too) uses it
   int32_t prefill_rows_per_item;
+  int32_t tile_split;    // > 0 (phase-consistent mode: kv_split): tile items cover one KV split
 };
 
 // Whether segment b (q_len ql >= 1) runs on the prefill tile kernel.
@@ -295,7 +296,22 @@ pkv::WorkspaceLayout layout_for(const StepShape& s, int32_t hq, int32_t head_dim
     const int32_t ql = s.cu[b + 1] - s.cu[b];
     if (ql == 0) continue;
     if (on_tiles(s, ql)) {
-      L.n_prefill += ceil_div(ql, s.prefill_rows_per_item);
+      const int32_t prior = s.ctx[b] - ql;
+      if (s.tile_split == 0) {
+        L.n_prefill += ceil_div(ql, s.prefill_rows_per_item);
+        continue;
+      }
+      // an item per row chunk and split reached by its last row; split partials for every row
+      // of a segment whose context reaches past split 0, and a merge per such row
+      for (int32_t r0 = 0; r0 < ql; r0 += s.prefill_rows_per_item) {
+        const int32_t last = prior + std::min(r0 + s.prefill_rows_per_item, ql) - 1;
+        L.n_prefill += last / s.tile_split + 1;
+      }
+      const int64_t ns_max = ceil_div(s.ctx[b], s.tile_split);
+      if (ns_max > 1) {
+        L.n_part += static_cast<int64_t>(ql) * ns_max;
+        L.n_merge += prior + ql - std::max(prior, s.tile_split);
+      }
       continue;
     }
     for (int32_t i = 0; i < ql; ++i) {
@@ -338,12 +354,28 @@ void build_lists(const StepShape& s, const pkv::WorkspaceLayout& L, char* host) 
     if (ql == 0) continue;
     if (on_tiles(s, ql)) {
       const int32_t prior = s.ctx[b] - ql;
+      const int32_t S = s.tile_split;
+      const int32_t ns_max = S > 0 ? static_cast<int32_t>(ceil_div(s.ctx[b], S)) : 1;
+      const int32_t pbase = ns_max > 1 ? static_cast<int32_t>(part) : -1;
+      if (ns_max > 1) {
+        part += static_cast<int64_t>(ql) * ns_max;
+        for (int32_t i = std::max(0, S - prior); i < ql; ++i)   // rows at positions >= S
+          mer[nm++] = pkv::MergeItem{s.cu[b] + i, (prior + i) / S + 1, pbase + i * ns_max, 0};
+      }
       for (int32_t r0 = 0; r0 < ql; r0 += s.prefill_rows_per_item) {
-        pkv::PrefillItem& p = pre[np++];
-        p.seq = b;
-        p.row0 = s.cu[b] + r0;
-        p.n_rows = std::min(s.prefill_rows_per_item, ql - r0);
-        p.pos0 = prior + r0;
+        const int32_t n = std::min(s.prefill_rows_per_item, ql - r0);
+        const int32_t n_splits = S > 0 ? (prior + r0 + n - 1) / S + 1 : 1;
+        for (int32_t sp = 0; sp < n_splits; ++sp) {
+          pkv::PrefillItem& p = pre[np++];
+          p.seq = b;
+          p.row0 = s.cu[b] + r0;
+          p.n_rows = n;
+          p.pos0 = prior + r0;
+          p.split = sp;
+          p.part = pbase < 0 ? -1 : pbase + r0 * ns_max;
+          p.pstride = ns_max;
+          p.pad = 0;
+        }
       }
       continue;
     }
@@ -362,8 +394,14 @@ void build_lists(const StepShape& s, const pkv::WorkspaceLayout& L, char* host) 
   }
   // longest work first: short tail items then fill the gaps at the end of each launch (item
   // order never affects any row's bits). A prefill item's work grows with its last key.
-  std::stable_sort(pre, pre + np, [](const pkv::PrefillItem& x, const pkv::PrefillItem& y) {
-    return x.pos0 + x.n_rows > y.pos0 + y.n_rows;
+  const auto pre_keys = [&](const pkv::PrefillItem& x) -> int64_t {
+    const int64_t end = x.pos0 + x.n_rows;
+    if (s.tile_split == 0) return end;
+    const int64_t k0 = static_cast<int64_t>(x.split) * s.tile_split;
+    return std::min<int64_t>(end, k0 + s.tile_split) - k0;
+  };
+  std::stable_sort(pre, pre + np, [&](const pkv::PrefillItem& x, const pkv::PrefillItem& y) {
+    return pre_keys(x) > pre_keys(y);
   });
   std::stable_sort(dec, dec + nd, [&](const pkv::DecodeItem& x, const pkv::DecodeItem& y) {
     const int64_t kx = std::min<int64_t>(x.n_keys - static_cast<int64_t>(x.split) * s.kv_split, s.kv_split);
@@ -398,12 +436,18 @@ int32_t check_step(const int32_t* ctx, const int32_t* cu, int32_t B, int32_t T,
   return PKV_OK;
 }
 
-int32_t check_heads(int32_t hq, int32_t hkv, int32_t head_dim, int32_t kv_split, int32_t dtype) {
+// kv_split: a positive multiple of 64, at most 2048 for the split decode pass; the
+// phase-consistent mode (tile path only) takes any positive multiple of 64.
+int32_t check_heads(int32_t hq, int32_t hkv, int32_t head_dim, int32_t kv_split, int32_t dtype,
+                    uint32_t flags) {
   if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID, "dtype must be PKV_F32 or PKV_BF16");
   if (hq <= 0 || hkv <= 0) return fail(PKV_ERR_INVALID, "head counts must be positive");
   if (hq % hkv != 0) return fail(PKV_ERR_INVALID, "num_q_heads must be a multiple of num_kv_heads");
-  if (kv_split <= 0 || kv_split % pkv::kDecodeTile != 0 || kv_split > pkv::kMaxDecodeSplit)
-    return fail(PKV_ERR_INVALID, "kv_split must be a positive multiple of 64, at most 2048");
+  const bool tiles_only = (flags & PKV_ATTN_PHASE_CONSISTENT) != 0;
+  if (kv_split <= 0 || kv_split % pkv::kDecodeTile != 0 ||
+      (!tiles_only && kv_split > pkv::kMaxDecodeSplit))
+    return fail(PKV_ERR_INVALID, "kv_split must be a positive multiple of 64, at most 2048 "
+                                 "(no upper bound in the phase-consistent mode)");
   if (!pkv::decode_supported(head_dim, hq / hkv))
     return fail(PKV_ERR_UNSUPPORTED, "head_dim must be 64 or 128 and num_q_heads / num_kv_heads "
                                      "one of 1, 2, 4, 8");
@@ -431,6 +475,7 @@ StepShape shape_for(const int32_t* ctx, const int32_t* cu, int32_t B, int32_t hq
   const int group = hq / hkv;
   s.prefill_on_mfma = pkv::prefill_supported(head_dim, group, dtype == PKV_BF16);
   s.prefill_rows_per_item = pkv::kPrefillMRows / group;
+  s.tile_split = s.all_mfma ? kv_split : 0;
   return s;
 }
 
@@ -529,7 +574,7 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
                        const float* fp8_scales = nullptr, pkv::WriteFp8Args* wr8 = nullptr) {
   // fp8_scales != nullptr: q is bfloat16 and the pools hold E4M3 codes with per-tensor scales
   // {k_scale, v_scale}; rows are routed as for bfloat16 pools, onto the E4M3 kernels
-  int32_t st = check_heads(num_q_heads, num_kv_heads, head_dim, kv_split, dtype);
+  int32_t st = check_heads(num_q_heads, num_kv_heads, head_dim, kv_split, dtype, flags);
   if (st != PKV_OK) return st;
   st = check_flags(flags, num_q_heads, num_kv_heads, head_dim, dtype);
   if (st != PKV_OK) return st;
@@ -668,6 +713,10 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
       p.v_scale = v_scale;
       p.items = reinterpret_cast<const pkv::PrefillItem*>(ws + L.prefill_off);
       p.out = out;
+      p.tile_split = s.tile_split;
+      p.part_m = part_m;
+      p.part_l = part_l;
+      p.part_acc = part_acc;
       const int pr = prof_begin(1, strm);
       hipError_t e = pkv::launch_prefill(p, L.n_prefill, head_dim, group, fp8_scales != nullptr,
                                          strm);
@@ -735,7 +784,7 @@ int32_t workspace_size_impl(const int32_t* ctx_lens_host, const int32_t* cu_seql
   if (bytes == nullptr) return fail(PKV_ERR_INVALID, "workspace_size: bytes is NULL");
   *bytes = 0;
   if (n_write_rows < 0) return fail(PKV_ERR_INVALID, "workspace_size: n_rows must be >= 0");
-  int32_t st = check_heads(num_q_heads, num_kv_heads, head_dim, kv_split, dtype);
+  int32_t st = check_heads(num_q_heads, num_kv_heads, head_dim, kv_split, dtype, flags);
   if (st != PKV_OK) return st;
   st = check_flags(flags, num_q_heads, num_kv_heads, head_dim, dtype);
   if (st != PKV_OK) return st;

@@ -101,6 +101,10 @@ struct PrefillArgs {
   float v_scale;      // E4M3 pools: the V scale (1 otherwise)
   const PrefillItem* items;
   float* out;
+  int32_t tile_split;  // > 0: each item covers one KV split of this many keys (see PrefillItem)
+  float* part_m;       // split partials, laid out as those of DecodeArgs
+  float* part_l;
+  float* part_acc;
 };
 
 // Each launcher enqueues one kernel on `stream` and returns hipSuccess or the launch error.

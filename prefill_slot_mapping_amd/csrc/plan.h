@@ -42,12 +42,19 @@ struct MergeItem {
 };
 
 // One prefill tile: rows row0 .. row0 + n_rows - 1 of sequence seq, at positions
-// pos0 .. pos0 + n_rows - 1. The kernel grid runs items x Hkv.
+// pos0 .. pos0 + n_rows - 1. The kernel grid runs items x Hkv. Without a tile split the item
+// covers keys [0, pos0 + n_rows); with one (PrefillArgs::tile_split = S > 0) it covers keys
+// [split * S, (split + 1) * S) of those, and a row at position pos whose keys reach past split
+// 0 (pos >= S) writes partial slot part + (row - row0) * pstride + split instead of its output.
 struct PrefillItem {
   int32_t seq;
   int32_t row0;
   int32_t n_rows;
   int32_t pos0;
+  int32_t split;
+  int32_t part;
+  int32_t pstride;
+  int32_t pad;
 };
 
 // Byte offsets of each region inside the caller's workspace (all 256-byte aligned).

@@ -162,7 +162,13 @@ prefill_kernel(PrefillArgs a) {
   }
 
   const int key_limit = it.pos0 + it.n_rows;           // keys >= key_limit: no row needs them
-  const int n_tiles = (key_limit + kPrefillKeyTile - 1) / kPrefillKeyTile;
+  // this item's keys: [kv0, kv_end), tiles kt0 .. n_tiles - 1 (a split is a whole number of tiles)
+  const int kv0 = a.tile_split > 0 ? it.split * a.tile_split : 0;
+  const int kv_end = a.tile_split > 0
+      ? static_cast<int>(min(static_cast<int64_t>(kv0) + a.tile_split, static_cast<int64_t>(key_limit)))
+      : key_limit;
+  const int kt0 = kv0 / kPrefillKeyTile;
+  const int n_tiles = (kv_end + kPrefillKeyTile - 1) / kPrefillKeyTile;
   const int32_t* bt = a.block_tables + static_cast<int64_t>(it.seq) * a.max_blocks;
   const uint4* __restrict__ kp = static_cast<const uint4*>(a.k_cache);
   const uint4* __restrict__ vp = static_cast<const uint4*>(a.v_cache);
@@ -172,7 +178,7 @@ prefill_kernel(PrefillArgs a) {
 
   auto entry_of = [&](int key) { return a.bs_log2 >= 0 ? key >> a.bs_log2 : key / a.block_size; };
   const int n_entries = entry_of(key_limit - 1) + 1;
-  int win0 = 0;
+  int win0 = entry_of(kv0);
 
   // Block-table entries win0 .. win0 + window - 1 into s_blk. An out-of-pool block id marks the
   // item bad and is replaced by block 0, so no load ever leaves the pool.
@@ -315,28 +321,29 @@ prefill_kernel(PrefillArgs a) {
   if (tid == 0) s_bad = 0;
   load_window();
   __syncthreads();
-  if constexpr (F8) dma_codes(0, 0);
-  else dma_tile(0, 0);
+  if constexpr (F8) dma_codes(kt0, 0);
+  else dma_tile(kt0, 0);
 
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const int buf = F8 ? 0 : (kt & 1);
+  for (int kt = kt0; kt < n_tiles; ++kt) {
+    const int par = (kt - kt0) & 1;   // tile kt in buffer par (E4M3: its codes)
+    const int buf = F8 ? 0 : par;
     // tile kt has landed in LDS; every wave is done with tile kt - 1 and with the block window
     tile_barrier();
     if (kt + 1 < n_tiles) {
-      const int last_key = min((kt + 2) * kPrefillKeyTile, key_limit) - 1;
+      const int last_key = min((kt + 2) * kPrefillKeyTile, kv_end) - 1;
       if (entry_of(last_key) >= win0 + kPrefillBlockWindow) {   // uniform: slide the window
         win0 = entry_of((kt + 1) * kPrefillKeyTile);
         load_window();
         tile_barrier();
       }
       // in flight while this tile is computed
-      if constexpr (F8) dma_codes(kt + 1, (kt + 1) & 1);
+      if constexpr (F8) dma_codes(kt + 1, par ^ 1);
       else dma_tile(kt + 1, buf ^ 1);
     }
     if constexpr (F8) {
       // every wave widens its share of tile kt (its codes landed before the barrier above; the
       // bf16 buffer is free: every wave has finished tile kt - 1), then the workgroup meets
-      widen(kt & 1);
+      widen(par);
       lds_barrier();
     }
 
@@ -465,6 +472,32 @@ prefill_kernel(PrefillArgs a) {
   if (!real) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float vs = a.v_scale;
+  if (a.tile_split > 0 && !(it.split == 0 && pos < a.tile_split)) {
+    // a row whose keys reach past split 0: the partial (m, l, V-scaled acc) of this split, or
+    // nothing when the row ends before the split
+    if (pos < kv0) return;
+    const int64_t pidx = (static_cast<int64_t>(it.part) + static_cast<int64_t>(qrow) * it.pstride +
+                          it.split) * a.hq + static_cast<int64_t>(g) * G + head;
+    if (h32 == 0) {
+      a.part_m[pidx] = m_ref;
+      a.part_l[pidx] = bad_item ? __builtin_nanf("") : l_tot;
+    }
+    float* pd = a.part_acc + pidx * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        float4 o;
+        o.x = F8 ? acc[db][4 * rq + 0] * vs : acc[db][4 * rq + 0];
+        o.y = F8 ? acc[db][4 * rq + 1] * vs : acc[db][4 * rq + 1];
+        o.z = F8 ? acc[db][4 * rq + 2] * vs : acc[db][4 * rq + 2];
+        o.w = F8 ? acc[db][4 * rq + 3] * vs : acc[db][4 * rq + 3];
+        if (bad_item) o = make_float4(__builtin_nanf(""), __builtin_nanf(""),
+                                      __builtin_nanf(""), __builtin_nanf(""));
+        *reinterpret_cast<float4*>(pd + 32 * db + 8 * rq + 4 * h32) = o;
+      }
+    return;
+  }
   float* dst = a.out + ((static_cast<int64_t>(it.row0) + qrow) * a.hq +
                         static_cast<int64_t>(g) * G + head) * D;
 #pragma unroll

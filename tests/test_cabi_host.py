@@ -243,12 +243,32 @@ def test_phase_consistent_flag_validation():
                                      phase_consistent=True)
 
 
-def test_phase_consistent_workspace_has_no_split_partials():
-    # a 4096-key decode row: 8 splits and their partials normally; one tile item when consistent
-    normal = pkv.attention_workspace_size([4096], [0, 1], 8, 2, 128, 512)
-    cons = pkv.attention_workspace_size([4096], [0, 1], 8, 2, 128, 512, phase_consistent=True)
-    assert normal >= 8 * 8 * 130 * 4
-    assert 0 < cons < 1024
+def test_phase_consistent_workspace_holds_tile_split_partials():
+    # a 4096-key decode row is cut into kv_split splits in both modes: 8 partial slots of
+    # 8 heads x (128 + 2) floats at kv_split 512, 2 at 2048, none when one split covers it
+    part = 8 * (128 + 2) * 4
+    for split, n in [(512, 8), (2048, 2)]:
+        normal = pkv.attention_workspace_size([4096], [0, 1], 8, 2, 128, split)
+        cons = pkv.attention_workspace_size([4096], [0, 1], 8, 2, 128, split, phase_consistent=True)
+        assert n * part <= normal < n * part + 4096
+        assert n * part <= cons < n * part + 4096
+    assert 0 < pkv.attention_workspace_size([2048], [0, 1], 8, 2, 128, 2048,
+                                            phase_consistent=True) < 1024
+    # a prefill segment: partial slots for every row times the segment's splits
+    cons = pkv.attention_workspace_size([1100], [0, 100], 8, 2, 128, 512, phase_consistent=True)
+    assert 100 * 3 * part <= cons < 100 * 3 * part + 8192
+
+
+def test_kv_split_beyond_2048_only_in_the_consistent_mode():
+    with pytest.raises(pkv.InvalidArgument):
+        pkv.attention_workspace_size([5000], [0, 1], 8, 2, 128, 4096)
+    assert pkv.attention_workspace_size([5000], [0, 1], 8, 2, 128, 4096,
+                                        phase_consistent=True) > 2 * 8 * 130 * 4
+    # one split longer than every context: no partials
+    assert pkv.attention_workspace_size([5000], [0, 1], 8, 2, 128, 1 << 20,
+                                        phase_consistent=True) < 1024
+    with pytest.raises(pkv.InvalidArgument):
+        pkv.attention_workspace_size([5000], [0, 1], 8, 2, 128, 4100, phase_consistent=True)
 
 
 def _fused(**kw):

@@ -39,22 +39,24 @@ def test_consistent_mode_matches_oracle(name):
     assert err <= TOL
 
 
-def _run_rows(gst, w, b, q_rows, ctx, phase_consistent):
+def _run_rows(gst, w, b, q_rows, ctx, phase_consistent, kv_split=512):
     """Rows q_rows of sequence b attending as the last len(q_rows) positions of ctx keys."""
     n = q_rows.shape[0]
     out = pkv.attention(q_rows.contiguous(), gst.k_cache, gst.v_cache,
                         gst.block_tables_dev[b:b + 1].contiguous(), [ctx], [0, n], w.scale,
-                        phase_consistent=phase_consistent)
+                        kv_split=kv_split, phase_consistent=phase_consistent)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
 
-@pytest.mark.parametrize("dims", [(32, 8, 128, 16), (16, 2, 128, 32), (8, 8, 64, 16),
-                                  (8, 1, 64, 5)])
+@pytest.mark.parametrize("dims", [(32, 8, 128, 16, 512), (16, 2, 128, 32, 512),
+                                  (8, 8, 64, 16, 512), (8, 1, 64, 5, 512), (32, 8, 128, 16, 64),
+                                  (16, 4, 64, 32, 128), (32, 8, 128, 16, 1 << 20)])
 def test_decode_row_equals_prefill_row_bitwise(dims):
     """The token at position p: as a decode row (q_len 1, ctx p + 1), as the last row of a
-    chunk ending at p, and in the middle of a chunk that runs past p, all bitwise equal."""
-    hq, hkv, d, bs = dims
+    chunk ending at p, and in the middle of a chunk that runs past p, all bitwise equal (the
+    consistent mode cuts every row's keys into the same kv_split splits)."""
+    hq, hkv, d, bs, split = dims
     C = 700
     w = make_workload(explicit_spec(f"phase-{hq}-{hkv}-{d}-{bs}", "bf16", hq, hkv, d, bs,
                                     [(C, 1), (333, 1)]))
@@ -65,16 +67,16 @@ def test_decode_row_equals_prefill_row_bitwise(dims):
         torch.bfloat16).to(DEV)
     for p in [0, 1, 63, 64, 65, 127, 300, 511, 512, C - 1]:
         print(f"[phase] dims={dims} p={p}", flush=True)
-        dec = _run_rows(gst, w, 0, qs[p:p + 1], p + 1, True)[0]
+        dec = _run_rows(gst, w, 0, qs[p:p + 1], p + 1, True, split)[0]
         lo = max(0, p - 40)
-        end = _run_rows(gst, w, 0, qs[lo:p + 1], p + 1, True)[-1]
+        end = _run_rows(gst, w, 0, qs[lo:p + 1], p + 1, True, split)[-1]
         assert np.array_equal(dec, end), f"chunk ending at {p}"
         hi = min(C, p + 37)
-        mid = _run_rows(gst, w, 0, qs[lo:hi], hi, True)[p - lo]
+        mid = _run_rows(gst, w, 0, qs[lo:hi], hi, True, split)[p - lo]
         assert np.array_equal(dec, mid), f"chunk through {p}"
         # the default mode computes the decode row on the split decode path: same values
         # within tolerance, bits free to differ
-        plain = _run_rows(gst, w, 0, qs[p:p + 1], p + 1, False)[0]
+        plain = _run_rows(gst, w, 0, qs[p:p + 1], p + 1, False, min(split, 2048))[0]
         assert float(np.abs(plain.astype(np.float64) - dec).max()) <= TOL
 
 
