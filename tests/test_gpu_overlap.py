@@ -91,3 +91,39 @@ def test_caller_stream_waits_for_the_decode_pass(fused):
         side.synchronize()
         print(f"[overlap] fused={fused} repeat {rep}", flush=True)
         assert np.array_equal(_bits(snap), ref)
+
+
+def test_forked_steps_from_two_threads():
+    """Two host threads run forked mixed steps on streams of their own: the library's lock
+    around the fork and the join and its staging ring keep every result whole."""
+    import threading
+    from prefill_slot_mapping_amd.harness import build_gpu_step
+    w = make_workload(ALL_CONFIGS["mixed-ragged-step"])
+    steps = [build_gpu_step(w, device=DEV) for _ in range(2)]
+    refs = []
+    for gst in steps:
+        refs.append(_bits(gst.attention()))
+        torch.cuda.synchronize()
+    errors = []
+
+    def run(i):
+        try:
+            gst = steps[i]
+            s = torch.cuda.Stream(device=DEV)
+            for rep in range(4):
+                with torch.cuda.stream(s):
+                    gst.out.fill_(float("nan"))
+                    snap = gst.attention(stream=s).clone()
+                s.synchronize()
+                if not np.array_equal(_bits(snap), refs[i]):
+                    errors.append(f"thread {i} repeat {rep}")
+        except Exception as e:   # reported by the main thread
+            errors.append(f"thread {i}: {e!r}")
+
+    threads = [threading.Thread(target=run, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=100)
+    print(f"[overlap] two threads: {errors or 'ok'}", flush=True)
+    assert not any(t.is_alive() for t in threads) and not errors, errors
