@@ -271,6 +271,19 @@ def test_kv_split_beyond_2048_only_in_the_consistent_mode():
         pkv.attention_workspace_size([5000], [0, 1], 8, 2, 128, 4100, phase_consistent=True)
 
 
+def test_consistent_workspace_sums_the_segments():
+    # partials of a multi-segment step: per segment, q_len rows x ceil(ctx / kv_split) slots
+    # when ctx > kv_split, none otherwise; decode rows count as 1-row segments
+    hq, hkv, d, split = 8, 2, 128, 256
+    ctx = [1000, 300, 256, 5000, 40]
+    ql = [100, 1, 1, 1, 40]
+    cu = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+    slots = sum(q * -(-c // split) for c, q in zip(ctx, ql) if c > split)
+    got = pkv.attention_workspace_size(ctx, cu, hq, hkv, d, split, phase_consistent=True)
+    part = slots * hq * (d + 2) * 4
+    assert part <= got < part + 64 * 1024
+
+
 def _fused(**kw):
     """Raw pkv_write_kv_attention call with fake device pointers: only validation may run."""
     lib = pkv.lib()
