@@ -20,7 +20,9 @@
  *     launched, nothing is copied and no allocator state changes.
  *   - No exception crosses the ABI. No entry point allocates device memory: device buffers
  *     are owned by the caller; the library owns only allocator handles, a small ring of
- *     pinned host staging buffers for work lists and, per device, one stream and two events.
+ *     pinned host staging buffers for work lists (allocated by the first call on a device and
+ *     grown only by a call larger than any before it: see pkv_staging_info) and, per device,
+ *     one stream and two events.
  *   - Device work is enqueued on the caller's stream (a hipStream_t passed as void*; NULL is
  *     the default stream) and is asynchronous with respect to the host. An attention step with
  *     a large prefill pass (over 512 workgroups: the segments' tiles of 128 / group query
@@ -322,10 +324,10 @@ int32_t pkv_attention_ex(const void* q, const void* k_cache, const void* v_cache
  * the pinned buffer in place (no separate host-to-device copy).
  *   slots_host:   host int32 [n_rows]; row t of k_new / v_new ([n_rows, num_kv_heads,
  *                 head_dim], device, dtype) goes to slot slots_host[t]. A negative slot skips
- *                 its row; a slot >= num_blocks * block_size is PKV_ERR_INVALID (checked before
- *                 anything is enqueued). Duplicate non-negative slots leave the destination
- *                 undefined (pkv_validate_slots checks a host array). The array is copied
- *                 before the call returns.
+ *                 its row; a slot >= num_blocks * block_size, or a non-negative slot that appears
+ *                 twice, is PKV_ERR_INVALID (the rules of pkv_validate_slots, checked before
+ *                 anything is enqueued: two rows sent to one slot would leave it undefined).
+ *                 The array is copied before the call returns.
  *   workspace:    at least pkv_write_kv_attention_workspace_size() bytes (the attention
  *                 workspace plus the staged slots); same ownership rules as pkv_attention.
  * Every other argument as in pkv_write_kv and pkv_attention_ex. n_rows == 0 is the plain
@@ -395,7 +397,7 @@ int32_t pkv_attention_fp8(const void* q, const void* k_cache, const void* v_cach
 /* Fused E4M3 step: pkv_write_kv_fp8 of k_new / v_new through host slots followed by
  * pkv_attention_fp8, with the slots in the same host-to-device copy as the work lists, as
  * pkv_write_kv_attention does for bfloat16 / float32 pools (same slot rules: negative skips,
- * >= num_blocks * block_size is PKV_ERR_INVALID). Workspace from
+ * >= num_blocks * block_size or a repeated non-negative slot is PKV_ERR_INVALID). Workspace from
  * pkv_write_kv_attention_fp8_workspace_size (same flags, n_rows >= 0). Errors: as
  * pkv_write_kv_fp8 and pkv_attention_fp8. */
 int32_t pkv_write_kv_attention_fp8_workspace_size(const int32_t* ctx_lens_host,
@@ -425,6 +427,13 @@ int32_t pkv_write_kv_attention_fp8(const void* q, const void* k_new, const void*
  * Not thread-safe with concurrent launches from several host threads. */
 int32_t pkv_profile_enable(int32_t enable);
 int32_t pkv_profile_read(int32_t kernel_kind, double* total_ms, int64_t* launches);
+/* The calling thread's current device's pinned staging ring: bytes per slot (0 before the
+ * first staged call) and how many times its arena has been allocated so far. The arena (16
+ * equal slots) is allocated by the first call that stages work lists on a device and replaced
+ * only when a call needs more than a slot holds (the new slot size is the next power of two at
+ * or above twice the old one and the request, at least 1 MiB), so steps of a size already seen
+ * allocate nothing. Either pointer may be NULL. */
+int32_t pkv_staging_info(size_t* slot_bytes, int64_t* allocations);
 /* Kernel kinds bracketed from now on while profiling is enabled: bit k = kind k (default all,
  * 0xF); records already taken are kept. Each event record costs the stream a few
  * microseconds, so a caller timing whole steps can bracket only the kernel it reports, or

@@ -9,7 +9,7 @@ from ._lib import (  # noqa: F401
     PkvError, PoolExhausted, SchedPlan, Scheduler, SharedWrite, Unsupported, attention,
     attention_fp8, attention_fp8_workspace_size, attention_workspace_size, copy_blocks,
     header_functions, lib, profile_enable, profile_read, profile_set_kinds, slot_mapping_step,
-    validate_slots, version, write_kv, write_kv_attention, write_kv_attention_workspace_size,
+    staging_info, validate_slots, version, write_kv, write_kv_attention, write_kv_attention_workspace_size,
     write_kv_attention_fp8, write_kv_attention_fp8_workspace_size, write_kv_fp8,
 )
 from . import accounting  # noqa: F401

@@ -148,6 +148,7 @@ _SIGS = {
                                     ctypes.c_float, ctypes.c_float, ctypes.c_float, _i32,
                                     ctypes.c_uint32, _vp, _vp, ctypes.c_size_t, _vp], _i32),
     "pkv_profile_set_kinds": ([ctypes.c_uint32], _i32),
+    "pkv_staging_info": ([ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(_i64)], _i32),
     "pkv_profile_enable": ([_i32], _i32),
     "pkv_profile_read": ([_i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)], _i32),
 }
@@ -416,6 +417,16 @@ def _stream_ptr(t, stream) -> int:
     return int(stream.cuda_stream)
 
 
+def _on_stream(stream):
+    """Context in which the wrappers allocate their temporaries (device copies of host slots,
+    workspaces, outputs): the stream the library enqueues on. Memory the caching allocator
+    hands out there is only reused by work ordered after ours on that stream, and a host-slot
+    copy made there runs before the kernel that reads it."""
+    import contextlib
+    import torch
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _need_cuda(*ts):
     for t in ts:
         if not (t.is_cuda and t.is_contiguous()):
@@ -431,17 +442,18 @@ def write_kv(k_new, v_new, slots, k_cache, v_cache, stream=None) -> None:
     import torch
     _need_cuda(k_new, v_new, k_cache, v_cache)
     nb, bs, hkv, d = k_cache.shape
-    if hasattr(slots, "is_cuda") and slots.is_cuda:
-        sl = slots
-    else:
-        host = _host_i32(slots)
-        validate_slots(host, nb * bs)
-        sl = torch.from_numpy(host).to(k_cache.device)
-    if sl.dtype != torch.int32 or not sl.is_contiguous():
-        raise ValueError("slots must be a contiguous int32 tensor")
-    _check(lib().pkv_write_kv(k_new.data_ptr(), v_new.data_ptr(), sl.data_ptr(),
-                              int(k_new.shape[0]), k_cache.data_ptr(), v_cache.data_ptr(), nb, bs,
-                              hkv, d, _dtype_code(k_cache), _stream_ptr(k_cache, stream)))
+    with _on_stream(stream):
+        if hasattr(slots, "is_cuda") and slots.is_cuda:
+            sl = slots
+        else:
+            host = _host_i32(slots)
+            validate_slots(host, nb * bs)
+            sl = torch.from_numpy(host).to(k_cache.device)
+        if sl.dtype != torch.int32 or not sl.is_contiguous():
+            raise ValueError("slots must be a contiguous int32 tensor")
+        _check(lib().pkv_write_kv(k_new.data_ptr(), v_new.data_ptr(), sl.data_ptr(),
+                                  int(k_new.shape[0]), k_cache.data_ptr(), v_cache.data_ptr(), nb,
+                                  bs, hkv, d, _dtype_code(k_cache), _stream_ptr(k_cache, stream)))
 
 
 def copy_blocks(pairs, k_cache, v_cache, workspace=None, stream=None) -> None:
@@ -454,13 +466,14 @@ def copy_blocks(pairs, k_cache, v_cache, workspace=None, stream=None) -> None:
         return
     nb, bs, hkv, d = k_cache.shape
     need = (8 * n + 255) // 256 * 256
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=k_cache.device)
     dt = PKV_E4M3 if k_cache.dtype == torch.uint8 else _dtype_code(k_cache)
-    _check(lib().pkv_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), _ptr(pr), n, nb, bs, hkv,
-                                 d, dt, workspace.data_ptr(),
-                                 workspace.numel() * workspace.element_size(),
-                                 _stream_ptr(k_cache, stream)))
+    with _on_stream(stream):
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=k_cache.device)
+        _check(lib().pkv_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), _ptr(pr), n, nb, bs,
+                                     hkv, d, dt, workspace.data_ptr(),
+                                     workspace.numel() * workspace.element_size(),
+                                     _stream_ptr(k_cache, stream)))
 
 
 def attention_workspace_size(ctx_lens, cu_seqlens_q, num_q_heads: int, num_kv_heads: int,
@@ -499,21 +512,22 @@ def attention(q, k_cache, v_cache, block_tables, ctx_lens, cu_seqlens_q, scale: 
     if block_tables.dim() != 2 or block_tables.shape[0] != B:
         raise ValueError("block_tables must be [B, max_blocks]")
     dt = _dtype_code(q)
-    if out is None:
-        out = torch.empty((T, hq, d), dtype=torch.float32, device=q.device)
-    _need_cuda(out)
     need = attention_workspace_size(ctx, cu, hq, hkv, d, kv_split, dt, phase_consistent)
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    args = [q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
-            int(block_tables.shape[1]), _ptr(ctx), _ptr(cu), B, T, hq, hkv, d, bs, nb,
-            float(scale), int(kv_split), dt]
-    tail = [out.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-            _stream_ptr(q, stream)]
-    if phase_consistent:
-        _check(lib().pkv_attention_ex(*args, PKV_ATTN_PHASE_CONSISTENT, *tail))
-    else:
-        _check(lib().pkv_attention(*args, *tail))
+    with _on_stream(stream):
+        if out is None:
+            out = torch.empty((T, hq, d), dtype=torch.float32, device=q.device)
+        _need_cuda(out)
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        args = [q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+                int(block_tables.shape[1]), _ptr(ctx), _ptr(cu), B, T, hq, hkv, d, bs, nb,
+                float(scale), int(kv_split), dt]
+        tail = [out.data_ptr(), workspace.data_ptr(),
+                workspace.numel() * workspace.element_size(), _stream_ptr(q, stream)]
+        if phase_consistent:
+            _check(lib().pkv_attention_ex(*args, PKV_ATTN_PHASE_CONSISTENT, *tail))
+        else:
+            _check(lib().pkv_attention(*args, *tail))
     return out
 
 
@@ -556,21 +570,23 @@ def write_kv_attention(q, k_new, v_new, slots, k_cache, v_cache, block_tables, c
     if block_tables.dim() != 2 or block_tables.shape[0] != B:
         raise ValueError("block_tables must be [B, max_blocks]")
     dt = _dtype_code(q)
-    if out is None:
-        out = torch.empty((T, hq, d), dtype=torch.float32, device=q.device)
-    _need_cuda(out)
-    ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    if workspace is None:
-        need = write_kv_attention_workspace_size(ctx, cu, hq, hkv, d, n_rows, kv_split, dt,
-                                                 phase_consistent)
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-        ws_have = workspace.numel()
     flags = PKV_ATTN_PHASE_CONSISTENT if phase_consistent else 0
-    _check(lib().pkv_write_kv_attention(
-        q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), _ptr(sl), n_rows, k_cache.data_ptr(),
-        v_cache.data_ptr(), block_tables.data_ptr(), int(block_tables.shape[1]), _ptr(ctx),
-        _ptr(cu), B, T, hq, hkv, d, bs, nb, float(scale), int(kv_split), dt, flags,
-        out.data_ptr(), workspace.data_ptr(), ws_have, _stream_ptr(q, stream)))
+    with _on_stream(stream):
+        if out is None:
+            out = torch.empty((T, hq, d), dtype=torch.float32, device=q.device)
+        _need_cuda(out)
+        ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        if workspace is None:
+            need = write_kv_attention_workspace_size(ctx, cu, hq, hkv, d, n_rows, kv_split, dt,
+                                                     phase_consistent)
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+            ws_have = workspace.numel()
+        _check(lib().pkv_write_kv_attention(
+            q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), _ptr(sl), n_rows,
+            k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+            int(block_tables.shape[1]), _ptr(ctx), _ptr(cu), B, T, hq, hkv, d, bs, nb,
+            float(scale), int(kv_split), dt, flags, out.data_ptr(), workspace.data_ptr(), ws_have,
+            _stream_ptr(q, stream)))
     return out
 
 
@@ -594,18 +610,19 @@ def write_kv_fp8(k_new, v_new, slots, k_cache, v_cache, k_scale: float, v_scale:
     if k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16:
         raise ValueError("k_new / v_new must be bfloat16")
     nb, bs, hkv, d = k_cache.shape
-    if hasattr(slots, "is_cuda") and slots.is_cuda:
-        sl = slots
-    else:
-        host = _host_i32(slots)
-        validate_slots(host, nb * bs)
-        sl = torch.from_numpy(host).to(k_cache.device)
-    if sl.dtype != torch.int32 or not sl.is_contiguous():
-        raise ValueError("slots must be a contiguous int32 tensor")
-    _check(lib().pkv_write_kv_fp8(k_new.data_ptr(), v_new.data_ptr(), sl.data_ptr(),
-                                  int(k_new.shape[0]), k_cache.data_ptr(), v_cache.data_ptr(),
-                                  nb, bs, hkv, d, float(k_scale), float(v_scale),
-                                  _stream_ptr(k_cache, stream)))
+    with _on_stream(stream):
+        if hasattr(slots, "is_cuda") and slots.is_cuda:
+            sl = slots
+        else:
+            host = _host_i32(slots)
+            validate_slots(host, nb * bs)
+            sl = torch.from_numpy(host).to(k_cache.device)
+        if sl.dtype != torch.int32 or not sl.is_contiguous():
+            raise ValueError("slots must be a contiguous int32 tensor")
+        _check(lib().pkv_write_kv_fp8(k_new.data_ptr(), v_new.data_ptr(), sl.data_ptr(),
+                                      int(k_new.shape[0]), k_cache.data_ptr(), v_cache.data_ptr(),
+                                      nb, bs, hkv, d, float(k_scale), float(v_scale),
+                                      _stream_ptr(k_cache, stream)))
 
 
 def attention_fp8_workspace_size(ctx_lens, cu_seqlens_q, num_q_heads: int, num_kv_heads: int,
@@ -644,19 +661,20 @@ def attention_fp8(q, k_cache, v_cache, block_tables, ctx_lens, cu_seqlens_q, sca
     B = ctx.size
     if block_tables.dim() != 2 or block_tables.shape[0] != B:
         raise ValueError("block_tables must be [B, max_blocks]")
-    if out is None:
-        out = torch.empty((T, hq, d), dtype=torch.float32, device=q.device)
-    _need_cuda(out)
     need = attention_fp8_workspace_size(ctx, cu, hq, hkv, d, kv_split, phase_consistent)
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     flags = PKV_ATTN_PHASE_CONSISTENT if phase_consistent else 0
-    _check(lib().pkv_attention_fp8(
-        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
-        int(block_tables.shape[1]), _ptr(ctx), _ptr(cu), B, T, hq, hkv, d, bs, nb, float(scale),
-        float(k_scale), float(v_scale), int(kv_split), flags, out.data_ptr(),
-        workspace.data_ptr(),
-        workspace.numel() * workspace.element_size(), _stream_ptr(q, stream)))
+    with _on_stream(stream):
+        if out is None:
+            out = torch.empty((T, hq, d), dtype=torch.float32, device=q.device)
+        _need_cuda(out)
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        _check(lib().pkv_attention_fp8(
+            q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+            int(block_tables.shape[1]), _ptr(ctx), _ptr(cu), B, T, hq, hkv, d, bs, nb,
+            float(scale), float(k_scale), float(v_scale), int(kv_split), flags, out.data_ptr(),
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            _stream_ptr(q, stream)))
     return out
 
 
@@ -702,20 +720,22 @@ def write_kv_attention_fp8(q, k_new, v_new, slots, k_cache, v_cache, block_table
     B = ctx.size
     if block_tables.dim() != 2 or block_tables.shape[0] != B:
         raise ValueError("block_tables must be [B, max_blocks]")
-    if out is None:
-        out = torch.empty((T, hq, d), dtype=torch.float32, device=q.device)
-    _need_cuda(out)
-    if workspace is None:
-        need = write_kv_attention_fp8_workspace_size(ctx, cu, hq, hkv, d, n_rows, kv_split,
-                                                     phase_consistent)
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     flags = PKV_ATTN_PHASE_CONSISTENT if phase_consistent else 0
-    _check(lib().pkv_write_kv_attention_fp8(
-        q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), _ptr(sl), n_rows, k_cache.data_ptr(),
-        v_cache.data_ptr(), block_tables.data_ptr(), int(block_tables.shape[1]), _ptr(ctx),
-        _ptr(cu), B, T, hq, hkv, d, bs, nb, float(scale), float(k_scale), float(v_scale),
-        int(kv_split), flags, out.data_ptr(), workspace.data_ptr(),
-        workspace.numel() * workspace.element_size(), _stream_ptr(q, stream)))
+    with _on_stream(stream):
+        if out is None:
+            out = torch.empty((T, hq, d), dtype=torch.float32, device=q.device)
+        _need_cuda(out)
+        if workspace is None:
+            need = write_kv_attention_fp8_workspace_size(ctx, cu, hq, hkv, d, n_rows, kv_split,
+                                                         phase_consistent)
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        _check(lib().pkv_write_kv_attention_fp8(
+            q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), _ptr(sl), n_rows,
+            k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+            int(block_tables.shape[1]), _ptr(ctx), _ptr(cu), B, T, hq, hkv, d, bs, nb,
+            float(scale), float(k_scale), float(v_scale), int(kv_split), flags, out.data_ptr(),
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            _stream_ptr(q, stream)))
     return out
 
 
@@ -740,3 +760,11 @@ def profile_read(kind: str) -> Tuple[float, int]:
     n = _i64(0)
     _check(lib().pkv_profile_read(KERNEL_KINDS[kind], ctypes.byref(ms), ctypes.byref(n)))
     return float(ms.value), int(n.value)
+
+
+def staging_info() -> Tuple[int, int]:
+    """(bytes per staging slot, arena allocations so far) on the current device."""
+    sb = ctypes.c_size_t(0)
+    n = _i64(0)
+    _check(lib().pkv_staging_info(ctypes.byref(sb), ctypes.byref(n)))
+    return int(sb.value), int(n.value)

@@ -22,7 +22,7 @@ ARCH = "gfx950"
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 DEVICE_SOURCES = ["write_kv.hip", "decode.hip", "decode_fp8.hip", "merge.hip", "prefill.hip"]
-HOST_SOURCES = ["allocator.cpp", "api.cpp", "scheduler.cpp"]
+HOST_SOURCES = ["allocator.cpp", "api.cpp", "planner.cpp", "scheduler.cpp"]
 
 # Packed-FP32 instructions are disabled for all device code: the compiler may not form
 # v_pk_{add,mul,fma}_f32 from ordinary float code.

@@ -235,21 +235,55 @@ extern "C" int32_t pkv_slot_mapping_step(const pkv_alloc* a, const int32_t* bloc
   return ok();
 }
 
+namespace pkv {
+
+// Every slot negative (skipped) or in [0, num_slots), no non-negative slot twice. Uses a bitmap
+// over the slots' range when that is at most 64 bits per slot (one pass, the usual case for a
+// step's slots), else a sorted copy. `what` prefixes the message.
+int32_t check_slots(const int32_t* slots, int32_t n, int64_t num_slots, const char* what) {
+  int32_t lo = INT32_MAX, hi = -1;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t s = slots[i];
+    if (s < 0) continue;
+    if (s >= num_slots)
+      return fail(PKV_ERR_INVALID, std::string(what) + ": slot " + std::to_string(s) + " outside the pool");
+    lo = std::min(lo, s);
+    hi = std::max(hi, s);
+  }
+  if (hi < 0) return PKV_OK;
+  const int64_t range = static_cast<int64_t>(hi) - lo + 1;
+  int32_t dup = -1;
+  if (range <= 64 * static_cast<int64_t>(n)) {
+    static thread_local std::vector<uint64_t> bits;
+    bits.assign(static_cast<size_t>((range + 63) / 64), 0);
+    for (int32_t i = 0; i < n && dup < 0; ++i) {
+      const int32_t s = slots[i];
+      if (s < 0) continue;
+      const int64_t k = static_cast<int64_t>(s) - lo;
+      const uint64_t m = uint64_t(1) << (k & 63);
+      if (bits[k >> 6] & m) dup = s;
+      bits[k >> 6] |= m;
+    }
+  } else {
+    static thread_local std::vector<int32_t> seen;
+    seen.clear();
+    for (int32_t i = 0; i < n; ++i)
+      if (slots[i] >= 0) seen.push_back(slots[i]);
+    std::sort(seen.begin(), seen.end());
+    auto d = std::adjacent_find(seen.begin(), seen.end());
+    if (d != seen.end()) dup = *d;
+  }
+  if (dup >= 0)
+    return fail(PKV_ERR_INVALID, std::string(what) + ": slot " + std::to_string(dup) + " appears twice");
+  return PKV_OK;
+}
+
+}  // namespace pkv
+
 extern "C" int32_t pkv_validate_slots(const int32_t* slots_host, int32_t n, int64_t num_slots) {
   if (n < 0 || (n > 0 && slots_host == nullptr))
     return fail(PKV_ERR_INVALID, "validate_slots: bad array");
-  std::vector<int32_t> seen;
-  seen.reserve(n);
-  for (int32_t i = 0; i < n; ++i) {
-    int32_t s = slots_host[i];
-    if (s < 0) continue;
-    if (s >= num_slots)
-      return fail(PKV_ERR_INVALID, "validate_slots: slot " + std::to_string(s) + " outside the pool");
-    seen.push_back(s);
-  }
-  std::sort(seen.begin(), seen.end());
-  auto dup = std::adjacent_find(seen.begin(), seen.end());
-  if (dup != seen.end())
-    return fail(PKV_ERR_INVALID, "validate_slots: slot " + std::to_string(*dup) + " appears twice");
+  const int32_t st = pkv::check_slots(slots_host, n, num_slots, "validate_slots");
+  if (st != PKV_OK) return st;
   return ok();
 }

@@ -22,14 +22,18 @@
 #include "common.h"
 #include "kernels.h"
 #include "plan.h"
+#include "planner.h"
 
 using pkv::fail;
 using pkv::ok;
 
 namespace {
 
-constexpr size_t kAlign = 256;
-size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+using pkv::align_up;
+using pkv::build_lists;
+using pkv::check_step;
+using pkv::layout_for;
+using pkv::StepShape;
 
 // The kernels move 16-byte vectors through q, the new rows, the pools and the workspace.
 bool misaligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
@@ -45,16 +49,14 @@ int elem_bytes(int32_t dt) { return dt == PKV_BF16 ? 2 : 4; }
 // covers that work. Fences are recorded every kFenceEvery calls, not every call: each event
 // record costs the stream a few microseconds. A reader left uncovered because its stream was
 // not used again before the slot came round is waited for with a device synchronisation.
+// All slots live in one pinned arena of kRingSlots equal slots. The arena is allocated by the
+// first call on a device and replaced only when a call needs more than a slot holds: then
+// every slot's last reader is waited for, and the new slot size is the next power of two at or
+// above twice the old one and the request (at least kMinSlotBytes). So a process pays at most
+// a few allocations, all before its steps reach their largest size, and none per step after.
 constexpr int kRingSlots = 16;
 constexpr int kFenceEvery = 4;
-
-struct StagingSlot {
-  void* host = nullptr;
-  void* dev = nullptr;          // device mapping of host (kernels read it in place)
-  size_t cap = 0;
-  int64_t call = -1;            // call whose copy last read this slot (-1: none)
-  hipStream_t stream = nullptr; // the stream of that copy
-};
+constexpr size_t kMinSlotBytes = size_t(1) << 20;
 
 struct Fence {
   hipEvent_t ev;
@@ -64,10 +66,21 @@ struct Fence {
 
 struct DeviceRing {
   std::mutex mu;
-  StagingSlot slots[kRingSlots];
+  char* host = nullptr;        // pinned arena: kRingSlots slots of slot_cap bytes
+  char* dev = nullptr;         // its device mapping (kernels read it in place)
+  size_t slot_cap = 0;
+  int64_t grows = 0;           // arena (re)allocations so far
+  int64_t slot_call[kRingSlots];          // call whose reader last used the slot (-1: none)
+  hipStream_t slot_stream[kRingSlots];    // the stream of that reader
   int64_t calls = 0;
   std::deque<Fence> fences;       // in record order
   std::vector<hipEvent_t> spare;  // event objects for reuse
+  DeviceRing() {
+    for (int i = 0; i < kRingSlots; ++i) {
+      slot_call[i] = -1;
+      slot_stream[i] = nullptr;
+    }
+  }
 };
 
 std::mutex g_rings_mu;
@@ -93,7 +106,7 @@ void drop_completed_fences(DeviceRing* r) {
   }
 }
 
-// Blocks until the copy of call `call` on `stream` has completed.
+// Blocks until the reader of call `call` on `stream` has completed.
 hipError_t wait_for_copy(DeviceRing* r, int64_t call, hipStream_t stream) {
   for (const Fence& f : r->fences) {
     if (f.stream == stream && f.covers >= call) {
@@ -129,48 +142,66 @@ hipError_t record_fence(DeviceRing* r, hipStream_t stream, int64_t covers) {
   return hipSuccess;
 }
 
-// Copies `bytes` of host-built data to device memory dst on stream strm through the current
-// device's staging ring; fill(host) writes the data into the staging buffer.
+// Makes every slot of the ring hold at least `bytes` (caller holds r->mu). Waits for every
+// slot's last reader before the old arena is released.
+hipError_t ring_reserve(DeviceRing* r, size_t bytes) {
+  if (bytes <= r->slot_cap && r->host != nullptr) return hipSuccess;
+  for (int i = 0; i < kRingSlots; ++i) {
+    if (r->slot_call[i] < 0) continue;
+    hipError_t e = wait_for_copy(r, r->slot_call[i], r->slot_stream[i]);
+    if (e != hipSuccess) return e;
+    r->slot_call[i] = -1;
+  }
+  size_t cap = std::max(kMinSlotBytes, 2 * r->slot_cap);
+  while (cap < bytes) cap *= 2;
+  if (r->host != nullptr) (void)hipHostFree(r->host);
+  r->host = nullptr;
+  r->dev = nullptr;
+  r->slot_cap = 0;
+  void* h = nullptr;
+  hipError_t e = hipHostMalloc(&h, cap * kRingSlots, hipHostMallocDefault);
+  if (e != hipSuccess) return e;
+  void* d = nullptr;
+  e = hipHostGetDevicePointer(&d, h, 0);
+  if (e != hipSuccess) {
+    (void)hipHostFree(h);
+    return e;
+  }
+  r->host = static_cast<char*>(h);
+  r->dev = static_cast<char*>(d);
+  r->slot_cap = cap;
+  r->grows += 1;
+  return hipSuccess;
+}
+
 // Stages `bytes` of host-built data in the current device's ring (fill(host) writes them) and
-// enqueues run(dev) on strm, the device work that reads them (through the device mapping dev of
-// the staging buffer, or with a copy); run returns a status.
+// enqueues run(host, dev) on strm, the device work that reads them (through the device mapping
+// dev of the staging buffer, or with a copy from host); run returns a status.
 template <typename Fill, typename Run>
 int32_t stage_and_run(size_t bytes, hipStream_t strm, const char* what, Fill fill, Run run) {
   int dev = 0;
   DeviceRing* ring = ring_for_current_device(&dev);
   if (ring == nullptr) return fail(PKV_ERR_HIP, std::string(what) + ": hipGetDevice failed");
   std::lock_guard<std::mutex> lk(ring->mu);
+  hipError_t e = ring_reserve(ring, bytes);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string(what) + ": pinned staging: " + hipGetErrorString(e));
   const int64_t call = ring->calls;
-  StagingSlot& slot = ring->slots[call % kRingSlots];
-  if (slot.call >= 0) {
-    hipError_t e = wait_for_copy(ring, slot.call, slot.stream);
+  const int si = static_cast<int>(call % kRingSlots);
+  if (ring->slot_call[si] >= 0) {
+    e = wait_for_copy(ring, ring->slot_call[si], ring->slot_stream[si]);
     if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string(what) + ": staging wait: " + hipGetErrorString(e));
-    slot.call = -1;
+    ring->slot_call[si] = -1;
   }
-  if (slot.cap < bytes) {
-    if (slot.host != nullptr) (void)hipHostFree(slot.host);
-    slot.host = nullptr;
-    slot.cap = 0;
-    const size_t want = std::max<size_t>(bytes, 1 << 16);
-    hipError_t e = hipHostMalloc(&slot.host, want, hipHostMallocDefault);
-    if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string(what) + ": pinned staging: " + hipGetErrorString(e));
-    e = hipHostGetDevicePointer(&slot.dev, slot.host, 0);
-    if (e != hipSuccess) {
-      (void)hipHostFree(slot.host);
-      slot.host = nullptr;
-      slot.dev = nullptr;
-      return fail(PKV_ERR_HIP, std::string(what) + ": staging mapping: " + hipGetErrorString(e));
-    }
-    slot.cap = want;
-  }
-  fill(static_cast<char*>(slot.host));
-  const int32_t rs = run(static_cast<const char*>(slot.host), static_cast<const char*>(slot.dev));
+  char* host = ring->host + static_cast<size_t>(si) * ring->slot_cap;
+  const char* devp = ring->dev + static_cast<size_t>(si) * ring->slot_cap;
+  fill(host);
+  const int32_t rs = run(static_cast<const char*>(host), devp);
   if (rs != PKV_OK) return rs;
   ring->calls = call + 1;
-  slot.call = call;
-  slot.stream = strm;
+  ring->slot_call[si] = call;
+  ring->slot_stream[si] = strm;
   if (call % kFenceEvery == kFenceEvery - 1) {
-    const hipError_t e = record_fence(ring, strm, call);
+    e = record_fence(ring, strm, call);
     if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string(what) + ": fence: " + hipGetErrorString(e));
   }
   return PKV_OK;
@@ -268,172 +299,6 @@ void prof_end(int idx, hipStream_t s) {
   if (idx < 0) return;
   std::lock_guard<std::mutex> lk(g_prof_mu);
   (void)hipEventRecord(g_prof_pending[idx].b, s);
-}
-
-// ---- work planning ----------------------------------------------------------------------
-struct StepShape {
-  const int32_t* ctx;
-  const int32_t* cu;
-  int32_t B;
-  int32_t kv_split;
-  bool prefill_on_mfma;  // segments with q_len > 1 use the prefill kernel
-  bool all_mfma;         // phase-consistent mode: every segment (decode rows too) uses it
-  int32_t prefill_rows_per_item;
-  int32_t tile_split;    // > 0 (phase-consistent mode: kv_split): tile items cover one KV split
-};
-
-// Whether segment b (q_len ql >= 1) runs on the prefill tile kernel.
-bool on_tiles(const StepShape& s, int32_t ql) { return s.all_mfma || (ql > 1 && s.prefill_on_mfma); }
-
-int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
-// Counts and layout only (no lists). n_write_rows > 0 reserves the slot array of a fused KV
-// append after the work lists (copied from the host with them).
-pkv::WorkspaceLayout layout_for(const StepShape& s, int32_t hq, int32_t head_dim,
-                                int32_t n_write_rows = 0) {
-  pkv::WorkspaceLayout L;
-  for (int32_t b = 0; b < s.B; ++b) {
-    const int32_t ql = s.cu[b + 1] - s.cu[b];
-    if (ql == 0) continue;
-    if (on_tiles(s, ql)) {
-      const int32_t prior = s.ctx[b] - ql;
-      if (s.tile_split == 0) {
-        L.n_prefill += ceil_div(ql, s.prefill_rows_per_item);
-        continue;
-      }
-      // an item per row chunk and split reached by its last row; split partials for every row
-      // of a segment whose context reaches past split 0, and a merge per such row
-      for (int32_t r0 = 0; r0 < ql; r0 += s.prefill_rows_per_item) {
-        const int32_t last = prior + std::min(r0 + s.prefill_rows_per_item, ql) - 1;
-        L.n_prefill += last / s.tile_split + 1;
-      }
-      const int64_t ns_max = ceil_div(s.ctx[b], s.tile_split);
-      if (ns_max > 1) {
-        L.n_part += static_cast<int64_t>(ql) * ns_max;
-        L.n_merge += prior + ql - std::max(prior, s.tile_split);
-      }
-      continue;
-    }
-    for (int32_t i = 0; i < ql; ++i) {
-      const int64_t n_keys = static_cast<int64_t>(s.ctx[b]) - ql + i + 1;
-      const int64_t ns = ceil_div(n_keys, s.kv_split);
-      L.n_decode += ns;
-      if (ns > 1) {
-        L.n_merge += 1;
-        L.n_part += ns;
-      }
-    }
-  }
-  size_t off = 0;
-  L.decode_off = off;
-  off = align_up(off + L.n_decode * sizeof(pkv::DecodeItem));
-  L.merge_off = off;
-  off = align_up(off + L.n_merge * sizeof(pkv::MergeItem));
-  L.prefill_off = off;
-  off = align_up(off + L.n_prefill * sizeof(pkv::PrefillItem));
-  L.slots_off = off;
-  off = align_up(off + static_cast<size_t>(n_write_rows) * sizeof(int32_t));
-  L.list_bytes = off;
-  L.part_m_off = off;
-  off = align_up(off + L.n_part * hq * sizeof(float));
-  L.part_l_off = off;
-  off = align_up(off + L.n_part * hq * sizeof(float));
-  L.part_acc_off = off;
-  off = align_up(off + L.n_part * hq * head_dim * sizeof(float));
-  L.total = off;
-  return L;
-}
-
-void build_lists(const StepShape& s, const pkv::WorkspaceLayout& L, char* host) {
-  auto* dec = reinterpret_cast<pkv::DecodeItem*>(host + L.decode_off);
-  auto* mer = reinterpret_cast<pkv::MergeItem*>(host + L.merge_off);
-  auto* pre = reinterpret_cast<pkv::PrefillItem*>(host + L.prefill_off);
-  int64_t nd = 0, nm = 0, np = 0, part = 0;
-  for (int32_t b = 0; b < s.B; ++b) {
-    const int32_t ql = s.cu[b + 1] - s.cu[b];
-    if (ql == 0) continue;
-    if (on_tiles(s, ql)) {
-      const int32_t prior = s.ctx[b] - ql;
-      const int32_t S = s.tile_split;
-      const int32_t ns_max = S > 0 ? static_cast<int32_t>(ceil_div(s.ctx[b], S)) : 1;
-      const int32_t pbase = ns_max > 1 ? static_cast<int32_t>(part) : -1;
-      if (ns_max > 1) {
-        part += static_cast<int64_t>(ql) * ns_max;
-        for (int32_t i = std::max(0, S - prior); i < ql; ++i)   // rows at positions >= S
-          mer[nm++] = pkv::MergeItem{s.cu[b] + i, (prior + i) / S + 1, pbase + i * ns_max, 0};
-      }
-      for (int32_t r0 = 0; r0 < ql; r0 += s.prefill_rows_per_item) {
-        const int32_t n = std::min(s.prefill_rows_per_item, ql - r0);
-        const int32_t n_splits = S > 0 ? (prior + r0 + n - 1) / S + 1 : 1;
-        for (int32_t sp = 0; sp < n_splits; ++sp) {
-          pkv::PrefillItem& p = pre[np++];
-          p.seq = b;
-          p.row0 = s.cu[b] + r0;
-          p.n_rows = n;
-          p.pos0 = prior + r0;
-          p.split = sp;
-          p.part = pbase < 0 ? -1 : pbase + r0 * ns_max;
-          p.pstride = ns_max;
-          p.pad = 0;
-        }
-      }
-      continue;
-    }
-    for (int32_t i = 0; i < ql; ++i) {
-      const int32_t row = s.cu[b] + i;
-      const int32_t n_keys = s.ctx[b] - ql + i + 1;
-      const int32_t ns = static_cast<int32_t>(ceil_div(n_keys, s.kv_split));
-      int32_t pbase = -1;
-      if (ns > 1) {
-        pbase = static_cast<int32_t>(part);
-        mer[nm++] = pkv::MergeItem{row, ns, pbase, 0};
-        part += ns;
-      }
-      for (int32_t sp = 0; sp < ns; ++sp) dec[nd++] = pkv::DecodeItem{row, b, n_keys, sp, pbase, 0, 0, 0};
-    }
-  }
-  // longest work first: short tail items then fill the gaps at the end of each launch (item
-  // order never affects any row's bits). A prefill item's work grows with its last key.
-  const auto pre_keys = [&](const pkv::PrefillItem& x) -> int64_t {
-    const int64_t end = x.pos0 + x.n_rows;
-    if (s.tile_split == 0) return end;
-    const int64_t k0 = static_cast<int64_t>(x.split) * s.tile_split;
-    return std::min<int64_t>(end, k0 + s.tile_split) - k0;
-  };
-  std::stable_sort(pre, pre + np, [&](const pkv::PrefillItem& x, const pkv::PrefillItem& y) {
-    return pre_keys(x) > pre_keys(y);
-  });
-  std::stable_sort(dec, dec + nd, [&](const pkv::DecodeItem& x, const pkv::DecodeItem& y) {
-    const int64_t kx = std::min<int64_t>(x.n_keys - static_cast<int64_t>(x.split) * s.kv_split, s.kv_split);
-    const int64_t ky = std::min<int64_t>(y.n_keys - static_cast<int64_t>(y.split) * s.kv_split, s.kv_split);
-    return kx > ky;
-  });
-}
-
-
-int32_t check_step(const int32_t* ctx, const int32_t* cu, int32_t B, int32_t T,
-                   int64_t max_keys) {
-  if (B < 0 || T < 0) return fail(PKV_ERR_INVALID, "B and T must be >= 0");
-  if (B > 0 && (ctx == nullptr || cu == nullptr))
-    return fail(PKV_ERR_INVALID, "ctx_lens_host / cu_seqlens_q_host is NULL");
-  if (B == 0) {
-    if (T != 0) return fail(PKV_ERR_INVALID, "T must be 0 when B is 0");
-    return PKV_OK;
-  }
-  if (cu[0] != 0) return fail(PKV_ERR_INVALID, "cu_seqlens_q[0] must be 0");
-  for (int32_t b = 0; b < B; ++b) {
-    const int32_t ql = cu[b + 1] - cu[b];
-    if (cu[b + 1] < cu[b]) return fail(PKV_ERR_INVALID, "cu_seqlens_q must be non-decreasing");
-    if (ctx[b] < 0) return fail(PKV_ERR_INVALID, "ctx_lens must be >= 0");
-    if (ql > ctx[b])
-      return fail(PKV_ERR_INVALID, "sequence " + std::to_string(b) + ": q_len " +
-                                       std::to_string(ql) + " > ctx_len " + std::to_string(ctx[b]));
-    if (max_keys >= 0 && ctx[b] > max_keys)
-      return fail(PKV_ERR_INVALID, "sequence " + std::to_string(b) +
-                                       ": ctx_len exceeds max_blocks * block_size");
-  }
-  if (cu[B] != T) return fail(PKV_ERR_INVALID, "cu_seqlens_q[B] must equal T");
-  return PKV_OK;
 }
 
 // kv_split: a positive multiple of 64, at most 2048 for the split decode pass; the
@@ -599,10 +464,10 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
   const int64_t n_slots = wr != nullptr ? wr->n_slots : (wr8 != nullptr ? wr8->n_slots : 0);
   if (n_write > 0) {
     if (slots_host == nullptr) return fail(PKV_ERR_INVALID, "write_kv_attention: slots_host is NULL");
-    for (int32_t i = 0; i < n_write; ++i)
-      if (slots_host[i] >= n_slots)
-        return fail(PKV_ERR_INVALID, "write_kv_attention: slot " + std::to_string(slots_host[i]) +
-                                         " outside the pool");
+    // range and duplicates: without an order between two rows sent to one slot, the slot's
+    // contents after the append would be undefined
+    st = pkv::check_slots(slots_host, n_write, n_slots, "write_kv_attention");
+    if (st != PKV_OK) return st;
   }
   if (T == 0 && n_write == 0) return ok();
   if (T > 0 && (q == nullptr || k_cache == nullptr || v_cache == nullptr ||
@@ -1055,5 +920,15 @@ extern "C" int32_t pkv_profile_read(int32_t kernel_kind, double* total_ms, int64
   g_prof_pending.clear();
   *total_ms = g_prof_ms[kernel_kind];
   *launches = g_prof_n[kernel_kind];
+  return ok();
+}
+
+extern "C" int32_t pkv_staging_info(size_t* slot_bytes, int64_t* allocations) {
+  int dev = 0;
+  DeviceRing* ring = ring_for_current_device(&dev);
+  if (ring == nullptr) return fail(PKV_ERR_HIP, "staging_info: hipGetDevice failed");
+  std::lock_guard<std::mutex> lk(ring->mu);
+  if (slot_bytes != nullptr) *slot_bytes = ring->slot_cap;
+  if (allocations != nullptr) *allocations = ring->grows;
   return ok();
 }

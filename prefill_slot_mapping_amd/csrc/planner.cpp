@@ -1,0 +1,165 @@
+// Host work planner (declarations and the rules it follows in planner.h).
+#include "planner.h"
+
+#include <algorithm>
+#include <string>
+
+#include "common.h"
+
+namespace pkv {
+
+namespace {
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+}  // namespace
+
+bool on_tiles(const StepShape& s, int32_t ql) { return s.all_mfma || (ql > 1 && s.prefill_on_mfma); }
+
+
+WorkspaceLayout layout_for(const StepShape& s, int32_t hq, int32_t head_dim,
+                           int32_t n_write_rows) {
+  WorkspaceLayout L;
+  for (int32_t b = 0; b < s.B; ++b) {
+    const int32_t ql = s.cu[b + 1] - s.cu[b];
+    if (ql == 0) continue;
+    if (on_tiles(s, ql)) {
+      const int32_t prior = s.ctx[b] - ql;
+      if (s.tile_split == 0) {
+        L.n_prefill += ceil_div(ql, s.prefill_rows_per_item);
+        continue;
+      }
+      // an item per row chunk and split reached by its last row; split partials for every row
+      // of a segment whose context reaches past split 0, and a merge per such row
+      for (int32_t r0 = 0; r0 < ql; r0 += s.prefill_rows_per_item) {
+        const int32_t last = prior + std::min(r0 + s.prefill_rows_per_item, ql) - 1;
+        L.n_prefill += last / s.tile_split + 1;
+      }
+      const int64_t ns_max = ceil_div(s.ctx[b], s.tile_split);
+      if (ns_max > 1) {
+        L.n_part += static_cast<int64_t>(ql) * ns_max;
+        L.n_merge += prior + ql - std::max(prior, s.tile_split);
+      }
+      continue;
+    }
+    for (int32_t i = 0; i < ql; ++i) {
+      const int64_t n_keys = static_cast<int64_t>(s.ctx[b]) - ql + i + 1;
+      const int64_t ns = ceil_div(n_keys, s.kv_split);
+      L.n_decode += ns;
+      if (ns > 1) {
+        L.n_merge += 1;
+        L.n_part += ns;
+      }
+    }
+  }
+  size_t off = 0;
+  L.decode_off = off;
+  off = align_up(off + L.n_decode * sizeof(DecodeItem));
+  L.merge_off = off;
+  off = align_up(off + L.n_merge * sizeof(MergeItem));
+  L.prefill_off = off;
+  off = align_up(off + L.n_prefill * sizeof(PrefillItem));
+  L.slots_off = off;
+  off = align_up(off + static_cast<size_t>(n_write_rows) * sizeof(int32_t));
+  L.list_bytes = off;
+  L.part_m_off = off;
+  off = align_up(off + L.n_part * hq * sizeof(float));
+  L.part_l_off = off;
+  off = align_up(off + L.n_part * hq * sizeof(float));
+  L.part_acc_off = off;
+  off = align_up(off + L.n_part * hq * head_dim * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+void build_lists(const StepShape& s, const WorkspaceLayout& L, char* host) {
+  auto* dec = reinterpret_cast<DecodeItem*>(host + L.decode_off);
+  auto* mer = reinterpret_cast<MergeItem*>(host + L.merge_off);
+  auto* pre = reinterpret_cast<PrefillItem*>(host + L.prefill_off);
+  int64_t nd = 0, nm = 0, np = 0, part = 0;
+  for (int32_t b = 0; b < s.B; ++b) {
+    const int32_t ql = s.cu[b + 1] - s.cu[b];
+    if (ql == 0) continue;
+    if (on_tiles(s, ql)) {
+      const int32_t prior = s.ctx[b] - ql;
+      const int32_t S = s.tile_split;
+      const int32_t ns_max = S > 0 ? static_cast<int32_t>(ceil_div(s.ctx[b], S)) : 1;
+      const int32_t pbase = ns_max > 1 ? static_cast<int32_t>(part) : -1;
+      if (ns_max > 1) {
+        part += static_cast<int64_t>(ql) * ns_max;
+        for (int32_t i = std::max(0, S - prior); i < ql; ++i)   // rows at positions >= S
+          mer[nm++] = MergeItem{s.cu[b] + i, (prior + i) / S + 1, pbase + i * ns_max, 0};
+      }
+      for (int32_t r0 = 0; r0 < ql; r0 += s.prefill_rows_per_item) {
+        const int32_t n = std::min(s.prefill_rows_per_item, ql - r0);
+        const int32_t n_splits = S > 0 ? (prior + r0 + n - 1) / S + 1 : 1;
+        for (int32_t sp = 0; sp < n_splits; ++sp) {
+          PrefillItem& p = pre[np++];
+          p.seq = b;
+          p.row0 = s.cu[b] + r0;
+          p.n_rows = n;
+          p.pos0 = prior + r0;
+          p.split = sp;
+          p.part = pbase < 0 ? -1 : pbase + r0 * ns_max;
+          p.pstride = ns_max;
+          p.pad = 0;
+        }
+      }
+      continue;
+    }
+    for (int32_t i = 0; i < ql; ++i) {
+      const int32_t row = s.cu[b] + i;
+      const int32_t n_keys = s.ctx[b] - ql + i + 1;
+      const int32_t ns = static_cast<int32_t>(ceil_div(n_keys, s.kv_split));
+      int32_t pbase = -1;
+      if (ns > 1) {
+        pbase = static_cast<int32_t>(part);
+        mer[nm++] = MergeItem{row, ns, pbase, 0};
+        part += ns;
+      }
+      for (int32_t sp = 0; sp < ns; ++sp) dec[nd++] = DecodeItem{row, b, n_keys, sp, pbase, 0, 0, 0};
+    }
+  }
+  // longest work first: short tail items then fill the gaps at the end of each launch (item
+  // order never affects any row's bits). A prefill item's work grows with its last key.
+  const auto pre_keys = [&](const PrefillItem& x) -> int64_t {
+    const int64_t end = x.pos0 + x.n_rows;
+    if (s.tile_split == 0) return end;
+    const int64_t k0 = static_cast<int64_t>(x.split) * s.tile_split;
+    return std::min<int64_t>(end, k0 + s.tile_split) - k0;
+  };
+  std::stable_sort(pre, pre + np, [&](const PrefillItem& x, const PrefillItem& y) {
+    return pre_keys(x) > pre_keys(y);
+  });
+  std::stable_sort(dec, dec + nd, [&](const DecodeItem& x, const DecodeItem& y) {
+    const int64_t kx = std::min<int64_t>(x.n_keys - static_cast<int64_t>(x.split) * s.kv_split, s.kv_split);
+    const int64_t ky = std::min<int64_t>(y.n_keys - static_cast<int64_t>(y.split) * s.kv_split, s.kv_split);
+    return kx > ky;
+  });
+}
+
+
+int32_t check_step(const int32_t* ctx, const int32_t* cu, int32_t B, int32_t T,
+                   int64_t max_keys) {
+  if (B < 0 || T < 0) return fail(PKV_ERR_INVALID, "B and T must be >= 0");
+  if (B > 0 && (ctx == nullptr || cu == nullptr))
+    return fail(PKV_ERR_INVALID, "ctx_lens_host / cu_seqlens_q_host is NULL");
+  if (B == 0) {
+    if (T != 0) return fail(PKV_ERR_INVALID, "T must be 0 when B is 0");
+    return PKV_OK;
+  }
+  if (cu[0] != 0) return fail(PKV_ERR_INVALID, "cu_seqlens_q[0] must be 0");
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t ql = cu[b + 1] - cu[b];
+    if (cu[b + 1] < cu[b]) return fail(PKV_ERR_INVALID, "cu_seqlens_q must be non-decreasing");
+    if (ctx[b] < 0) return fail(PKV_ERR_INVALID, "ctx_lens must be >= 0");
+    if (ql > ctx[b])
+      return fail(PKV_ERR_INVALID, "sequence " + std::to_string(b) + ": q_len " +
+                                       std::to_string(ql) + " > ctx_len " + std::to_string(ctx[b]));
+    if (max_keys >= 0 && ctx[b] > max_keys)
+      return fail(PKV_ERR_INVALID, "sequence " + std::to_string(b) +
+                                       ": ctx_len exceeds max_blocks * block_size");
+  }
+  if (cu[B] != T) return fail(PKV_ERR_INVALID, "cu_seqlens_q[B] must equal T");
+  return PKV_OK;
+}
+
+}  // namespace pkv

@@ -304,6 +304,8 @@ def _fused(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(slots=[3, -1, 64]), L.PKV_ERR_INVALID),           # slot == num_blocks * block_size
+    (dict(slots=[3, -1, 3]), L.PKV_ERR_INVALID),            # one slot twice
+    (dict(slots=[60, 2, 60]), L.PKV_ERR_INVALID),
     (dict(n=-1), L.PKV_ERR_INVALID),                        # negative row count
     (dict(slots=None), L.PKV_ERR_INVALID),                  # NULL host slots
     (dict(kn=0), L.PKV_ERR_INVALID),                        # NULL k_new
@@ -445,6 +447,8 @@ def test_fused_fp8_step_validation():
                                               0.1, ks, 0.5, 512, flags, F, F, wsb, None)
     assert call(slots=(3, -1, 64)) == L.PKV_ERR_INVALID       # slot outside the pool
     assert b"outside" in pkv.lib().pkv_last_error()
+    assert call(slots=(7, 7, -1)) == L.PKV_ERR_INVALID        # one slot twice
+    assert b"twice" in pkv.lib().pkv_last_error()
     assert call(ks=-1.0) == L.PKV_ERR_INVALID
     assert call(hq=16) == L.PKV_ERR_UNSUPPORTED
     assert call(wsb=16) == L.PKV_ERR_INVALID
@@ -453,3 +457,16 @@ def test_fused_fp8_step_validation():
     a = pkv.attention_fp8_workspace_size([5, 9], [0, 1, 3], 8, 2, 128, 512)
     b = pkv.write_kv_attention_fp8_workspace_size([5, 9], [0, 1, 3], 8, 2, 128, 1000, 512)
     assert b >= a + 4 * 1000
+
+
+def test_fused_step_refuses_duplicate_slots_on_both_check_paths():
+    """Duplicates are found whether the slots' range is dense (bitmap) or sparse (sorted copy);
+    negative slots may repeat (padding)."""
+    big = 1 << 20
+    assert _fused(slots=[5, 1, 5], nb=big // 16) == L.PKV_ERR_INVALID
+    assert b"appears twice" in pkv.lib().pkv_last_error()
+    assert _fused(slots=[0, big - 1, 0], nb=big // 16) == L.PKV_ERR_INVALID
+    assert b"appears twice" in pkv.lib().pkv_last_error()
+    # distinct slots and repeated padding pass the slot check (then stop at the workspace)
+    assert _fused(slots=[0, -1, -1], n=3, wsb=16) == L.PKV_ERR_INVALID
+    assert b"workspace" in pkv.lib().pkv_last_error()
