@@ -15,6 +15,16 @@ GB/s (KV bytes read + append bytes moved, per step time). The mixed ragged step
 batched decode step over E4M3 pools with per-tensor scales (pkv_write_kv_attention_fp8; its
 bytes counted at one byte per cached element).
 
+The long-context decode step (8 x 40960 keys, G 8, block 32) and the prefix-shared group decode
+step (16 groups x 8 samples sharing a 2048-token prompt) are timed the same way; decode-only
+steps carry a `roofline` object for their decode kernel (the prefix-shared step also on unique
+bytes). Each workload also gets the flushed-cache protocol (median, p10 and p90 of HIP-event
+step times over `--protocol-reps` reps, each after a 2 GiB scratch write that evicts L2 and the
+MALL) and bitwise invariance verdicts (sampled sequences alone, and for shared prompts each
+group, against the batched step). The cpu_baseline leg times the oracle on the headline
+workload and compares the oracle's rows with sampled GPU rows of every timed workload
+(`parity_vs_oracle`).
+
 Prints ONE JSON line (rank 0, N = 1). `--gpus N` with N > 1 exits: this build runs on one GPU.
 """
 from __future__ import annotations
@@ -39,8 +49,12 @@ def _parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="batched-bf16-decode")
-    ap.add_argument("--extra", default="mixed-ragged-step,batched-fp8-decode,mixed-fp8-step",
+    ap.add_argument("--extra", default="mixed-ragged-step,long-context-decode,"
+                                       "prefix-shared-decode,batched-fp8-decode,mixed-fp8-step",
                     help="comma-separated workloads timed the same way, reported under 'extra'")
+    ap.add_argument("--protocol-reps", type=int, default=50,
+                    help="reps of the flushed-cache protocol per workload (median, p10, p90 of "
+                         "HIP-event step times, a 2 GiB scratch write before each rep); 0: off")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -83,8 +97,100 @@ def _kv_bytes(w):
     return acc.decode_kv_bytes(w.ctx_lens, w.spec.Hkv, w.spec.D, w.kv_elem_bytes)
 
 
+def _sample_rows(w, seed=11):
+    """Sequences and query rows whose outputs are compared with the oracle: four decode
+    sequences, the longest sequence and two prefill segments, a few rows of each."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    dec = [b for b in range(w.B) if w.q_lens[b] == 1]
+    pre = [b for b in range(w.B) if w.q_lens[b] > 1]
+    seqs = set(rng.choice(dec, size=min(4, len(dec)), replace=False).tolist()) if dec else set()
+    seqs.add(int(np.argmax(w.ctx_lens)))
+    if pre:
+        seqs |= set(rng.choice(pre, size=min(2, len(pre)), replace=False).tolist())
+    rows = []
+    for b in sorted(seqs):
+        lo, hi = int(w.cu_seqlens_q[b]), int(w.cu_seqlens_q[b + 1])
+        rows += sorted(set([lo, hi - 1, (lo + hi) // 2] +
+                           rng.integers(lo, hi, size=min(3, hi - lo)).tolist()))
+    return sorted(int(b) for b in seqs), rows
+
+
+def _invariance(w, gst, out, split, phase_consistent):
+    """Bitwise verdicts of the step's rows against the same rows computed in other batches:
+    each sequence of a sample alone (all sequences of a prefix-sharing step, each also with
+    its group), through the attention entry point on the same pools."""
+    import numpy as np
+    import torch
+    import prefill_slot_mapping_amd as pkv
+    s = w.spec
+    full = out.detach().cpu().numpy()
+
+    def run(seqs):
+        seqs = list(seqs)
+        rows = np.concatenate([np.arange(w.cu_seqlens_q[b], w.cu_seqlens_q[b + 1])
+                               for b in seqs]).astype(np.int64)
+        cu = np.concatenate([[0], np.cumsum([w.q_lens[b] for b in seqs])]).astype(np.int32)
+        q = gst.q.index_select(0, torch.from_numpy(rows).to(gst.q.device)).contiguous()
+        bt = gst.block_tables_dev[torch.as_tensor(seqs, device=gst.q.device)].contiguous()
+        ctx = np.asarray([w.ctx_lens[b] for b in seqs], np.int32)
+        if w.kv_fp8:
+            o = pkv.attention_fp8(q, gst.k_cache, gst.v_cache, bt, ctx, cu, w.scale, s.k_scale,
+                                  s.v_scale, kv_split=split, phase_consistent=phase_consistent)
+        else:
+            o = pkv.attention(q, gst.k_cache, gst.v_cache, bt, ctx, cu, w.scale, kv_split=split,
+                              phase_consistent=phase_consistent)
+        return rows, o.cpu().numpy()
+
+    live = [b for b in range(w.B) if w.q_lens[b] > 0]
+    if (w.group_of >= 0).any():
+        alone = live
+    else:
+        rng = np.random.default_rng(5)
+        alone = sorted(set(rng.choice(live, size=min(8, len(live)), replace=False).tolist())
+                       | {int(np.argmax(w.ctx_lens))} | {b for b in live if w.q_lens[b] > 1})
+    bad_alone = 0
+    for b in alone:
+        rows, o = run([b])
+        bad_alone += int(not np.array_equal(o.view(np.uint32), full[rows].view(np.uint32)))
+    verdict = {"alone_vs_batch": {"sequences": len(alone), "bitwise_equal": len(alone) - bad_alone}}
+    groups = sorted(set(int(g) for g in w.group_of if g >= 0))
+    if groups:
+        bad = 0
+        for g in groups:
+            rows, o = run(np.flatnonzero(w.group_of == g).tolist())
+            bad += int(not np.array_equal(o.view(np.uint32), full[rows].view(np.uint32)))
+        verdict["group_vs_batch"] = {"groups": len(groups), "bitwise_equal": len(groups) - bad}
+    verdict["all_bitwise"] = all(v.get("bitwise_equal") == v.get("sequences", v.get("groups"))
+                                 for v in verdict.values() if isinstance(v, dict))
+    return verdict
+
+
+def _protocol(step, reps, device, value_of):
+    """Flushed-cache timing: before each rep a 2 GiB scratch write evicts L2 and the 256 MB
+    MALL (and keeps the GPU busy while the host enqueues the step); HIP events on the stream
+    bracket the step. Returns the median and p10 / p90 of the reps."""
+    import numpy as np
+    import torch
+    flush = torch.empty(1 << 29, dtype=torch.float32, device=device)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for i in range(reps):
+        flush.fill_(float(i))
+        evs[i][0].record()
+        step()
+        evs[i][1].record()
+    torch.cuda.synchronize(device)
+    ms = np.array([a.elapsed_time(z) for a, z in evs])
+    del flush
+    p10, med, p90 = (float(x) for x in np.percentile(ms, [10, 50, 90]))
+    return {"reps": reps, "flush_bytes": 1 << 31, "median_ms": med, "p10_ms": p10,
+            "p90_ms": p90, "median_value": value_of(med), "p10_value": value_of(p90),
+            "p90_value": value_of(p10)}
+
+
 def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
-                  kernel_events="timed", cold_steps=20, kv_split=None):
+                  kernel_events="timed", cold_steps=20, kv_split=None, protocol_reps=0):
     """Build the step, then time `steps` whole steps; returns a result dict. With
     phase_consistent the attention runs with PKV_ATTN_PHASE_CONSISTENT (decode rows on the
     prefill tile path, bitwise equal to the same tokens inside prefill chunks)."""
@@ -157,6 +263,7 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
         pkv.profile_set_kinds([])
         pkv.profile_enable(True)
     torch.cuda.synchronize(device)
+    stage0 = pkv.staging_info()
     host_ends = []
     t0 = time.perf_counter()
     for i in range(steps):
@@ -166,6 +273,7 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
         host_ends.append(time.perf_counter())
     torch.cuda.synchronize(device)
     dt = time.perf_counter() - t0
+    stage1 = pkv.staging_info()
     gc.callbacks.remove(on_gc)
     gc.unfreeze()
     host_ms = np.diff(np.array([t0] + host_ends)) * 1e3
@@ -204,6 +312,18 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
 
     ms_step = dt / steps * 1e3
     kv = _kv_bytes(w)
+    app0 = acc.append_bytes(w.T, s.Hkv, s.D, w.elem_bytes, w.kv_elem_bytes)
+    decode_only0 = bool((w.q_lens <= 1).all())
+
+    def value_of(ms):
+        # decode-only steps: GB/s of KV read + append; steps with prefill rows: tokens/s
+        return (kv + app0) / (ms * 1e-3) / 1e9 if decode_only0 else w.T / (ms * 1e-3)
+
+    proto = _protocol(step, protocol_reps, device, value_of) if protocol_reps > 0 else None
+    inv = _invariance(w, gst, out, split, phase_consistent)
+    seqs_s, rows_s = _sample_rows(w)
+    sample = {"seqs": seqs_s, "rows": rows_s,
+              "gpu": out[rows_s].detach().cpu().numpy().astype("float64")}
     app = acc.append_bytes(w.T, s.Hkv, s.D, w.elem_bytes, w.kv_elem_bytes)
     decode_rows = w.q_lens == 1
     decode_only = bool((w.q_lens <= 1).all())
@@ -230,13 +350,37 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
         "timed_region_kernel": timed,
         "cold_cache_kernel": cold,
         "kernel_launches": {k: v[1] for k, v in kern.items()},
+        "staging_allocations_in_timed_region": stage1[1] - stage0[1],
+        "staging_slot_bytes": stage1[0],
+        "protocol": proto,
+        "protocol_unit": "GB/s" if decode_only0 else "tokens/s",
+        "invariance": inv,
     }
     t_roof = max((kv + app) / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12))
     res["roofline_frac_step"] = t_roof / (ms_step * 1e-3)
     res["_gst"] = gst
     res["_w"] = w
     res["_out"] = out
+    res["_sample"] = sample
     return res
+
+
+def oracle_parity(samples):
+    """Part of the cpu_baseline leg: for each timed workload, the oracle's rows for the
+    sampled sequences against the GPU rows copied out of that workload's last timed step.
+    Returns {workload: {rows, max_abs_err, tolerance, within}}."""
+    import numpy as np
+    from oracle import build_oracle_step
+    out = {}
+    for key, (w, smp) in samples.items():
+        st = build_oracle_step(w, seqs=smp["seqs"], poison=False)
+        ref = st.attention(rows=smp["rows"])[smp["rows"]]
+        err = float(np.abs(smp["gpu"] - ref).max()) if len(smp["rows"]) else 0.0
+        tol = 2e-3 if w.spec.dtype == "bf16" else 1e-5
+        out[key] = {"rows": len(smp["rows"]), "sequences": len(smp["seqs"]),
+                    "max_abs_err": err, "tolerance": tol,
+                    "within": bool(np.isfinite(smp["gpu"]).all() and err <= tol)}
+    return out
 
 
 def cpu_baseline(w, budget_s, gpu_out=None):
@@ -324,12 +468,31 @@ def _decode_roofline(res, name, kernel):
     achieved = res["decode_kv_bytes"] / (ms * 1e-3) / 1e9 if ms else None
     cold = res.get("cold_cache_kernel") or {}
     cms = cold.get("avg_ms") if cold.get("kernel") == "decode" else None
-    return {"bound": "hbm", "kernel": kernel, "achieved": achieved, "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS if achieved else None,
-            "traffic": _traffic_for(name), "bytes_per_launch": res["decode_kv_bytes"],
-            "avg_launch_ms": ms,
-            "cold_cache": {"avg_launch_ms": cms,
-                           "achieved": res["decode_kv_bytes"] / (cms * 1e-3) / 1e9 if cms else None}}
+    r = {"bound": "hbm", "kernel": kernel, "achieved": achieved, "peak": HBM_PEAK_GBS,
+         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS if achieved else None,
+         "traffic": _traffic_for(name), "bytes_per_launch": res["decode_kv_bytes"],
+         "avg_launch_ms": ms,
+         "cold_cache": {"avg_launch_ms": cms,
+                        "achieved": res["decode_kv_bytes"] / (cms * 1e-3) / 1e9 if cms else None,
+                        "frac": res["decode_kv_bytes"] / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS
+                        if cms else None}}
+    uq = res["unique_kv_bytes"]
+    if uq != res["decode_kv_bytes"] and ms:
+        # blocks shared by several sequences: `achieved` counts every sequence's reads
+        # (logical bytes); this counts each distinct cached byte once
+        r["logical_bytes_per_launch"] = res["decode_kv_bytes"]
+        r["unique"] = {"bytes_per_launch": uq, "achieved": uq / (ms * 1e-3) / 1e9,
+                       "frac": uq / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                       "cold_cache_frac": uq / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS if cms else None}
+    return r
+
+
+def _decode_kernel_name(w):
+    """The decode kernel a decode-only workload runs on (its group and pool type)."""
+    if w.kv_fp8:
+        return "decode_fp8_kernel"
+    return "decode_pair_kernel" if (w.spec.Hq // w.spec.Hkv == 8 and w.spec.D == 128
+                                    and w.spec.dtype == "bf16") else "decode_split_kernel"
 
 
 def _clocks():
@@ -370,32 +533,44 @@ def main():
         return
     pkv.lib()   # fail loudly if the HIP library is not built
 
+    samples = {}
+    print(f"[bench] {args.workload}", file=sys.stderr, flush=True)
     main_res = time_workload(args.workload, args.steps, args.warmup,
-                             kernel_events=args.kernel_events)
+                             kernel_events=args.kernel_events, protocol_reps=args.protocol_reps)
     w = main_res["_w"]
+    samples[args.workload] = (w, main_res.pop("_sample"))
     extra = {}
     for name in [n for n in args.extra.split(",") if n and n != args.workload]:
-        r = time_workload(name, args.steps, args.warmup, kernel_events=args.kernel_events)
+        print(f"[bench] {name}", file=sys.stderr, flush=True)
+        r = time_workload(name, args.steps, args.warmup, kernel_events=args.kernel_events,
+                          protocol_reps=args.protocol_reps)
         if r["decode_kv_bytes"] and not (r["_w"].q_lens > 1).any():
-            r["roofline"] = _decode_roofline(r, name, "decode_fp8_kernel" if r["_w"].kv_fp8
-                                             else "decode_split_kernel")
+            r["roofline"] = _decode_roofline(r, name, _decode_kernel_name(r["_w"]))
+        samples[name] = (r["_w"], r.pop("_sample"))
         r.pop("_gst"); r.pop("_w"); r.pop("_out")
         extra[name] = r
         torch.cuda.empty_cache()
 
     for name in [n for n in args.consistent.split(",") if n]:
+        print(f"[bench] {name}/phase-consistent", file=sys.stderr, flush=True)
         r = time_workload(name, args.steps, args.warmup, phase_consistent=True,
-                          kernel_events=args.kernel_events, kv_split=args.consistent_split)
+                          kernel_events=args.kernel_events, kv_split=args.consistent_split,
+                          protocol_reps=args.protocol_reps)
+        samples[name + "/phase-consistent"] = (r["_w"], r.pop("_sample"))
         r.pop("_gst"); r.pop("_w"); r.pop("_out")
         extra[name + "/phase-consistent"] = r
         torch.cuda.empty_cache()
 
-    roofline = _decode_roofline(main_res, args.workload,
-                                "decode_fp8_kernel" if w.kv_fp8 else "decode_split_kernel")
+    roofline = _decode_roofline(main_res, args.workload, _decode_kernel_name(w))
     clocks = _clocks()
     cpu = None
+    parity = None
     if not args.no_cpu_baseline:
+        # the cpu_baseline leg: the oracle timed on the host cores, and its rows compared
+        # with every timed workload's sampled GPU rows
+        print("[bench] cpu_baseline leg", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, args.cpu_seconds, main_res["_out"])
+        parity = oracle_parity(samples)
     main_res.pop("_gst")
     main_res.pop("_w")
     main_res.pop("_out")
@@ -410,6 +585,9 @@ def main():
                    "cached_tokens": int(w.ctx_lens.sum()), "parallelism": "single-gpu"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "parity_vs_oracle": parity,
+        "invariance": {k: v["invariance"]["all_bitwise"]
+                       for k, v in [(args.workload, main_res)] + list(extra.items())},
         "gpu_clocks_after_timing": clocks,
         "detail": main_res,
         "extra": extra,

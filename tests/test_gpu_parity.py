@@ -251,3 +251,59 @@ def test_full_size_configs_on_sampled_rows(name):
                               rng.integers(lo, hi, size=min(3, hi - lo)).tolist()))
             rows += cand
     check_step(w, rows=rows, seqs=seqs)
+
+
+def _rows_of(w, seqs):
+    return np.concatenate([np.arange(w.cu_seqlens_q[b], w.cu_seqlens_q[b + 1])
+                           for b in seqs]).astype(np.int64)
+
+
+def _sub_batch(gst, w, seqs, **kw):
+    """The sequences `seqs` as a step of their own on the same pools (their q rows, table rows
+    and lengths); returns their output rows."""
+    rows = _rows_of(w, seqs)
+    cu = np.concatenate([[0], np.cumsum([w.q_lens[b] for b in seqs])]).astype(np.int32)
+    q = gst.q.index_select(0, torch.from_numpy(rows).to(DEV)).contiguous()
+    bt = gst.block_tables_dev[torch.as_tensor(list(seqs), device=DEV)].contiguous()
+    ctx = np.asarray([w.ctx_lens[b] for b in seqs], np.int32)
+    out = pkv.attention(q, gst.k_cache, gst.v_cache, bt, ctx, cu, w.scale,
+                        kv_split=w.spec.kv_split, **kw)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def test_full_size_prefix_shared_step_is_bitwise_invariant():
+    """All 128 sequences of the full prefix-shared step (16 groups x 8 samples on a shared
+    2048-token prompt): each alone, each group as a step, and the full batch give the same bits
+    for every sequence."""
+    w = make_workload(CONFIGS["prefix-shared-decode"])
+    print(f"[invariance] {w.spec.name} B={w.B}", flush=True)
+    gst = _harness()(w, device=DEV)
+    full = gst.attention().cpu().numpy().copy()
+    assert np.isfinite(full).all()
+    for b in range(w.B):
+        got = _sub_batch(gst, w, [b])
+        assert np.array_equal(got.view(np.uint32), full[_rows_of(w, [b])].view(np.uint32)), b
+    for g in sorted(set(w.group_of.tolist())):
+        members = np.flatnonzero(w.group_of == g).tolist()
+        got = _sub_batch(gst, w, members)
+        assert np.array_equal(got.view(np.uint32), full[_rows_of(w, members)].view(np.uint32)), g
+    # two groups together, in reverse order, as a third batch composition
+    pair = np.flatnonzero(w.group_of == 3).tolist()[::-1] + np.flatnonzero(w.group_of == 0).tolist()
+    got = _sub_batch(gst, w, pair)
+    assert np.array_equal(got.view(np.uint32), full[_rows_of(w, pair)].view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["mixed-ragged-step", "long-context-decode"])
+def test_full_size_sequences_alone_equal_the_batch_bitwise(name):
+    w = make_workload(CONFIGS[name])
+    print(f"[invariance] {w.spec.name} B={w.B} T={w.T}", flush=True)
+    gst = _harness()(w, device=DEV)
+    full = gst.attention().cpu().numpy().copy()
+    rng = np.random.default_rng(21)
+    live = [b for b in range(w.B) if w.q_lens[b] > 0]
+    seqs = sorted(set(rng.choice(live, size=min(12, len(live)), replace=False).tolist())
+                  | {b for b in live if w.q_lens[b] > 1} | {int(np.argmax(w.ctx_lens))})
+    for b in seqs:
+        got = _sub_batch(gst, w, [b])
+        assert np.array_equal(got.view(np.uint32), full[_rows_of(w, [b])].view(np.uint32)), b
