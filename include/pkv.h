@@ -418,6 +418,33 @@ int32_t pkv_write_kv_attention_fp8(const void* q, const void* k_new, const void*
                                    uint32_t flags, float* out, void* workspace,
                                    size_t workspace_bytes, void* stream);
 
+/* ---- allocation-free attention ---------------------------------------------------------
+ * For callers that cannot allocate device memory during a call: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.
+ * pkv_attention_noalloc is pkv_attention_ex (same arguments, semantics, kernels and bits)
+ * without the workspace arguments: its work lists and split partials live in a device array
+ * of PKV_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on until the process
+ * ends. The first call with a device current sets that device up (the array's address, and the
+ * pinned staging ring of 16 x 1 MiB if the device has none yet); every later call allocates
+ * nothing (no hipMalloc, hipFree, hipHostMalloc or torch allocation).
+ * Limits: a step whose workspace (pkv_attention_workspace_size_ex with the same arguments)
+ * exceeds PKV_NOALLOC_SCRATCH_BYTES, or whose work lists exceed one staging slot (1 MiB unless
+ * another entry point has grown the ring), is refused with PKV_ERR_UNSUPPORTED before
+ * anything is enqueued.
+ * Every call on one GPU shares that GPU's array: calls on one stream are ordered and safe;
+ * calls that can overlap on one GPU (other streams, other threads without ordering) race on
+ * it and give undefined results. Nothing in the array needs clearing between calls.
+ * Errors: as pkv_attention_ex, plus PKV_ERR_UNSUPPORTED for the limits above. */
+#define PKV_NOALLOC_SCRATCH_BYTES (64 * 1024 * 1024)
+
+int32_t pkv_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables_dev, int32_t max_blocks,
+                              const int32_t* ctx_lens_host, const int32_t* cu_seqlens_q_host,
+                              int32_t B, int32_t T, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                              float scale, int32_t kv_split, int32_t dtype, uint32_t flags,
+                              float* out, void* stream);
+
 /* ---- diagnostics: per-kernel device time ------------------------------------------------
  * While enabled, every kernel launched by pkv_write_kv / pkv_attention is bracketed by two HIP
  * events recorded on its launch stream (the library owns the events). pkv_profile_read waits

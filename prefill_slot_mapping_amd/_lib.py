@@ -149,6 +149,9 @@ _SIGS = {
                                     ctypes.c_uint32, _vp, _vp, ctypes.c_size_t, _vp], _i32),
     "pkv_profile_set_kinds": ([ctypes.c_uint32], _i32),
     "pkv_staging_info": ([ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(_i64)], _i32),
+    "pkv_attention_noalloc": ([_vp, _vp, _vp, _vp, _i32, _pi32, _pi32, _i32, _i32, _i32, _i32,
+                               _i32, _i32, _i32, ctypes.c_float, _i32, _i32, ctypes.c_uint32,
+                               _vp, _vp], _i32),
     "pkv_profile_enable": ([_i32], _i32),
     "pkv_profile_read": ([_i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)], _i32),
 }
@@ -528,6 +531,37 @@ def attention(q, k_cache, v_cache, block_tables, ctx_lens, cu_seqlens_q, scale: 
             _check(lib().pkv_attention_ex(*args, PKV_ATTN_PHASE_CONSISTENT, *tail))
         else:
             _check(lib().pkv_attention(*args, *tail))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024   # PKV_NOALLOC_SCRATCH_BYTES of include/pkv.h
+
+
+def attention_noalloc(q, k_cache, v_cache, block_tables, ctx_lens, cu_seqlens_q, scale: float,
+                      out, kv_split: int = 512, stream=None, phase_consistent: bool = False):
+    """pkv_attention_noalloc: pkv_attention_ex over the library's own device scratch (no
+    workspace argument, no allocation after the first call on a device). ``out`` (float32
+    [T, Hq, D]) is required: this wrapper allocates nothing either."""
+    import torch
+    _need_cuda(q, k_cache, v_cache, block_tables, out)
+    if block_tables.dtype != torch.int32:
+        raise ValueError("block_tables must be int32")
+    ctx = _host_i32(ctx_lens)
+    cu = _host_i32(cu_seqlens_q)
+    T, hq, d = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    if d2 != d or v_cache.shape != k_cache.shape or q.dtype != k_cache.dtype:
+        raise ValueError("q / pool shape or dtype mismatch")
+    if out.dtype != torch.float32 or tuple(out.shape) != (T, hq, d):
+        raise ValueError("out must be float32 [T, Hq, D]")
+    B = ctx.size
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B, max_blocks]")
+    flags = PKV_ATTN_PHASE_CONSISTENT if phase_consistent else 0
+    _check(lib().pkv_attention_noalloc(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+        int(block_tables.shape[1]), _ptr(ctx), _ptr(cu), B, T, hq, hkv, d, bs, nb, float(scale),
+        int(kv_split), _dtype_code(q), flags, out.data_ptr(), _stream_ptr(q, stream)))
     return out
 
 

@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(PKG_DIR, "libpkv.so")
 ARCH = "gfx950"
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
-DEVICE_SOURCES = ["write_kv.hip", "decode.hip", "decode_fp8.hip", "merge.hip", "prefill.hip"]
+DEVICE_SOURCES = ["write_kv.hip", "decode.hip", "decode_fp8.hip", "merge.hip", "prefill.hip",
+                  "noalloc.hip"]
 HOST_SOURCES = ["allocator.cpp", "api.cpp", "planner.cpp", "scheduler.cpp"]
 
 # Packed-FP32 instructions are disabled for all device code: the compiler may not form

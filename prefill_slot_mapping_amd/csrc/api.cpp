@@ -177,12 +177,18 @@ hipError_t ring_reserve(DeviceRing* r, size_t bytes) {
 // Stages `bytes` of host-built data in the current device's ring (fill(host) writes them) and
 // enqueues run(host, dev) on strm, the device work that reads them (through the device mapping
 // dev of the staging buffer, or with a copy from host); run returns a status.
+// With allow_grow false the ring must already hold `bytes` per slot (no allocation here).
 template <typename Fill, typename Run>
-int32_t stage_and_run(size_t bytes, hipStream_t strm, const char* what, Fill fill, Run run) {
+int32_t stage_and_run(size_t bytes, hipStream_t strm, const char* what, Fill fill, Run run,
+                      bool allow_grow = true) {
   int dev = 0;
   DeviceRing* ring = ring_for_current_device(&dev);
   if (ring == nullptr) return fail(PKV_ERR_HIP, std::string(what) + ": hipGetDevice failed");
   std::lock_guard<std::mutex> lk(ring->mu);
+  if (!allow_grow && (ring->host == nullptr || bytes > ring->slot_cap))
+    return fail(PKV_ERR_UNSUPPORTED, std::string(what) + ": work lists of " +
+                                         std::to_string(bytes) + " bytes exceed a staging slot (" +
+                                         std::to_string(ring->slot_cap) + " bytes)");
   hipError_t e = ring_reserve(ring, bytes);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string(what) + ": pinned staging: " + hipGetErrorString(e));
   const int64_t call = ring->calls;
@@ -210,12 +216,13 @@ int32_t stage_and_run(size_t bytes, hipStream_t strm, const char* what, Fill fil
 // Copies `bytes` of host-built data to device memory dst on stream strm through the current
 // device's staging ring; fill(host) writes the data into the staging buffer.
 template <typename Fill>
-int32_t stage_and_copy(void* dst, size_t bytes, hipStream_t strm, const char* what, Fill fill) {
+int32_t stage_and_copy(void* dst, size_t bytes, hipStream_t strm, const char* what, Fill fill,
+                       bool allow_grow = true) {
   return stage_and_run(bytes, strm, what, fill, [&](const char* host, const char*) -> int32_t {
     hipError_t e = hipMemcpyAsync(dst, host, bytes, hipMemcpyHostToDevice, strm);
     if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string(what) + ": list copy: " + hipGetErrorString(e));
     return PKV_OK;
-  });
+  }, allow_grow);
 }
 
 // ---- second stream: a large mixed step's decode pass runs beside its prefill pass -------
@@ -436,7 +443,10 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
                        int32_t kv_split, int32_t dtype, uint32_t flags, float* out,
                        void* workspace, size_t workspace_bytes, void* stream,
                        pkv::WriteArgs* wr, const int32_t* slots_host,
-                       const float* fp8_scales = nullptr, pkv::WriteFp8Args* wr8 = nullptr) {
+                       const float* fp8_scales = nullptr, pkv::WriteFp8Args* wr8 = nullptr,
+                       bool static_ws = false) {
+  // static_ws: the workspace is the library's fixed device scratch (pkv_attention_noalloc):
+  // a step that does not fit it, or whose lists do not fit a staging slot, is refused
   // fp8_scales != nullptr: q is bfloat16 and the pools hold E4M3 codes with per-tensor scales
   // {k_scale, v_scale}; rows are routed as for bfloat16 pools, onto the E4M3 kernels
   int32_t st = check_heads(num_q_heads, num_kv_heads, head_dim, kv_split, dtype, flags);
@@ -482,6 +492,10 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
   const StepShape s = shape_for(ctx_lens_host, cu_seqlens_q_host, B, num_q_heads, num_kv_heads,
                                 head_dim, kv_split, dtype, flags);
   const pkv::WorkspaceLayout L = layout_for(s, num_q_heads, head_dim, n_write);
+  if (static_ws && L.total > workspace_bytes)
+    return fail(PKV_ERR_UNSUPPORTED, "attention_noalloc: the step needs " +
+                                         std::to_string(L.total) + " bytes of scratch; the "
+                                         "static scratch holds " + std::to_string(workspace_bytes));
   if (workspace_bytes < L.total || (L.total > 0 && workspace == nullptr))
     return fail(PKV_ERR_INVALID, "attention: workspace smaller than the workspace-size query (" +
                                      std::to_string(L.total) + " bytes)");
@@ -524,7 +538,8 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
     });
     if (st != PKV_OK) return st;
   } else if (L.list_bytes > 0) {
-    st = stage_and_copy(ws, L.list_bytes, strm, "attention", fill);
+    st = stage_and_copy(ws, L.list_bytes, strm, static_ws ? "attention_noalloc" : "attention",
+                        fill, !static_ws);
     if (st != PKV_OK) return st;
   }
   if (T == 0) return ok();
@@ -666,6 +681,33 @@ int32_t workspace_size_impl(const int32_t* ctx_lens_host, const int32_t* cu_seql
 }
 
 }  // namespace
+
+namespace pkv {
+
+int32_t staging_setup() {
+  int dev = 0;
+  DeviceRing* ring = ring_for_current_device(&dev);
+  if (ring == nullptr) return fail(PKV_ERR_HIP, "staging set-up: hipGetDevice failed");
+  std::lock_guard<std::mutex> lk(ring->mu);
+  const hipError_t e = ring_reserve(ring, kMinSlotBytes);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("staging set-up: ") + hipGetErrorString(e));
+  return PKV_OK;
+}
+
+int32_t attention_static_scratch(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables_dev, int32_t max_blocks,
+                                 const int32_t* ctx_lens_host, const int32_t* cu_seqlens_q_host,
+                                 int32_t B, int32_t T, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                 float scale, int32_t kv_split, int32_t dtype, uint32_t flags,
+                                 float* out, void* scratch, size_t scratch_bytes, void* stream) {
+  return attention_impl(q, k_cache, v_cache, block_tables_dev, max_blocks, ctx_lens_host,
+                        cu_seqlens_q_host, B, T, num_q_heads, num_kv_heads, head_dim, block_size,
+                        num_blocks, scale, kv_split, dtype, flags, out, scratch, scratch_bytes,
+                        stream, nullptr, nullptr, nullptr, nullptr, true);
+}
+
+}  // namespace pkv
 
 extern "C" int32_t pkv_write_kv(const void* k_new, const void* v_new, const int32_t* slots_dev,
                                 int32_t n_rows, void* k_cache, void* v_cache, int32_t num_blocks,
