@@ -4,9 +4,11 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--extra A,B]
 
 One step = one pass of the whole path over one synthetic batch: the step's slot mapping on the
-host (pkv_slot_mapping_step), then one pkv_write_kv_attention call (host work planning, one
-host-to-device copy of the slots and work lists, the KV append, the prefill tiles, the decode
-split pass and the split merge). Inputs
+host (pkv_slot_mapping_step), then one pkv_write_kv_attention_shared call (E4M3 pools:
+pkv_write_kv_attention_fp8) with the step's host block tables: host work planning (a decode
+split whose blocks several rows share is read once per group of rows), one host-to-device copy
+of the slots and work lists, the KV append, the prefill tiles, the decode split pass and the
+split merge. Inputs
 are resident in HBM before timing starts; the timed region is bracketed by device
 synchronisation. The headline workload is the batched bf16 decode step (64 sequences,
 lognormal lengths with median 2048, Hq 32, Hkv 8, D 128, block 16), reported as algorithmic
@@ -216,8 +218,8 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
         ws_bytes = pkv.write_kv_attention_fp8_workspace_size(ctx_np, cu_np, s.Hq, s.Hkv, s.D,
                                                              w.T, split, phase_consistent)
     else:
-        ws_bytes = pkv.write_kv_attention_workspace_size(
-            ctx_np, cu_np, s.Hq, s.Hkv, s.D, w.T, split,
+        ws_bytes = pkv.write_kv_attention_shared_workspace_size(
+            ctx_np, cu_np, s.Hq, s.Hkv, s.D, w.T, bt_np, s.BS, split,
             pkv.PKV_BF16 if s.dtype == "bf16" else pkv.PKV_F32, phase_consistent)
     workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=device)
     out = torch.empty((w.T, s.Hq, s.D), dtype=torch.float32, device=device)
@@ -232,10 +234,12 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
                                        s.v_scale, out=out, workspace=workspace,
                                        kv_split=split, phase_consistent=phase_consistent)
             return
-        pkv.write_kv_attention(gst.q, gst.k_new, gst.v_new, sl, gst.k_cache, gst.v_cache,
-                               gst.block_tables_dev, ctx_np, cu_np, w.scale, out=out,
-                               workspace=workspace, kv_split=split,
-                               phase_consistent=phase_consistent)
+        # the host copy of the tables lets the planner read a split shared by several rows
+        # (a common prompt's blocks) once per group of rows; same bits as per-row reads
+        pkv.write_kv_attention_shared(gst.q, gst.k_new, gst.v_new, sl, gst.k_cache,
+                                      gst.v_cache, gst.block_tables_dev, bt_np, ctx_np, cu_np,
+                                      w.scale, out=out, workspace=workspace, kv_split=split,
+                                      phase_consistent=phase_consistent)
 
     for _ in range(warmup):
         step()
@@ -258,6 +262,8 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
     # would stretch the step it times). Every kernel's time is then taken in a second, untimed
     # pass of the same steps with all launches bracketed.
     dominant = "decode" if (w.q_lens == 1).any() and not phase_consistent else "prefill"
+    # a decode pass may be two launches (per-row items, group items): both are bracketed
+    dominant_kinds = [dominant, "decode_group"] if dominant == "decode" else [dominant]
     gc.callbacks.append(on_gc)
     if kernel_events == "timed":
         pkv.profile_set_kinds([])
@@ -268,7 +274,7 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
     t0 = time.perf_counter()
     for i in range(steps):
         if kernel_events == "timed":
-            pkv.profile_set_kinds([dominant] if i % EVENT_STRIDE == 0 else [])
+            pkv.profile_set_kinds(dominant_kinds if i % EVENT_STRIDE == 0 else [])
         step()
         host_ends.append(time.perf_counter())
     torch.cuda.synchronize(device)
@@ -279,15 +285,19 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
     host_ms = np.diff(np.array([t0] + host_ends)) * 1e3
     timed = {}
     if kernel_events == "timed":
-        tms, tn = pkv.profile_read(dominant)
+        # the decode pass of a bracketed step: its per-row launch and any group launch beside
+        # it, from the first start to the last end
+        tms, tn = pkv.profile_read_span(dominant_kinds)
+        gn = pkv.profile_read("decode_group")[1] if dominant == "decode" else 0
         timed = {"kernel": dominant, "launches_bracketed": tn,
-                 "avg_ms": tms / tn if tn else None}
-    kinds = ("write_kv", "prefill", "decode", "merge")
+                 "avg_ms": tms / tn if tn else None, "group_launches": gn}
+    kinds = ("write_kv", "prefill", "decode", "merge", "decode_group")
     pkv.profile_set_kinds(list(kinds))
     pkv.profile_enable(True)
     for _ in range(steps):
         step()
     kern = {k: pkv.profile_read(k) for k in kinds}
+    dspan = pkv.profile_read_span(["decode", "decode_group"])
     pkv.profile_enable(False)
     torch.cuda.synchronize(device)
     assert np.array_equal(slots_np[:w.T], gst.new_slots)
@@ -298,12 +308,12 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
     cold = {}
     if cold_steps > 0:
         scratch = torch.empty(1 << 28, dtype=torch.float32, device=device)
-        pkv.profile_set_kinds([dominant])
+        pkv.profile_set_kinds(dominant_kinds)
         pkv.profile_enable(True)
         for i in range(cold_steps):
             scratch.fill_(float(i))
             step()
-        cms, cn = pkv.profile_read(dominant)
+        cms, cn = pkv.profile_read_span(dominant_kinds)
         pkv.profile_enable(False)
         torch.cuda.synchronize(device)
         del scratch
@@ -340,13 +350,16 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
         # distinct cached bytes (a block shared by several sequences counted once) and, for
         # decode-only steps, the rate they give over the decode kernel's time
         "unique_kv_bytes": uq,
-        "decode_unique_gbs": (uq / (kern["decode"][0] / kern["decode"][1] * 1e-3) / 1e9
-                              if decode_only and kern["decode"][1] else None),
+        "decode_unique_gbs": (uq / (dspan[0] / dspan[1] * 1e-3) / 1e9
+                              if decode_only and dspan[1] else None),
         "build_s": t_build,
         "host_enqueue_ms": {"median": float(np.median(host_ms)), "max": float(host_ms.max())},
         "gc_pauses_in_timed_region": {"count": len(gc_pauses),
                                       "max_ms": max(gc_pauses, default=0.0) * 1e3},
         "kernels_ms": {k: (v[0] / v[1] if v[1] else None) for k, v in kern.items()},
+        # the decode pass per step: from the first start to the last end of its per-row
+        # launch and its group launch (when there is one, on the second stream beside it)
+        "decode_pass_ms": dspan[0] / dspan[1] if dspan[1] else None,
         "timed_region_kernel": timed,
         "cold_cache_kernel": cold,
         "kernel_launches": {k: v[1] for k, v in kern.items()},
@@ -464,7 +477,7 @@ def _decode_roofline(res, name, kernel):
     """Roofline object of a result's decode kernel: algorithmic KV bytes / its average launch
     in the timed steps; the cold-cache launch (L2 and MALL flushed first) is given beside it."""
     tr = res["timed_region_kernel"]
-    ms = tr.get("avg_ms") if tr.get("kernel") == "decode" else res["kernels_ms"]["decode"]
+    ms = tr.get("avg_ms") if tr.get("kernel") == "decode" else res["decode_pass_ms"]
     achieved = res["decode_kv_bytes"] / (ms * 1e-3) / 1e9 if ms else None
     cold = res.get("cold_cache_kernel") or {}
     cms = cold.get("avg_ms") if cold.get("kernel") == "decode" else None

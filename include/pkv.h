@@ -349,6 +349,46 @@ int32_t pkv_write_kv_attention(const void* q, const void* k_new, const void* v_n
                                int32_t kv_split, int32_t dtype, uint32_t flags, float* out,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- fused step with shared reads [P3 "Design > engine.py", Prefix sharing: G samples of a
+ *      prompt share its full blocks read-only; "Optional paged KV cache (vLLM-style) — v1
+ *      design", "Motivation": block-level sharing of a common prefix] --------------------
+ * pkv_write_kv_attention with a host copy of the block tables for the work planner:
+ *   block_tables_host: host int32 [B, max_blocks], the same entries as block_tables_dev over
+ *                 every row's context (the planner reads entries below ceil(ctx_lens[b] /
+ *                 block_size) only).
+ * A decode split (kv_split keys aligned at a multiple of kv_split) that lies wholly inside the
+ * contexts of several decode rows and covers the same physical blocks in each is read once per
+ * group of up to 4 (or 2, per build) of those rows, instead of once per row: one work item
+ * loads its K/V tiles once and runs every row's arithmetic of the per-row decode item on
+ * them, row by row. So every output bit is the same as with pkv_write_kv_attention (and as
+ * each row alone): only HBM and cache traffic change. Applies to bfloat16 pools with
+ * num_q_heads / num_kv_heads in {1, 2, 4} on the split decode pass (not in the
+ * phase-consistent mode, where decode rows run on the tile path); otherwise the call is
+ * exactly pkv_write_kv_attention. If the device tables name other blocks than the host copy
+ * for a row of a group, that row is written as NaN (never from another row's keys).
+ * The workspace comes from pkv_write_kv_attention_shared_workspace_size with the same host
+ * tables (the group items take the place of per-row items in the lists).
+ * Errors: as pkv_write_kv_attention, plus PKV_ERR_INVALID for NULL host tables (B > 0),
+ * max_blocks < 0 or a ctx_len beyond max_blocks * block_size. */
+int32_t pkv_write_kv_attention_shared_workspace_size(
+    const int32_t* ctx_lens_host, const int32_t* cu_seqlens_q_host, int32_t B,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t kv_split,
+    int32_t dtype, uint32_t flags, int32_t n_rows, const int32_t* block_tables_host,
+    int32_t max_blocks, int32_t block_size, size_t* bytes);
+
+int32_t pkv_write_kv_attention_shared(const void* q, const void* k_new, const void* v_new,
+                                      const int32_t* slots_host, int32_t n_rows,
+                                      void* k_cache, void* v_cache,
+                                      const int32_t* block_tables_dev,
+                                      const int32_t* block_tables_host, int32_t max_blocks,
+                                      const int32_t* ctx_lens_host,
+                                      const int32_t* cu_seqlens_q_host, int32_t B, int32_t T,
+                                      int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                      float scale, int32_t kv_split, int32_t dtype,
+                                      uint32_t flags, float* out, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
 /* ---- FP8 (OCP E4M3) KV pools with per-tensor scales [BC section 4.2: the KV cache kept in
  *      FP8, about 57 % of the BF16 bytes, one write path; P3 "Design > paged.py" and its
  *      single-device notes: a K/V dtype other than the model's is dequantised on read, and
@@ -449,11 +489,17 @@ int32_t pkv_attention_noalloc(const void* q, const void* k_cache, const void* v_
  * While enabled, every kernel launched by pkv_write_kv / pkv_attention is bracketed by two HIP
  * events recorded on its launch stream (the library owns the events). pkv_profile_read waits
  * for the recorded launches of one kernel kind and returns their summed elapsed time and count.
- * Kernel kinds: 0 KV append, 1 prefill tiles, 2 decode split pass, 3 split merge.
+ * Kernel kinds: 0 KV append, 1 prefill tiles, 2 decode split pass, 3 split merge, 4 decode
+ * group items (pkv_write_kv_attention_shared).
  * pkv_profile_enable(1) clears previous records; pkv_profile_enable(0) stops recording.
  * Not thread-safe with concurrent launches from several host threads. */
 int32_t pkv_profile_enable(int32_t enable);
 int32_t pkv_profile_read(int32_t kernel_kind, double* total_ms, int64_t* launches);
+/* Summed over the attention calls recorded since pkv_profile_enable(1): the span from the
+ * earliest start to the latest end of each call's bracketed launches whose kind bit is set in
+ * kinds (launches of one call may run concurrently on two streams, e.g. the decode pass's
+ * per-row items, kind 2, beside its group items, kind 4), and the number of such calls. */
+int32_t pkv_profile_read_span(uint32_t kinds, double* total_ms, int64_t* calls);
 /* The calling thread's current device's pinned staging ring: bytes per slot (0 before the
  * first staged call) and how many times its arena has been allocated so far. The arena (16
  * equal slots) is allocated by the first call that stages work lists on a device and replaced
@@ -462,9 +508,9 @@ int32_t pkv_profile_read(int32_t kernel_kind, double* total_ms, int64_t* launche
  * allocate nothing. Either pointer may be NULL. */
 int32_t pkv_staging_info(size_t* slot_bytes, int64_t* allocations);
 /* Kernel kinds bracketed from now on while profiling is enabled: bit k = kind k (default all,
- * 0xF); records already taken are kept. Each event record costs the stream a few
+ * 0x1F); records already taken are kept. Each event record costs the stream a few
  * microseconds, so a caller timing whole steps can bracket only the kernel it reports, or
- * only some of its launches. PKV_ERR_INVALID for bits above kind 3. */
+ * only some of its launches. PKV_ERR_INVALID for bits above kind 4. */
 int32_t pkv_profile_set_kinds(uint32_t kinds);
 
 #ifdef __cplusplus

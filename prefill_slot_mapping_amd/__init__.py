@@ -8,8 +8,9 @@ from ._lib import (  # noqa: F401
     PKV_ATTN_PHASE_CONSISTENT, PKV_BF16, PKV_E4M3, PKV_F32, BlockAllocator, DoubleFree, HipError, Inconsistent, InvalidArgument,
     PkvError, PoolExhausted, SchedPlan, Scheduler, SharedWrite, Unsupported, attention,
     attention_noalloc, attention_fp8, attention_fp8_workspace_size, attention_workspace_size, copy_blocks,
-    header_functions, lib, profile_enable, profile_read, profile_set_kinds, slot_mapping_step,
+    header_functions, lib, profile_enable, profile_read, profile_read_span, profile_set_kinds, slot_mapping_step,
     staging_info, validate_slots, version, write_kv, write_kv_attention, write_kv_attention_workspace_size,
+    write_kv_attention_shared, write_kv_attention_shared_workspace_size,
     write_kv_attention_fp8, write_kv_attention_fp8_workspace_size, write_kv_fp8,
 )
 from . import accounting  # noqa: F401

@@ -30,8 +30,11 @@ HOST_SOURCES = ["allocator.cpp", "api.cpp", "planner.cpp", "scheduler.cpp"]
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # Per-source extras. decode.hip, decode_fp8.hip: no floating-point operation there sees a NaN (bad rows are
 # written as a NaN bit pattern through an integer select), which lets maxima fuse with their
-# DPP lane permutes.
-SOURCE_FLAGS = {"decode.hip": ["-fno-honor-nans"], "decode_fp8.hip": ["-fno-honor-nans"]}
+# DPP lane permutes. decode.hip: no implicit contraction of a multiply and an add into an FMA
+# (every FMA is written out), so kernel instances that differ only in how many rows share a
+# tile compute every row with the same operations.
+SOURCE_FLAGS = {"decode.hip": ["-fno-honor-nans", "-ffp-contract=off"],
+                "decode_fp8.hip": ["-fno-honor-nans"]}
 
 
 def hipcc() -> str:

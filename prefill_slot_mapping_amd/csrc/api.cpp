@@ -268,15 +268,24 @@ SideStream* side_for_current_device() {
 struct ProfRecord {
   int kind;
   hipEvent_t a, b;
+  int64_t call;   // the attention call (per thread) whose launch it brackets
 };
+// a drained record: its launch's start and end in ms after the first start of its call
+struct ProfDone {
+  int kind;
+  int64_t call;
+  double start, end;
+};
+std::atomic<int64_t> g_prof_calls{0};
+thread_local int64_t t_prof_call = -1;
 std::mutex g_prof_mu;
 // read without the lock on every launch (the fast path when profiling is off)
 std::atomic<bool> g_prof_on{false};
-std::atomic<uint32_t> g_prof_kinds{0xFu};  // kernel kinds bracketed while profiling is on
+std::atomic<uint32_t> g_prof_kinds{0x1Fu};  // kernel kinds bracketed while profiling is on
 std::vector<ProfRecord> g_prof_pending;
 std::vector<hipEvent_t> g_prof_free;
-double g_prof_ms[4] = {0, 0, 0, 0};
-int64_t g_prof_n[4] = {0, 0, 0, 0};
+constexpr int kProfKinds = 5;  // append, prefill tiles, decode split pass, merge, group items
+std::vector<ProfDone> g_prof_done;
 
 hipEvent_t prof_event() {
   if (!g_prof_free.empty()) {
@@ -295,7 +304,7 @@ int prof_begin(int kind, hipStream_t s) {
       ((g_prof_kinds.load(std::memory_order_relaxed) >> kind) & 1u) == 0)
     return -1;
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  ProfRecord r{kind, prof_event(), prof_event()};
+  ProfRecord r{kind, prof_event(), prof_event(), t_prof_call};
   if (r.a == nullptr || r.b == nullptr) return -1;
   if (hipEventRecord(r.a, s) != hipSuccess) return -1;
   g_prof_pending.push_back(r);
@@ -337,7 +346,9 @@ int32_t check_flags(uint32_t flags, int32_t hq, int32_t hkv, int32_t head_dim, i
 }
 
 StepShape shape_for(const int32_t* ctx, const int32_t* cu, int32_t B, int32_t hq, int32_t hkv,
-                    int32_t head_dim, int32_t kv_split, int32_t dtype, uint32_t flags) {
+                    int32_t head_dim, int32_t kv_split, int32_t dtype, uint32_t flags,
+                    const int32_t* bt_host = nullptr, int32_t bt_stride = 0,
+                    int32_t block_size = 0, bool fp8 = false) {
   StepShape s;
   s.all_mfma = (flags & PKV_ATTN_PHASE_CONSISTENT) != 0;
   s.ctx = ctx;
@@ -348,6 +359,14 @@ StepShape shape_for(const int32_t* ctx, const int32_t* cu, int32_t B, int32_t hq
   s.prefill_on_mfma = pkv::prefill_supported(head_dim, group, dtype == PKV_BF16);
   s.prefill_rows_per_item = pkv::kPrefillMRows / group;
   s.tile_split = s.all_mfma ? kv_split : 0;
+  // shared reads: bf16 pools on the split decode pass, groups the group-item kernel serves
+  if (bt_host != nullptr && !fp8 && dtype == PKV_BF16 && !s.all_mfma &&
+      pkv::decode_groups_supported(head_dim, group)) {
+    s.bt_host = bt_host;
+    s.bt_stride = bt_stride;
+    s.block_size = block_size;
+    s.group_rows = pkv::decode_group_rows();
+  }
   return s;
 }
 
@@ -382,6 +401,7 @@ int32_t check_write(const void* k_new, const void* v_new, int32_t n_rows, const 
 }
 
 int32_t launch_write(const pkv::WriteArgs& a, hipStream_t strm) {
+  t_prof_call = g_prof_calls.fetch_add(1, std::memory_order_relaxed);
   const int pr = prof_begin(0, strm);
   hipError_t e = pkv::launch_write_kv(a, strm);
   prof_end(pr, strm);
@@ -425,6 +445,7 @@ int32_t check_write_fp8(const void* k_new, const void* v_new, int32_t n_rows,
 }
 
 int32_t launch_write_fp8(const pkv::WriteFp8Args& a, hipStream_t strm) {
+  t_prof_call = g_prof_calls.fetch_add(1, std::memory_order_relaxed);
   const int pr = prof_begin(0, strm);
   hipError_t e = pkv::launch_write_kv_fp8(a, strm);
   prof_end(pr, strm);
@@ -444,7 +465,7 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
                        void* workspace, size_t workspace_bytes, void* stream,
                        pkv::WriteArgs* wr, const int32_t* slots_host,
                        const float* fp8_scales = nullptr, pkv::WriteFp8Args* wr8 = nullptr,
-                       bool static_ws = false) {
+                       bool static_ws = false, const int32_t* block_tables_host = nullptr) {
   // static_ws: the workspace is the library's fixed device scratch (pkv_attention_noalloc):
   // a step that does not fit it, or whose lists do not fit a staging slot, is refused
   // fp8_scales != nullptr: q is bfloat16 and the pools hold E4M3 codes with per-tensor scales
@@ -489,8 +510,15 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
     return fail(PKV_ERR_INVALID, "attention: q, pools and workspace must be 16-byte aligned, "
                                  "out and block_tables 4-byte aligned");
 
-  const StepShape s = shape_for(ctx_lens_host, cu_seqlens_q_host, B, num_q_heads, num_kv_heads,
-                                head_dim, kv_split, dtype, flags);
+  StepShape s = shape_for(ctx_lens_host, cu_seqlens_q_host, B, num_q_heads, num_kv_heads,
+                          head_dim, kv_split, dtype, flags, block_tables_host, max_blocks,
+                          block_size, fp8_scales != nullptr);
+  // the shared splits are found once for the layout and the lists
+  pkv::SharedSplits shared;
+  if (s.bt_host != nullptr && s.group_rows > 1) {
+    shared = pkv::find_shared_splits(s);
+    s.shared = &shared;
+  }
   const pkv::WorkspaceLayout L = layout_for(s, num_q_heads, head_dim, n_write);
   if (static_ws && L.total > workspace_bytes)
     return fail(PKV_ERR_UNSUPPORTED, "attention_noalloc: the step needs " +
@@ -499,11 +527,13 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
   if (workspace_bytes < L.total || (L.total > 0 && workspace == nullptr))
     return fail(PKV_ERR_INVALID, "attention: workspace smaller than the workspace-size query (" +
                                      std::to_string(L.total) + " bytes)");
-  if (L.n_decode * num_q_heads > INT32_MAX || L.n_prefill * num_kv_heads > INT32_MAX)
+  if (L.n_decode * num_q_heads > INT32_MAX || L.n_prefill * num_kv_heads > INT32_MAX ||
+      L.n_group * num_kv_heads > INT32_MAX)
     return fail(PKV_ERR_UNSUPPORTED, "attention: step too large for one launch");
 
   hipStream_t strm = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
+  t_prof_call = g_prof_calls.fetch_add(1, std::memory_order_relaxed);
 
   // work lists (and fused-append slots) -> pinned staging -> workspace, one async copy ordered
   // before the kernels
@@ -560,17 +590,23 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
   // a large mixed step forks its decode pass (and merge) onto the second stream
   const bool fork = L.n_prefill * num_kv_heads > kForkMinPrefillWgs &&
                     L.n_decode * num_kv_heads >= kForkMinDecodeWgs;
+  // a step with group items and per-row decode items runs the group launch on the second
+  // stream beside the per-row launch (joined before the merge): the two launches hold
+  // different register budgets, so on one stream the second would wait for the first to drain
+  const bool fork_groups = !fork && L.n_group > 0 && L.n_decode > 0;
   SideStream* side = nullptr;
   std::unique_lock<std::mutex> side_lock;
-  hipStream_t dstrm = strm;
-  if (fork) {
+  hipStream_t dstrm = strm;   // per-row decode items (and the merge)
+  hipStream_t gstrm = strm;   // group items
+  if (fork || fork_groups) {
     side = side_for_current_device();
     if (side == nullptr) return fail(PKV_ERR_HIP, "attention: second stream set-up failed");
     side_lock = std::unique_lock<std::mutex>(side->mu);
     hipError_t e = hipEventRecord(side->fork, strm);
     if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
     if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("attention: fork: ") + hipGetErrorString(e));
-    dstrm = side->s;
+    gstrm = side->s;
+    if (fork) dstrm = side->s;
   }
   // the passes; after a failed launch the join below still runs, so that the caller's stream
   // never runs ahead of work already enqueued on the second stream
@@ -603,6 +639,33 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
       prof_end(pr, strm);
       if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("prefill launch: ") + hipGetErrorString(e));
     }
+    if (L.n_group > 0) {
+      pkv::DecodeArgs d;
+      d.q = q;
+      d.k_cache = k_cache;
+      d.v_cache = v_cache;
+      d.block_tables = block_tables_dev;
+      d.max_blocks = max_blocks;
+      d.block_size = block_size;
+      d.bs_log2 = bs_log2;
+      d.num_blocks = num_blocks;
+      d.hq = num_q_heads;
+      d.hkv = num_kv_heads;
+      d.kv_split = kv_split;
+      d.scale_log2e = scale_log2e;
+      d.v_scale = v_scale;
+      d.items = nullptr;
+      d.groups = reinterpret_cast<const pkv::DecodeGroupItem*>(ws + L.group_off);
+      d.group = group;
+      d.out = out;
+      d.part_m = part_m;
+      d.part_l = part_l;
+      d.part_acc = part_acc;
+      const int pr = prof_begin(4, gstrm);
+      hipError_t e = pkv::launch_decode_groups(d, L.n_group, head_dim, group, gstrm);
+      prof_end(pr, gstrm);
+      if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("decode group launch: ") + hipGetErrorString(e));
+    }
     if (L.n_decode > 0) {
       pkv::DecodeArgs d;
       d.q = q;
@@ -619,6 +682,7 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
       d.scale_log2e = scale_log2e;
       d.v_scale = v_scale;
       d.items = reinterpret_cast<const pkv::DecodeItem*>(ws + L.decode_off);
+      d.groups = nullptr;
       d.group = group;
       d.out = out;
       d.part_m = part_m;
@@ -630,6 +694,12 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
                          : pkv::launch_decode(d, L.n_decode, head_dim, group, dtype == PKV_BF16, dstrm);
       prof_end(pr, dstrm);
       if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("decode launch: ") + hipGetErrorString(e));
+    }
+    if (fork_groups) {
+      // the merge reads the group items' partials
+      hipError_t e = hipEventRecord(side->join, gstrm);
+      if (e == hipSuccess) e = hipStreamWaitEvent(strm, side->join, 0);
+      if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("attention: join: ") + hipGetErrorString(e));
     }
     if (L.n_merge > 0) {
       pkv::MergeArgs mg;
@@ -648,6 +718,11 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
     return PKV_OK;
   };
   int32_t rc = launch_passes();
+  if (fork_groups && rc != PKV_OK) {
+    // a launch failed before the join: the caller's stream still waits for the second stream
+    hipError_t e = hipEventRecord(side->join, gstrm);
+    if (e == hipSuccess) (void)hipStreamWaitEvent(strm, side->join, 0);
+  }
   if (fork) {
     hipError_t e = hipEventRecord(side->join, dstrm);
     if (e == hipSuccess) e = hipStreamWaitEvent(strm, side->join, 0);
@@ -660,7 +735,9 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
 int32_t workspace_size_impl(const int32_t* ctx_lens_host, const int32_t* cu_seqlens_q_host,
                             int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
                             int32_t head_dim, int32_t kv_split, int32_t dtype, uint32_t flags,
-                            int32_t n_write_rows, size_t* bytes, bool fp8 = false) {
+                            int32_t n_write_rows, size_t* bytes, bool fp8 = false,
+                            const int32_t* block_tables_host = nullptr, int32_t max_blocks = 0,
+                            int32_t block_size = 0) {
   if (bytes == nullptr) return fail(PKV_ERR_INVALID, "workspace_size: bytes is NULL");
   *bytes = 0;
   if (n_write_rows < 0) return fail(PKV_ERR_INVALID, "workspace_size: n_rows must be >= 0");
@@ -672,7 +749,8 @@ int32_t workspace_size_impl(const int32_t* ctx_lens_host, const int32_t* cu_seql
   st = check_step(ctx_lens_host, cu_seqlens_q_host, B, T, -1);
   if (st != PKV_OK) return st;
   StepShape s = shape_for(ctx_lens_host, cu_seqlens_q_host, B, num_q_heads, num_kv_heads,
-                          head_dim, kv_split, dtype, flags);
+                          head_dim, kv_split, dtype, flags, block_tables_host, max_blocks,
+                          block_size, fp8);
   if (fp8 && !pkv::decode_fp8_supported(head_dim, num_q_heads / num_kv_heads))
     return fail(PKV_ERR_UNSUPPORTED, "attention_fp8: head_dim 64 or 128 and num_q_heads / "
                                      "num_kv_heads one of 1, 2, 4");
@@ -849,6 +927,59 @@ extern "C" int32_t pkv_write_kv_attention(
                         workspace_bytes, stream, &a, slots_host);
 }
 
+// Host tables for the planner: every read entry in [0, max_blocks) of a row, validated for
+// the rows' whole contexts (the device tables are the ones the kernels read).
+static int32_t check_host_tables(const int32_t* bt, int32_t max_blocks, int32_t block_size,
+                                 const int32_t* ctx, int32_t B) {
+  if (B > 0 && bt == nullptr) return fail(PKV_ERR_INVALID, "block_tables_host is NULL");
+  if (max_blocks < 0 || block_size <= 0)
+    return fail(PKV_ERR_INVALID, "max_blocks must be >= 0 and block_size > 0");
+  for (int32_t b = 0; b < B; ++b)
+    if (ctx[b] > static_cast<int64_t>(max_blocks) * block_size)
+      return fail(PKV_ERR_INVALID, "sequence " + std::to_string(b) +
+                                       ": ctx_len exceeds max_blocks * block_size");
+  return PKV_OK;
+}
+
+extern "C" int32_t pkv_write_kv_attention_shared_workspace_size(
+    const int32_t* ctx_lens_host, const int32_t* cu_seqlens_q_host, int32_t B,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t kv_split,
+    int32_t dtype, uint32_t flags, int32_t n_rows, const int32_t* block_tables_host,
+    int32_t max_blocks, int32_t block_size, size_t* bytes) {
+  if (bytes != nullptr) *bytes = 0;
+  if (B > 0 && ctx_lens_host != nullptr) {
+    const int32_t st = check_host_tables(block_tables_host, max_blocks, block_size,
+                                         ctx_lens_host, B);
+    if (st != PKV_OK) return st;
+  }
+  return workspace_size_impl(ctx_lens_host, cu_seqlens_q_host, B, num_q_heads, num_kv_heads,
+                             head_dim, kv_split, dtype, flags, n_rows, bytes, false,
+                             block_tables_host, max_blocks, block_size);
+}
+
+extern "C" int32_t pkv_write_kv_attention_shared(
+    const void* q, const void* k_new, const void* v_new, const int32_t* slots_host,
+    int32_t n_rows, void* k_cache, void* v_cache, const int32_t* block_tables_dev,
+    const int32_t* block_tables_host, int32_t max_blocks, const int32_t* ctx_lens_host,
+    const int32_t* cu_seqlens_q_host, int32_t B, int32_t T, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+    int32_t kv_split, int32_t dtype, uint32_t flags, float* out, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  pkv::WriteArgs a;
+  int32_t st = check_write(k_new, v_new, n_rows, k_cache, v_cache, num_blocks, block_size,
+                           num_kv_heads, head_dim, dtype, &a);
+  if (st != PKV_OK) return st;
+  if (B > 0 && ctx_lens_host != nullptr) {
+    st = check_host_tables(block_tables_host, max_blocks, block_size, ctx_lens_host, B);
+    if (st != PKV_OK) return st;
+  }
+  return attention_impl(q, k_cache, v_cache, block_tables_dev, max_blocks, ctx_lens_host,
+                        cu_seqlens_q_host, B, T, num_q_heads, num_kv_heads, head_dim, block_size,
+                        num_blocks, scale, kv_split, dtype, flags, out, workspace,
+                        workspace_bytes, stream, &a, slots_host, nullptr, nullptr, false,
+                        block_tables_host);
+}
+
 extern "C" int32_t pkv_write_kv_fp8(const void* k_new, const void* v_new,
                                     const int32_t* slots_dev, int32_t n_rows, void* k_cache,
                                     void* v_cache, int32_t num_blocks, int32_t block_size,
@@ -920,7 +1051,7 @@ extern "C" int32_t pkv_write_kv_attention_fp8(
 }
 
 extern "C" int32_t pkv_profile_set_kinds(uint32_t kinds) {
-  if ((kinds & ~0xFu) != 0) return fail(PKV_ERR_INVALID, "profile_set_kinds: unknown kind bits");
+  if ((kinds & ~0x1Fu) != 0) return fail(PKV_ERR_INVALID, "profile_set_kinds: unknown kind bits");
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof_kinds.store(kinds, std::memory_order_relaxed);
   return ok();
@@ -935,33 +1066,87 @@ extern "C" int32_t pkv_profile_enable(int32_t enable) {
       g_prof_free.push_back(r.b);
     }
     g_prof_pending.clear();
-    for (int k = 0; k < 4; ++k) {
-      g_prof_ms[k] = 0;
-      g_prof_n[k] = 0;
-    }
+    g_prof_done.clear();
   }
   g_prof_on.store(enable != 0, std::memory_order_relaxed);
   return ok();
 }
 
-extern "C" int32_t pkv_profile_read(int32_t kernel_kind, double* total_ms, int64_t* launches) {
-  if (kernel_kind < 0 || kernel_kind > 3 || total_ms == nullptr || launches == nullptr)
-    return fail(PKV_ERR_INVALID, "profile_read: bad arguments");
-  std::lock_guard<std::mutex> lk(g_prof_mu);
+// Waits for the pending records and turns them into ProfDone entries (times relative to the
+// first start of each call: launches of one call may run on two streams). Caller holds the
+// lock.
+static int32_t prof_drain(const char* what) {
+  size_t i0 = 0;
+  while (i0 < g_prof_pending.size()) {
+    size_t i1 = i0 + 1;   // records of one call are contiguous (one thread enqueues a call)
+    while (i1 < g_prof_pending.size() && g_prof_pending[i1].call == g_prof_pending[i0].call) ++i1;
+    const hipEvent_t ref = g_prof_pending[i0].a;
+    for (size_t i = i0; i < i1; ++i) {
+      const ProfRecord& r = g_prof_pending[i];
+      hipError_t e = hipEventSynchronize(r.b);
+      float s_ms = 0.f, e_ms = 0.f;
+      if (e == hipSuccess) e = hipEventElapsedTime(&s_ms, ref, r.a);
+      if (e == hipSuccess) e = hipEventElapsedTime(&e_ms, ref, r.b);
+      if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+      g_prof_done.push_back(ProfDone{r.kind, r.call, s_ms, e_ms});
+    }
+    i0 = i1;
+  }
   for (auto& r : g_prof_pending) {
-    hipError_t e = hipEventSynchronize(r.b);
-    if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("profile_read: ") + hipGetErrorString(e));
-    float ms = 0.f;
-    e = hipEventElapsedTime(&ms, r.a, r.b);
-    if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("profile_read: ") + hipGetErrorString(e));
-    g_prof_ms[r.kind] += ms;
-    g_prof_n[r.kind] += 1;
     g_prof_free.push_back(r.a);
     g_prof_free.push_back(r.b);
   }
   g_prof_pending.clear();
-  *total_ms = g_prof_ms[kernel_kind];
-  *launches = g_prof_n[kernel_kind];
+  return PKV_OK;
+}
+
+extern "C" int32_t pkv_profile_read(int32_t kernel_kind, double* total_ms, int64_t* launches) {
+  if (kernel_kind < 0 || kernel_kind >= kProfKinds || total_ms == nullptr || launches == nullptr)
+    return fail(PKV_ERR_INVALID, "profile_read: bad arguments");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  const int32_t st = prof_drain("profile_read");
+  if (st != PKV_OK) return st;
+  double ms = 0.0;
+  int64_t n = 0;
+  for (const ProfDone& d : g_prof_done)
+    if (d.kind == kernel_kind) {
+      ms += d.end - d.start;
+      n += 1;
+    }
+  *total_ms = ms;
+  *launches = n;
+  return ok();
+}
+
+extern "C" int32_t pkv_profile_read_span(uint32_t kinds, double* total_ms, int64_t* calls) {
+  if ((kinds & ~0x1Fu) != 0 || kinds == 0 || total_ms == nullptr || calls == nullptr)
+    return fail(PKV_ERR_INVALID, "profile_read_span: bad arguments");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  const int32_t st = prof_drain("profile_read_span");
+  if (st != PKV_OK) return st;
+  double ms = 0.0;
+  int64_t n = 0;
+  size_t i0 = 0;
+  while (i0 < g_prof_done.size()) {
+    size_t i1 = i0 + 1;
+    while (i1 < g_prof_done.size() && g_prof_done[i1].call == g_prof_done[i0].call) ++i1;
+    double lo = 0.0, hi = 0.0;
+    bool any = false;
+    for (size_t i = i0; i < i1; ++i) {
+      const ProfDone& d = g_prof_done[i];
+      if (((kinds >> d.kind) & 1u) == 0) continue;
+      lo = any ? std::min(lo, d.start) : d.start;
+      hi = any ? std::max(hi, d.end) : d.end;
+      any = true;
+    }
+    if (any) {
+      ms += hi - lo;
+      n += 1;
+    }
+    i0 = i1;
+  }
+  *total_ms = ms;
+  *calls = n;
   return ok();
 }
 

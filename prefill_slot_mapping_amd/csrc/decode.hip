@@ -52,7 +52,14 @@ namespace pkv {
 //      h % SPL of each key's group forms p for head h),
 //   4. accumulates P.V in the split-D layout (each lane owns EPL columns of its key group).
 // ---------------------------------------------------------------------------------------
-template <int D, int G, bool BF, int HT, int W>
+// R > 1: a group item (DecodeGroupItem) of up to R rows whose split reads the same physical
+// blocks. The split's K and V tiles are loaded once; each row keeps its own running state
+// (reference, sums, accumulators) and its own wave merge, and runs exactly the operations of
+// the R = 1 kernel on every tile in the same order, so its bits do not depend on the rows it
+// was grouped with. The slots come from the first row's table; a row whose table names other
+// blocks over the split (the host planned from tables that differ from the device's) is
+// written as NaN instead of reading the first row's keys.
+template <int D, int G, bool BF, int HT, int W, int R = 1>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(W, W)))
 decode_split_kernel(DecodeArgs a) {
   constexpr int E = BF ? 2 : 4;
@@ -71,13 +78,14 @@ decode_split_kernel(DecodeArgs a) {
   static_assert(LPT >= 8 && LPT <= 32 && (LPT & (LPT - 1)) == 0 && HT % TPI == 0, "shape");
   static_assert(HT == 16 || HT == 32, "tile");
   static_assert(NI % 2 == 0, "slot reads are 8- or 16-byte vectors");
+  static_assert(R >= 1 && R <= kGroupRows, "rows per item");
 
   // K tiles of the four waves; reused as the wave-merge scratch at the end
   constexpr int kTileU4 = kDecodeWaves * HT * LPT;
   constexpr int kMergeU4 = (kDecodeWaves * G * (D + 2) * 4 + 15) / 16;
   __shared__ uint4 s_k[kTileU4 > kMergeU4 ? kTileU4 : kMergeU4];
   __shared__ __align__(16) float s_p[kDecodeWaves][HT * G];
-  __shared__ uint4 s_q[G * LPT];
+  __shared__ uint4 s_q[R][G * LPT];
   __shared__ __align__(16) uint32_t s_slot[kMaxDecodeSplit];
 
   const int tid = threadIdx.x;
@@ -90,13 +98,34 @@ decode_split_kernel(DecodeArgs a) {
   const int item_idx = f / a.hkv;
   const int g = f - item_idx * a.hkv;        // the kv head of this work item
   const int hq0 = g * G;                     // its first query head
-  const DecodeItem it = a.items[item_idx];
+  int split, n_keys, n_rows;
+  int row[R], seq[R], part[R];
+  if constexpr (R == 1) {
+    const DecodeItem it = a.items[item_idx];
+    split = it.split;
+    n_keys = it.n_keys;
+    n_rows = 1;
+    row[0] = it.row;
+    seq[0] = it.seq;
+    part[0] = it.part;
+  } else {
+    const DecodeGroupItem it = a.groups[item_idx];
+    split = it.split;
+    n_keys = it.n_keys;
+    n_rows = it.n_rows;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      row[r] = it.row[r];
+      seq[r] = it.seq[r];
+      part[r] = it.part[r];
+    }
+  }
 
-  const int t0 = it.split * a.kv_split;
-  const int t1 = min(it.n_keys, t0 + a.kv_split);
+  const int t0 = split * a.kv_split;
+  const int t1 = min(n_keys, t0 + a.kv_split);
   const int nk = t1 - t0;                    // >= 1
   const int nk_pad = (nk + HT - 1) / HT * HT;
-  const int32_t* bt = a.block_tables + static_cast<int64_t>(it.seq) * a.max_blocks;
+  const int32_t* bt = a.block_tables + static_cast<int64_t>(seq[0]) * a.max_blocks;
   bool bad = false;
 
   // an out-of-pool block id marks the item bad and is replaced by slot 0, so no load ever
@@ -117,9 +146,29 @@ decode_split_kernel(DecodeArgs a) {
     const int w = k % HT;
     s_slot[(k - w) + (w % TPI) * NI + w / TPI] = ok ? static_cast<uint32_t>(b * a.block_size + off) : 0u;
   }
-  const uint4* qsrc = reinterpret_cast<const uint4*>(
-      static_cast<const char*>(a.q) + (static_cast<int64_t>(it.row) * a.hq + hq0) * ROWB);
-  for (int c = tid; c < G * LPT; c += 256) s_q[c] = qsrc[c];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r >= n_rows) break;
+    const uint4* qsrc = reinterpret_cast<const uint4*>(
+        static_cast<const char*>(a.q) + (static_cast<int64_t>(row[r]) * a.hq + hq0) * ROWB);
+    for (int c = tid; c < G * LPT; c += 256) s_q[r][c] = qsrc[c];
+  }
+  // rows after the first must name the same blocks over the split
+  bool row_bad[R];
+  row_bad[0] = false;
+  if constexpr (R > 1) {
+    const int j0 = a.bs_log2 >= 0 ? t0 >> a.bs_log2 : t0 / a.block_size;
+    const int j1 = a.bs_log2 >= 0 ? (t1 - 1) >> a.bs_log2 : (t1 - 1) / a.block_size;
+#pragma unroll
+    for (int r = 1; r < R; ++r) {
+      bool mis = false;
+      if (r < n_rows) {
+        const int32_t* btr = a.block_tables + static_cast<int64_t>(seq[r]) * a.max_blocks;
+        for (int j = j0 + tid; j <= j1; j += 256) mis |= btr[j] != bt[j];
+      }
+      row_bad[r] = __syncthreads_or(mis) != 0;
+    }
+  }
   __syncthreads();
 
   const int grp = lane / LPT;               // P.V stage / loads: key group of this lane
@@ -132,15 +181,18 @@ decode_split_kernel(DecodeArgs a) {
   uint4* sk = s_k + wave * HT * LPT;
   float* sp = s_p[wave];
 
-  float m[G], lo[GO], acc[G][EPL];
+  float m[R][G], lo[R][GO], acc[R][G][EPL];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
+  for (int r = 0; r < R; ++r) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+    for (int h = 0; h < G; ++h) {
+      m[r][h] = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[r][h][e] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < GO; ++j) lo[r][j] = 0.f;
   }
-#pragma unroll
-  for (int j = 0; j < GO; ++j) lo[j] = 0.f;
 
   auto load = [&](uint4 (&kr)[NI], uint4 (&vr)[NI], int hs) {
     const uint32_t* sl = s_slot + (hs - t0) + grp * NI;
@@ -164,16 +216,14 @@ decode_split_kernel(DecodeArgs a) {
     }
   };
 
-  auto compute = [&](const uint4 (&kr)[NI], const uint4 (&vr)[NI], int hs) {
-    // q chunks are re-read from LDS in every tile: holding them in registers across the loop
-    // would cost more registers than the K/V buffers
+  // one row's scores, softmax and P.V on the tile staged in sk (K) and vr (V)
+  auto row_tile = [&](const uint4 (&vr)[NI], int hs, int r) {
+    // The lanes exchange p through sp (each lane reads values other lanes wrote). The compiler
+    // barrier makes every row reload them: without it a lane that writes no p for a head (group
+    // sizes below SPL) could be handed the previous row's values it read from the same slots.
     asm volatile("" ::: "memory");
     const int n = min(HT, t1 - hs);
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int tok = i * TPI + grp;
-      sk[tok * LPT + (cl ^ (tok & (LPT - 1)))] = kr[i];
-    }
+    const uint4* sq = s_q[r];
     // scores: lanes SPL k .. SPL k + SPL - 1 hold parts of key k's dot products
     float s[G];
 #pragma unroll
@@ -184,7 +234,7 @@ decode_split_kernel(DecodeArgs a) {
       const uint4 kc = sk[kk * LPT + (c ^ (kk & (LPT - 1)))];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const uint4 qc = s_q[h * LPT + c];
+        const uint4 qc = sq[h * LPT + c];
         if constexpr (BF) {
           s[h] = dot2_bf16(qc.x, kc.x, s[h]);
           s[h] = dot2_bf16(qc.y, kc.y, s[h]);
@@ -211,18 +261,18 @@ decode_split_kernel(DecodeArgs a) {
       // tiles that do not move it skip the wave maxima and the accumulator rescale.
       bool over = false;
 #pragma unroll
-      for (int h = 0; h < G; ++h) over |= s[h] > m[h] + kRescaleLog2;
+      for (int h = 0; h < G; ++h) over |= s[h] > m[r][h] + kRescaleLog2;
       if (__any(over)) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           const float mt = max_over_groups<SPL>(s[h]);
-          const float mn = mt > m[h] + kRescaleLog2 ? mt : m[h];
-          const float al = fast_exp2(m[h] - mn);  // exactly 1 for a head that keeps m
-          m[h] = mn;
+          const float mn = mt > m[r][h] + kRescaleLog2 ? mt : m[r][h];
+          const float al = fast_exp2(m[r][h] - mn);  // exactly 1 for a head that keeps m
+          m[r][h] = mn;
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[h][e] *= al;
+          for (int e = 0; e < EPL; ++e) acc[r][h][e] *= al;
           const int j = G >= SPL ? h / SPL : 0;
-          lo[j] = hf == (G >= SPL ? h % SPL : h) ? lo[j] * al : lo[j];
+          lo[r][j] = hf == (G >= SPL ? h % SPL : h) ? lo[r][j] * al : lo[r][j];
         }
       }
     } else {
@@ -232,38 +282,38 @@ decode_split_kernel(DecodeArgs a) {
       float alpha[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float mn = fmaxf(m[h], max_over_groups<SPL>(s[h]));
-        alpha[h] = fast_exp2(m[h] - mn);
+        const float mn = fmaxf(m[r][h], max_over_groups<SPL>(s[h]));
+        alpha[h] = fast_exp2(m[r][h] - mn);
         moved |= alpha[h] != 1.f;
-        m[h] = mn;
+        m[r][h] = mn;
       }
 #pragma unroll
       for (int j = 0; j < GO; ++j) {
         float av = alpha[G >= SPL ? j * SPL : 0];
 #pragma unroll
-        for (int r = 1; r < (G >= SPL ? SPL : G); ++r)
-          av = hf == r ? opaque(alpha[j * SPL + r]) : av;
-        lo[j] *= av;
+        for (int q = 1; q < (G >= SPL ? SPL : G); ++q)
+          av = hf == q ? opaque(alpha[j * SPL + q]) : av;
+        lo[r][j] *= av;
       }
       if (__any(moved)) {
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha[h];
+          for (int e = 0; e < EPL; ++e) acc[r][h][e] *= alpha[h];
       }
     }
     // p of (key kk, head h) is formed by the lane of that key with hf == h % SPL (heads
     // below SPL: by the lanes hf < G, the others idle)
 #pragma unroll
     for (int j = 0; j < GO; ++j) {
-      float sv = s[G >= SPL ? j * SPL : 0], mv = m[G >= SPL ? j * SPL : 0];
+      float sv = s[G >= SPL ? j * SPL : 0], mv = m[r][G >= SPL ? j * SPL : 0];
 #pragma unroll
-      for (int r = 1; r < (G >= SPL ? SPL : G); ++r) {
-        sv = hf == r ? opaque(s[j * SPL + r]) : sv;
-        mv = hf == r ? opaque(m[j * SPL + r]) : mv;
+      for (int q = 1; q < (G >= SPL ? SPL : G); ++q) {
+        sv = hf == q ? opaque(s[j * SPL + q]) : sv;
+        mv = hf == q ? opaque(m[r][j * SPL + q]) : mv;
       }
       const float p = fast_exp2(sv - mv);
-      lo[j] += p;
+      lo[r][j] += p;
       if (G >= SPL || hf < G) sp[kk * G + j * SPL + hf] = p;
     }
     // P.V, split-D layout: this lane owns columns cl*EPL .. +EPL of keys i*TPI + grp
@@ -294,7 +344,23 @@ decode_split_kernel(DecodeArgs a) {
 #pragma unroll
       for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pp[h], vf[e], acc[h][e]);
+        for (int e = 0; e < EPL; ++e) acc[r][h][e] = fmaf(pp[h], vf[e], acc[r][h][e]);
+    }
+  };
+
+  auto compute = [&](const uint4 (&kr)[NI], const uint4 (&vr)[NI], int hs) {
+    // q chunks are re-read from LDS in every tile: holding them in registers across the loop
+    // would cost more registers than the K/V buffers
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int tok = i * TPI + grp;
+      sk[tok * LPT + (cl ^ (tok & (LPT - 1)))] = kr[i];
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (r >= n_rows) break;
+      row_tile(vr, hs, r);
     }
   };
 
@@ -314,58 +380,63 @@ decode_split_kernel(DecodeArgs a) {
     hs = hs2;
   }
 
-  // wave totals: l over the lanes that formed it, acc over the TPI key groups
-#pragma unroll
-  for (int j = 0; j < GO; ++j) lo[j] = sum_same_class<SPL>(lo[j]);
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] = sum_key_groups<LPT>(acc[h][e]);
-
-  const bool bad_row = __syncthreads_or(bad) != 0;  // also: every wave is done with s_k
+  const bool bad_blk = __syncthreads_or(bad) != 0;  // also: every wave is done with s_k
   float* mg_acc = reinterpret_cast<float*>(s_k);             // [4][G][D]
   float* mg_m = mg_acc + kDecodeWaves * G * D;                // [4][G]
   float* mg_l = mg_m + kDecodeWaves * G;                      // [4][G]
-  if (lane < LPT) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r >= n_rows) break;
+    if (r > 0) __syncthreads();   // the previous row's merge has read the scratch
+    // wave totals: l over the lanes that formed it, acc over the TPI key groups
+#pragma unroll
+    for (int j = 0; j < GO; ++j) lo[r][j] = sum_same_class<SPL>(lo[r][j]);
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) mg_acc[(wave * G + h) * D + lane * EPL + e] = acc[h][e];
-  }
-  if (lane == 0) {
+      for (int e = 0; e < EPL; ++e) acc[r][h][e] = sum_key_groups<LPT>(acc[r][h][e]);
+    if (lane < LPT) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) mg_m[wave * G + h] = m[h];
-  }
-  if (lane < (G >= SPL ? SPL : G)) {
+      for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int j = 0; j < GO; ++j) mg_l[wave * G + j * SPL + lane] = lo[j];
-  }
-  __syncthreads();
-  for (int idx = tid; idx < G * D; idx += 256) {
-    const int h = idx / D;
-    const int d = idx - h * D;
-    float M = mg_m[h];
-#pragma unroll
-    for (int w = 1; w < kDecodeWaves; ++w) M = fmaxf(M, mg_m[w * G + h]);
-    float num = 0.f, den = 0.f;
-#pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) {
-      const float fw = fast_exp2(mg_m[w * G + h] - M);
-      num = fmaf(fw, mg_acc[(w * G + h) * D + d], num);
-      den = fmaf(fw, mg_l[w * G + h], den);
+        for (int e = 0; e < EPL; ++e) mg_acc[(wave * G + h) * D + lane * EPL + e] = acc[r][h][e];
     }
-    const uint32_t nan_bits = 0x7fc00000u;
-    const int hq = hq0 + h;
-    if (it.part < 0) {
-      const float o = num / den;
-      a.out[(static_cast<int64_t>(it.row) * a.hq + hq) * D + d] =
-          __uint_as_float(bad_row ? nan_bits : __float_as_uint(o));
-    } else {
-      const int64_t p = static_cast<int64_t>(it.part + it.split) * a.hq + hq;
-      a.part_acc[p * D + d] = __uint_as_float(bad_row ? nan_bits : __float_as_uint(num));
-      if (d == 0) {
-        a.part_m[p] = M;
-        a.part_l[p] = __uint_as_float(bad_row ? nan_bits : __float_as_uint(den));
+    if (lane == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) mg_m[wave * G + h] = m[r][h];
+    }
+    if (lane < (G >= SPL ? SPL : G)) {
+#pragma unroll
+      for (int j = 0; j < GO; ++j) mg_l[wave * G + j * SPL + lane] = lo[r][j];
+    }
+    __syncthreads();
+    const bool bad_row = bad_blk || row_bad[r];
+    for (int idx = tid; idx < G * D; idx += 256) {
+      const int h = idx / D;
+      const int d = idx - h * D;
+      float M = mg_m[h];
+#pragma unroll
+      for (int w = 1; w < kDecodeWaves; ++w) M = fmaxf(M, mg_m[w * G + h]);
+      float num = 0.f, den = 0.f;
+#pragma unroll
+      for (int w = 0; w < kDecodeWaves; ++w) {
+        const float fw = fast_exp2(mg_m[w * G + h] - M);
+        num = fmaf(fw, mg_acc[(w * G + h) * D + d], num);
+        den = fmaf(fw, mg_l[w * G + h], den);
+      }
+      const uint32_t nan_bits = 0x7fc00000u;
+      const int hq = hq0 + h;
+      if (part[r] < 0) {
+        const float o = num / den;
+        a.out[(static_cast<int64_t>(row[r]) * a.hq + hq) * D + d] =
+            __uint_as_float(bad_row ? nan_bits : __float_as_uint(o));
+      } else {
+        const int64_t p = static_cast<int64_t>(part[r] + split) * a.hq + hq;
+        a.part_acc[p * D + d] = __uint_as_float(bad_row ? nan_bits : __float_as_uint(num));
+        if (d == 0) {
+          a.part_m[p] = M;
+          a.part_l[p] = __uint_as_float(bad_row ? nan_bits : __float_as_uint(den));
+        }
       }
     }
   }
@@ -677,6 +748,42 @@ static hipError_t launch_decode_d(const DecodeArgs& a, uint32_t grid, int group,
     case 2: launch_one<D, BF, 2>(a, grid, stream); break;
     case 4: launch_one<D, BF, 4>(a, grid, stream); break;
     case 8: launch_one<D, BF, 8>(a, grid, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// Group items: bf16 groups up to 4, the single-row kernel with the state of kGroupR rows at
+// kGroupW waves per SIMD (measured on the prefix-shared step: 2 rows at two waves per SIMD
+// 151 us per decode pass beside the per-row launch; 4 rows at one wave 183 us; wider row
+// sets spill at two waves).
+constexpr int kGroupR = 2;
+constexpr int kGroupW = 2;
+bool decode_groups_supported(int head_dim, int group) {
+  return (head_dim == 64 || head_dim == 128) && (group == 1 || group == 2 || group == 4);
+}
+int decode_group_rows() { return kGroupR; }
+
+template <int D, int G>
+static void launch_group_one(const DecodeArgs& a, uint32_t grid, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_split_kernel<D, G, true, tile_keys<D, true, G>(), kGroupW, kGroupR>),
+                     dim3(grid), dim3(256), 0, stream, a);
+}
+
+hipError_t launch_decode_groups(const DecodeArgs& a, int64_t n_groups, int head_dim, int group,
+                                hipStream_t stream) {
+  const int64_t grid64 = n_groups * a.hkv;
+  if (grid64 == 0) return hipSuccess;
+  if (grid64 > 0x7fffffffLL || a.group != group || !decode_groups_supported(head_dim, group))
+    return hipErrorInvalidValue;
+  const uint32_t grid = static_cast<uint32_t>(grid64);
+  switch (group * 1000 + head_dim) {
+    case 1064: launch_group_one<64, 1>(a, grid, stream); break;
+    case 2064: launch_group_one<64, 2>(a, grid, stream); break;
+    case 4064: launch_group_one<64, 4>(a, grid, stream); break;
+    case 1128: launch_group_one<128, 1>(a, grid, stream); break;
+    case 2128: launch_group_one<128, 2>(a, grid, stream); break;
+    case 4128: launch_group_one<128, 4>(a, grid, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -55,6 +55,7 @@ struct DecodeArgs {
                       // (E4M3 pools: times the K scale as well)
   float v_scale;      // E4M3 pools: the V scale (1 otherwise)
   const DecodeItem* items;
+  const DecodeGroupItem* groups;  // group items (launch_decode_groups only)
   float* out;
   float* part_m;
   float* part_l;
@@ -120,11 +121,18 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, int64_t n_items, int head_dim,
 hipError_t launch_decode(const DecodeArgs& a, int64_t n_items, int head_dim, int group,
                          bool bf16, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int64_t n_items, int head_dim, hipStream_t stream);
+// The group items a.groups[0 .. n_groups): each row computed exactly as by launch_decode.
+hipError_t launch_decode_groups(const DecodeArgs& a, int64_t n_groups, int head_dim, int group,
+                                hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int64_t n_items, int head_dim, int group,
                           bool fp8, hipStream_t stream);
 
 // Whether a (head_dim, group, dtype) combination has a built decode / prefill kernel.
 bool decode_supported(int head_dim, int group);
+// Whether a (head_dim, group) combination of bf16 pools has a group-item decode kernel, and
+// how many rows its group items hold at most.
+bool decode_groups_supported(int head_dim, int group);
+int decode_group_rows();
 bool decode_fp8_supported(int head_dim, int group);
 bool prefill_supported(int head_dim, int group, bool bf16);
 

@@ -33,6 +33,24 @@ struct DecodeItem {
   int32_t pad0, pad1, pad2;
 };
 
+// Rows per group item at most.
+constexpr int kGroupRows = 4;
+
+// One decode split read once for several rows: split `split` of rows row[0 .. n_rows) (of
+// sequences seq[]), whose block tables hold the same physical blocks over the split's keys
+// [split * kv_split, (split + 1) * kv_split) and whose contexts cover the whole split (n_keys,
+// the smallest of theirs, is at least (split + 1) * kv_split). Each row's arithmetic is that of
+// its single-row item; row r writes its output (part[r] < 0) or partial slot part[r] + split.
+struct DecodeGroupItem {
+  int32_t split;
+  int32_t n_rows;
+  int32_t n_keys;
+  int32_t pad;
+  int32_t row[kGroupRows];
+  int32_t seq[kGroupRows];
+  int32_t part[kGroupRows];
+};
+
 // Split merge of one query row: partial slots part .. part + n_splits - 1, in ascending order.
 struct MergeItem {
   int32_t row;
@@ -59,9 +77,9 @@ struct PrefillItem {
 
 // Byte offsets of each region inside the caller's workspace (all 256-byte aligned).
 struct WorkspaceLayout {
-  size_t decode_off = 0, merge_off = 0, prefill_off = 0, slots_off = 0, part_m_off = 0,
-         part_l_off = 0, part_acc_off = 0, total = 0;
-  int64_t n_decode = 0, n_merge = 0, n_prefill = 0, n_part = 0;
+  size_t decode_off = 0, group_off = 0, merge_off = 0, prefill_off = 0, slots_off = 0,
+         part_m_off = 0, part_l_off = 0, part_acc_off = 0, total = 0;
+  int64_t n_decode = 0, n_group = 0, n_merge = 0, n_prefill = 0, n_part = 0;
   size_t list_bytes = 0;  // lists (+ fused-append slots): the part copied from the host
 };
 

@@ -2,7 +2,11 @@
 #include "planner.h"
 
 #include <algorithm>
+#include <climits>
+#include <map>
+#include <set>
 #include <string>
+#include <vector>
 
 #include "common.h"
 
@@ -10,7 +14,100 @@ namespace pkv {
 
 namespace {
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
 }  // namespace
+
+bool SharedSplits::contains(int32_t row, int32_t split) const {
+  return std::binary_search(taken.begin(), taken.end(), std::make_pair(row, split));
+}
+
+SharedSplits find_shared_splits(const StepShape& s) {
+  SharedSplits out;
+  if (s.bt_host == nullptr || s.group_rows < 2 || s.block_size <= 0) return out;
+  // one record per whole split of a decode row, keyed by a hash of the split index and the
+  // block ids covering it (no allocation per split); equal keys are compared id by id below
+  struct Rec {
+    uint64_t h;
+    int32_t split, row, seq, n_keys, part;
+    int64_t j0, j1;
+  };
+  std::vector<Rec> recs;
+  int64_t part = 0;
+  for (int32_t b = 0; b < s.B; ++b) {
+    const int32_t ql = s.cu[b + 1] - s.cu[b];
+    if (ql == 0) continue;
+    if (on_tiles(s, ql)) {
+      if (s.tile_split > 0) {
+        const int64_t ns_max = ceil_div(s.ctx[b], s.tile_split);
+        if (ns_max > 1) part += static_cast<int64_t>(ql) * ns_max;
+      }
+      continue;
+    }
+    const int32_t* tb = s.bt_host + static_cast<int64_t>(b) * s.bt_stride;
+    for (int32_t i = 0; i < ql; ++i) {
+      const int32_t row = s.cu[b] + i;
+      const int32_t n_keys = s.ctx[b] - ql + i + 1;
+      const int32_t ns = static_cast<int32_t>(ceil_div(n_keys, s.kv_split));
+      const int32_t pbase = ns > 1 ? static_cast<int32_t>(part) : -1;
+      if (ns > 1) part += ns;
+      for (int32_t sp = 0; sp < ns; ++sp) {
+        const int64_t k1 = static_cast<int64_t>(sp + 1) * s.kv_split;   // the split's end
+        if (k1 > n_keys) continue;                                       // not a whole split
+        const int64_t j0 = static_cast<int64_t>(sp) * s.kv_split / s.block_size;
+        const int64_t j1 = (k1 - 1) / s.block_size;
+        uint64_t h = 1469598103934665603ull ^ static_cast<uint64_t>(sp);
+        for (int64_t j = j0; j <= j1; ++j) {
+          h ^= static_cast<uint32_t>(tb[j]);
+          h *= 1099511628211ull;
+        }
+        recs.push_back(Rec{h, sp, row, b, n_keys, pbase, j0, j1});
+      }
+    }
+  }
+  // equal keys together, in step order within a key
+  std::stable_sort(recs.begin(), recs.end(), [](const Rec& x, const Rec& y) {
+    return x.h != y.h ? x.h < y.h : x.split < y.split;
+  });
+  const auto same_blocks = [&](const Rec& x, const Rec& y) {
+    if (x.split != y.split) return false;
+    const int32_t* tx = s.bt_host + static_cast<int64_t>(x.seq) * s.bt_stride;
+    const int32_t* ty = s.bt_host + static_cast<int64_t>(y.seq) * s.bt_stride;
+    return std::equal(tx + x.j0, tx + x.j1 + 1, ty + y.j0);
+  };
+  for (size_t i0 = 0; i0 < recs.size();) {
+    size_t i1 = i0 + 1;
+    while (i1 < recs.size() && recs[i1].h == recs[i0].h && recs[i1].split == recs[i0].split) ++i1;
+    // members that name exactly the first one's blocks (a hash collision leaves the others
+    // as per-row items)
+    std::vector<size_t> mem;
+    for (size_t k = i0; k < i1; ++k)
+      if (k == i0 || same_blocks(recs[i0], recs[k])) mem.push_back(k);
+    for (size_t m0 = 0; m0 < mem.size(); m0 += s.group_rows) {
+      const size_t n = std::min(mem.size() - m0, static_cast<size_t>(s.group_rows));
+      if (n < 2) break;
+      DecodeGroupItem gi{};
+      gi.split = recs[mem[m0]].split;
+      gi.n_rows = static_cast<int32_t>(n);
+      gi.n_keys = INT32_MAX;
+      for (int r = 0; r < kGroupRows; ++r) {
+        gi.row[r] = gi.seq[r] = 0;
+        gi.part[r] = -1;
+      }
+      for (size_t r = 0; r < n; ++r) {
+        const Rec& m = recs[mem[m0 + r]];
+        gi.row[r] = m.row;
+        gi.seq[r] = m.seq;
+        gi.part[r] = m.part;
+        gi.n_keys = std::min(gi.n_keys, m.n_keys);
+        out.taken.push_back({m.row, gi.split});
+      }
+      out.groups.push_back(gi);
+    }
+    i0 = i1;
+  }
+  std::sort(out.taken.begin(), out.taken.end());
+  return out;
+}
 
 bool on_tiles(const StepShape& s, int32_t ql) { return s.all_mfma || (ql > 1 && s.prefill_on_mfma); }
 
@@ -50,9 +147,17 @@ WorkspaceLayout layout_for(const StepShape& s, int32_t hq, int32_t head_dim,
       }
     }
   }
+  if (s.bt_host != nullptr && s.group_rows > 1) {
+    SharedSplits local;
+    const SharedSplits& sh = s.shared != nullptr ? *s.shared : (local = find_shared_splits(s));
+    L.n_group = static_cast<int64_t>(sh.groups.size());
+    L.n_decode -= static_cast<int64_t>(sh.taken.size());
+  }
   size_t off = 0;
   L.decode_off = off;
   off = align_up(off + L.n_decode * sizeof(DecodeItem));
+  L.group_off = off;
+  off = align_up(off + L.n_group * sizeof(DecodeGroupItem));
   L.merge_off = off;
   off = align_up(off + L.n_merge * sizeof(MergeItem));
   L.prefill_off = off;
@@ -71,6 +176,11 @@ WorkspaceLayout layout_for(const StepShape& s, int32_t hq, int32_t head_dim,
 }
 
 void build_lists(const StepShape& s, const WorkspaceLayout& L, char* host) {
+  SharedSplits local;
+  const SharedSplits& sh = L.n_group == 0 ? local
+                           : s.shared != nullptr ? *s.shared : (local = find_shared_splits(s));
+  std::copy(sh.groups.begin(), sh.groups.end(),
+            reinterpret_cast<DecodeGroupItem*>(host + L.group_off));
   auto* dec = reinterpret_cast<DecodeItem*>(host + L.decode_off);
   auto* mer = reinterpret_cast<MergeItem*>(host + L.merge_off);
   auto* pre = reinterpret_cast<PrefillItem*>(host + L.prefill_off);
@@ -115,7 +225,9 @@ void build_lists(const StepShape& s, const WorkspaceLayout& L, char* host) {
         mer[nm++] = MergeItem{row, ns, pbase, 0};
         part += ns;
       }
-      for (int32_t sp = 0; sp < ns; ++sp) dec[nd++] = DecodeItem{row, b, n_keys, sp, pbase, 0, 0, 0};
+      for (int32_t sp = 0; sp < ns; ++sp)
+        if (sh.taken.empty() || !sh.contains(row, sp))
+          dec[nd++] = DecodeItem{row, b, n_keys, sp, pbase, 0, 0, 0};
     }
   }
   // longest work first: short tail items then fill the gaps at the end of each launch (item

@@ -232,12 +232,36 @@ void fuzz_planner(Rng& rng, long* counters) {
   s.all_mfma = consistent;
   s.prefill_rows_per_item = 128 / group;
   s.tile_split = consistent ? kv_split : 0;
+  // host tables for shared reads: some rows copy a prefix of an earlier row's blocks
+  const int bs = 1 << uni(rng, 0, 6);
+  int max_blocks = 1;
+  for (int b = 0; b < B; ++b) max_blocks = std::max(max_blocks, (ctx[b] + bs - 1) / bs);
+  std::vector<int32_t> tables(static_cast<size_t>(std::max(B, 1)) * max_blocks, -1);
+  int next_block = 0;
+  for (int b = 0; b < B; ++b) {
+    const int nb = (ctx[b] + bs - 1) / bs;
+    const int src = b > 0 && unif(rng) < 0.6 ? uni(rng, 0, b - 1) : -1;
+    const int nsrc = src >= 0 ? (ctx[src] + bs - 1) / bs : 0;
+    const int shared = src >= 0 ? uni(rng, 0, std::min(nb, nsrc)) : 0;
+    for (int j = 0; j < nb; ++j)
+      tables[static_cast<size_t>(b) * max_blocks + j] =
+          j < shared ? tables[static_cast<size_t>(src) * max_blocks + j] : next_block++;
+  }
+  const int gr = std::vector<int>{0, 2, 4}[uni(rng, 0, 2)];
+  if (gr > 0) {
+    s.bt_host = tables.data();
+    s.bt_stride = max_blocks;
+    s.block_size = bs;
+    s.group_rows = gr;
+  }
   const int n_write = uni(rng, 0, 50);
   const pkv::WorkspaceLayout L = pkv::layout_for(s, hq, head_dim, n_write);
   // the lists exactly as large as the layout says: ASan reports a write past them
   std::vector<char> host(L.list_bytes);
   pkv::build_lists(s, L, host.data());
-  CHECK(L.decode_off + L.n_decode * sizeof(pkv::DecodeItem) <= L.merge_off);
+  CHECK(L.decode_off + L.n_decode * sizeof(pkv::DecodeItem) <= L.group_off);
+  CHECK(L.group_off + L.n_group * sizeof(pkv::DecodeGroupItem) <= L.merge_off);
+  CHECK(gr > 0 || L.n_group == 0);
   CHECK(L.merge_off + L.n_merge * sizeof(pkv::MergeItem) <= L.prefill_off);
   CHECK(L.prefill_off + L.n_prefill * sizeof(pkv::PrefillItem) <= L.slots_off);
   CHECK(L.slots_off + n_write * sizeof(int32_t) <= L.list_bytes);
@@ -250,14 +274,51 @@ void fuzz_planner(Rng& rng, long* counters) {
   std::vector<int> part_use(static_cast<size_t>(L.n_part), 0);
   // decode rows: splits 0..ns-1 once each; a merge and ns partial slots iff ns > 1
   std::map<int, std::vector<int>> splits_of_row;
-  std::map<int, const pkv::DecodeItem*> any_item;
+  std::map<int, int> part_of_row;           // a row's partial base, as its items carry it
+  std::map<int, int> keys_of_row;
   for (int64_t i = 0; i < L.n_decode; ++i) {
     splits_of_row[dec[i].row].push_back(dec[i].split);
-    any_item[dec[i].row] = &dec[i];
+    part_of_row[dec[i].row] = dec[i].part;
+    keys_of_row[dec[i].row] = dec[i].n_keys;
+    CHECK(dec[i].seq >= 0 && dec[i].seq < B);
     if (dec[i].part >= 0) {
       const int64_t p = static_cast<int64_t>(dec[i].part) + dec[i].split;
       CHECK(p >= 0 && p < L.n_part);
       part_use[p] += 1;
+    }
+  }
+  // group items: 2 .. group_rows rows, a whole split of each, the same blocks over it
+  const auto* grpi = reinterpret_cast<const pkv::DecodeGroupItem*>(host.data() + L.group_off);
+  std::map<int, int> seq_of_row;
+  for (int b = 0; b < B; ++b)
+    for (int r = cu[b]; r < cu[b + 1]; ++r) seq_of_row[r] = b;
+  for (int64_t i = 0; i < L.n_group; ++i) {
+    const pkv::DecodeGroupItem& gi = grpi[i];
+    counters[7] += 1;
+    CHECK(gi.n_rows >= 2 && gi.n_rows <= gr && gi.n_rows <= pkv::kGroupRows);
+    const int64_t k1 = static_cast<int64_t>(gi.split + 1) * kv_split;
+    CHECK(gi.n_keys >= k1);
+    const int j0 = gi.split * kv_split / bs;
+    const int j1 = static_cast<int>((k1 - 1) / bs);
+    for (int r = 0; r < gi.n_rows; ++r) {
+      const int row = gi.row[r];
+      CHECK(seq_of_row.count(row) == 1 && seq_of_row[row] == gi.seq[r]);
+      const int b = gi.seq[r];
+      const int ql = cu[b + 1] - cu[b];
+      const int n_keys = ctx[b] - ql + (row - cu[b]) + 1;
+      CHECK(n_keys >= k1);
+      for (int j = j0; j <= j1; ++j)
+        CHECK(tables[static_cast<size_t>(b) * max_blocks + j] ==
+              tables[static_cast<size_t>(gi.seq[0]) * max_blocks + j]);
+      splits_of_row[row].push_back(gi.split);
+      if (part_of_row.count(row)) CHECK(part_of_row[row] == gi.part[r]);
+      part_of_row[row] = gi.part[r];
+      keys_of_row[row] = n_keys;
+      if (gi.part[r] >= 0) {
+        const int64_t p = static_cast<int64_t>(gi.part[r]) + gi.split;
+        CHECK(p >= 0 && p < L.n_part);
+        part_use[p] += 1;
+      }
     }
   }
   std::map<int, const pkv::MergeItem*> merge_of_row;
@@ -282,11 +343,10 @@ void fuzz_planner(Rng& rng, long* counters) {
       std::sort(sp.begin(), sp.end());
       CHECK(static_cast<int>(sp.size()) == ns);
       for (int k = 0; k < ns; ++k) CHECK(sp[k] == k);
-      const pkv::DecodeItem* it = any_item[row];
-      CHECK(it->seq == b && it->n_keys == n_keys);
+      CHECK(keys_of_row[row] == n_keys);
       CHECK((ns > 1) == (merge_of_row.count(row) == 1));
-      if (ns > 1) CHECK(merge_of_row[row]->n_splits == ns && merge_of_row[row]->part == it->part);
-      else CHECK(it->part < 0);
+      if (ns > 1) CHECK(merge_of_row[row]->n_splits == ns && merge_of_row[row]->part == part_of_row[row]);
+      else CHECK(part_of_row[row] < 0);
     }
   }
   // tile-path rows: each row once per split its last key reaches (once without splits)
@@ -330,15 +390,16 @@ int main(int argc, char** argv) {
   const unsigned long seed = argc > 1 ? std::strtoul(argv[1], nullptr, 10) : 1;
   const int rounds = argc > 2 ? std::atoi(argv[2]) : 20;
   Rng rng(seed);
-  long counters[7] = {0, 0, 0, 0, 0, 0, 0};
+  long counters[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int r = 0; r < rounds && g_fail == 0; ++r) {
     fuzz_allocator(rng, 2000, counters);
     fuzz_scheduler(rng, 300, counters);
     for (int k = 0; k < 50 && g_fail == 0; ++k) fuzz_planner(rng, counters);
   }
   std::printf("host_fuzz seed=%lu rounds=%d exhaustions=%ld shared_admits=%ld refusals=%ld "
-              "sched_rows=%ld preemptions=%ld copies=%ld planned_items=%ld failures=%d\n",
+              "sched_rows=%ld preemptions=%ld copies=%ld planned_items=%ld group_items=%ld "
+              "failures=%d\n",
               seed, rounds, counters[0], counters[1], counters[2], counters[3], counters[4],
-              counters[5], counters[6], g_fail);
+              counters[5], counters[6], counters[7], g_fail);
   return g_fail == 0 ? 0 : 1;
 }

@@ -333,7 +333,8 @@ def test_fused_step_workspace_holds_the_slots():
 
 
 def test_profile_kind_mask_validation():
-    assert pkv.lib().pkv_profile_set_kinds(0x10) == L.PKV_ERR_INVALID
+    assert pkv.lib().pkv_profile_set_kinds(0x20) == L.PKV_ERR_INVALID
+    assert pkv.lib().pkv_profile_set_kinds(0x1F) == L.PKV_OK
     pkv.profile_set_kinds(["decode"])
     pkv.profile_set_kinds(["write_kv", "prefill", "decode", "merge"])
 

@@ -49,3 +49,4 @@ def test_host_code_is_clean_under_asan_and_ubsan(fuzz_binary, seed):
     # the traces reached the cases they are meant to reach
     assert int(fields["exhaustions"]) > 100 and int(fields["shared_admits"]) > 100
     assert int(fields["refusals"]) > 100 and int(fields["preemptions"]) > 0
+    assert int(fields["group_items"]) > 100
