@@ -17,8 +17,9 @@ GB/s (KV bytes read + append bytes moved, per step time). The mixed ragged step
 batched decode step over E4M3 pools with per-tensor scales (pkv_write_kv_attention_fp8; its
 bytes counted at one byte per cached element).
 
-The long-context decode step (8 x 40960 keys, G 8, block 32) and the prefix-shared group decode
-step (16 groups x 8 samples sharing a 2048-token prompt) are timed the same way; decode-only
+The long-context decode step (8 x 40960 keys, G 8, block 32; also over E4M3 pools) and the
+prefix-shared group decode step (16 groups x 8 samples sharing a 2048-token prompt) are timed
+the same way; decode-only
 steps carry a `roofline` object for their decode kernel (the prefix-shared step also on unique
 bytes). Each workload also gets the flushed-cache protocol (median, p10 and p90 of HIP-event
 step times over `--protocol-reps` reps, each after a 2 GiB scratch write that evicts L2 and the
@@ -52,7 +53,8 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="batched-bf16-decode")
     ap.add_argument("--extra", default="mixed-ragged-step,long-context-decode,"
-                                       "prefix-shared-decode,batched-fp8-decode,mixed-fp8-step",
+                                       "prefix-shared-decode,batched-fp8-decode,mixed-fp8-step,"
+                                       "long-context-fp8-decode",
                     help="comma-separated workloads timed the same way, reported under 'extra'")
     ap.add_argument("--protocol-reps", type=int, default=50,
                     help="reps of the flushed-cache protocol per workload (median, p10, p90 of "

@@ -412,7 +412,7 @@ int32_t pkv_write_kv_attention_shared(const void* q, const void* k_new, const vo
  * row) on the MFMA tile path, which widens each tile's codes to bfloat16 in LDS. Codes widen
  * exactly (every E4M3 value is a bfloat16 value); k_scale folds into the score scale, v_scale
  * multiplies each split numerator (decode) or output (tiles) once. head_dim 64 or 128,
- * num_q_heads / num_kv_heads in {1, 2, 4}; flags as pkv_attention_ex. Workspace from
+ * num_q_heads / num_kv_heads in {1, 2, 4, 8}; flags as pkv_attention_ex. Workspace from
  * pkv_attention_fp8_workspace_size (same flags), same ownership rules as pkv_attention.
  * Errors: as pkv_attention_ex, plus PKV_ERR_INVALID for scales that are not finite and > 0. */
 int32_t pkv_write_kv_fp8(const void* k_new, const void* v_new, const int32_t* slots_dev,

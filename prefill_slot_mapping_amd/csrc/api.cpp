@@ -478,7 +478,7 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
     if (dtype != PKV_BF16) return fail(PKV_ERR_INVALID, "attention_fp8: q must be bfloat16");
     if (!pkv::decode_fp8_supported(head_dim, num_q_heads / num_kv_heads))
       return fail(PKV_ERR_UNSUPPORTED, "attention_fp8: head_dim 64 or 128 and num_q_heads / "
-                                       "num_kv_heads one of 1, 2, 4");
+                                       "num_kv_heads one of 1, 2, 4, 8");
     for (int i = 0; i < 2; ++i)
       if (!(std::isfinite(fp8_scales[i]) && fp8_scales[i] > 0.f))
         return fail(PKV_ERR_INVALID, "attention_fp8: scales must be finite and > 0");
@@ -753,7 +753,7 @@ int32_t workspace_size_impl(const int32_t* ctx_lens_host, const int32_t* cu_seql
                           block_size, fp8);
   if (fp8 && !pkv::decode_fp8_supported(head_dim, num_q_heads / num_kv_heads))
     return fail(PKV_ERR_UNSUPPORTED, "attention_fp8: head_dim 64 or 128 and num_q_heads / "
-                                     "num_kv_heads one of 1, 2, 4");
+                                     "num_kv_heads one of 1, 2, 4, 8");
   *bytes = layout_for(s, num_q_heads, head_dim, n_write_rows).total;
   return ok();
 }

@@ -328,11 +328,21 @@ decode_fp8_kernel(DecodeArgs a) {
 }
 
 bool decode_fp8_supported(int head_dim, int group) {
-  return (head_dim == 64 || head_dim == 128) && (group == 1 || group == 2 || group == 4);
+  return (head_dim == 64 || head_dim == 128) &&
+         (group == 1 || group == 2 || group == 4 || group == 8);
 }
 
 // Instances (keys per tile, waves-per-SIMD register budget, ring depth), measured on the
 // batched 64-sequence step (groups of 4) and 32-sequence steps with groups of 1 and 2.
+#ifndef PKV_F8G8_HT
+#define PKV_F8G8_HT 16
+#endif
+#ifndef PKV_F8G8_W
+#define PKV_F8G8_W 2
+#endif
+#ifndef PKV_F8G8_NB
+#define PKV_F8G8_NB 2
+#endif
 template <int D>
 static hipError_t launch_fp8_d(const DecodeArgs& a, uint32_t grid, int group,
                                hipStream_t stream) {
@@ -340,6 +350,7 @@ static hipError_t launch_fp8_d(const DecodeArgs& a, uint32_t grid, int group,
     case 1: hipLaunchKernelGGL((decode_fp8_kernel<D, 1, 32, 3, 2>), dim3(grid), dim3(256), 0, stream, a); break;
     case 2: hipLaunchKernelGGL((decode_fp8_kernel<D, 2, 32, 3, 2>), dim3(grid), dim3(256), 0, stream, a); break;
     case 4: hipLaunchKernelGGL((decode_fp8_kernel<D, 4, 16, 4, 3>), dim3(grid), dim3(256), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((decode_fp8_kernel<D, 8, PKV_F8G8_HT, PKV_F8G8_W, PKV_F8G8_NB>), dim3(grid), dim3(256), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -535,6 +535,7 @@ static hipError_t launch_prefill_d(const PrefillArgs& a, uint32_t grid, int grou
       case 1: hipLaunchKernelGGL((prefill_kernel<D, 1, true>), dim3(grid), dim3(256), 0, stream, a); break;
       case 2: hipLaunchKernelGGL((prefill_kernel<D, 2, true>), dim3(grid), dim3(256), 0, stream, a); break;
       case 4: hipLaunchKernelGGL((prefill_kernel<D, 4, true>), dim3(grid), dim3(256), 0, stream, a); break;
+      case 8: hipLaunchKernelGGL((prefill_kernel<D, 8, true>), dim3(grid), dim3(256), 0, stream, a); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -393,7 +393,7 @@ def _attn_fp8(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(hq=16, hkv=2), L.PKV_ERR_UNSUPPORTED),            # group 8 has no E4M3 instance
+    (dict(hq=32, hkv=2), L.PKV_ERR_UNSUPPORTED),            # group 16 has no instance
     (dict(d=96), L.PKV_ERR_UNSUPPORTED),
     (dict(ks=0.0), L.PKV_ERR_INVALID),
     (dict(vs=float("nan")), L.PKV_ERR_INVALID),
@@ -420,7 +420,7 @@ def test_attention_fp8_reaches_the_workspace_check_and_routes_rows_as_bf16():
             bf = pkv.attention_workspace_size(ctx, cu, 8, 2, 128, 512, phase_consistent=pc)
             assert f8 == bf
     with pytest.raises(pkv.Unsupported):
-        pkv.attention_fp8_workspace_size([5], [0, 1], 16, 2, 128, 512)
+        pkv.attention_fp8_workspace_size([5], [0, 1], 32, 2, 128, 512)
 
 
 def test_misaligned_device_pointers_are_refused():
@@ -451,7 +451,7 @@ def test_fused_fp8_step_validation():
     assert call(slots=(7, 7, -1)) == L.PKV_ERR_INVALID        # one slot twice
     assert b"twice" in pkv.lib().pkv_last_error()
     assert call(ks=-1.0) == L.PKV_ERR_INVALID
-    assert call(hq=16) == L.PKV_ERR_UNSUPPORTED
+    assert call(hq=32) == L.PKV_ERR_UNSUPPORTED
     assert call(wsb=16) == L.PKV_ERR_INVALID
     assert b"workspace" in pkv.lib().pkv_last_error()
     assert call(flags=4) == L.PKV_ERR_INVALID

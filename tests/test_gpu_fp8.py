@@ -120,6 +120,10 @@ EDGE = [
     (4, 4, 64, 1, [(1, 1), (5, 5), (300, 1), (70, 3)]),
     (16, 8, 64, 32, [(3, 1), (100, 100), (1300, 1), (97, 33)]),
     (16, 4, 64, 64, [(128, 1), (129, 2), (1, 1), (4097, 1)], {"kv_split": 2048}),
+    # groups of 8: the decode pass and the tile path at head_dim 128 and 64
+    (64, 8, 128, 32, [(17, 1), (4097, 1), (2049, 1), (300, 90)], {"kv_split": 2048}),
+    (16, 2, 128, 5, [(7, 1), (129, 1), (1500, 1), (88, 20)]),
+    (32, 4, 64, 16, [(2, 1), (513, 1), (1100, 1), (40, 9)]),
 ]
 
 

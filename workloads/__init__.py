@@ -367,6 +367,12 @@ FP8_CONFIGS = {
                            decode_ctx=("lognormal", 3000, 1.0, 16, 16384, 120),
                            prefill=(8, 512, 0, 8192), interleave=True,
                            kv_dtype="fp8", k_scale=1 / 64, v_scale=1 / 64),
+    # the long-context step (G 8, 8 x 40960 keys, 1 % of K rows x 8) over E4M3 pools; the K
+    # scale 1/8 keeps the outlier rows (|k| up to about 40) inside the +-448 code range
+    "long-context-fp8-decode": Spec("long-context-fp8-decode", "bf16", Hq=64, Hkv=8, D=128,
+                                    BS=32, decode_ctx=("fixed", [40960] * 8),
+                                    k_outlier=(0.01, 8.0), kv_dtype="fp8", k_scale=1 / 8,
+                                    v_scale=1 / 64),
 }
 
 FP8_SMALL_CONFIGS = {
@@ -380,6 +386,10 @@ FP8_SMALL_CONFIGS = {
     "prefix-shared-fp8-decode": Spec("prefix-shared-fp8-decode-small", "bf16", Hq=16, Hkv=4,
                                      D=64, BS=16, shared=(2, 3, 64, 1, 600),
                                      kv_dtype="fp8", k_scale=0.02, v_scale=0.015),
+    "long-context-fp8-decode": Spec("long-context-fp8-decode-small", "bf16", Hq=64, Hkv=8,
+                                    D=128, BS=32, decode_ctx=("fixed", [1100, 1537]),
+                                    k_outlier=(0.01, 8.0), kv_dtype="fp8", k_scale=1 / 8,
+                                    v_scale=1 / 64),
 }
 
 ALL_CONFIGS = {**CONFIGS, **FP8_CONFIGS}
