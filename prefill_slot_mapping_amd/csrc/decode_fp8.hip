@@ -334,15 +334,6 @@ bool decode_fp8_supported(int head_dim, int group) {
 
 // Instances (keys per tile, waves-per-SIMD register budget, ring depth), measured on the
 // batched 64-sequence step (groups of 4) and 32-sequence steps with groups of 1 and 2.
-#ifndef PKV_F8G8_HT
-#define PKV_F8G8_HT 16
-#endif
-#ifndef PKV_F8G8_W
-#define PKV_F8G8_W 2
-#endif
-#ifndef PKV_F8G8_NB
-#define PKV_F8G8_NB 2
-#endif
 template <int D>
 static hipError_t launch_fp8_d(const DecodeArgs& a, uint32_t grid, int group,
                                hipStream_t stream) {
@@ -350,7 +341,6 @@ static hipError_t launch_fp8_d(const DecodeArgs& a, uint32_t grid, int group,
     case 1: hipLaunchKernelGGL((decode_fp8_kernel<D, 1, 32, 3, 2>), dim3(grid), dim3(256), 0, stream, a); break;
     case 2: hipLaunchKernelGGL((decode_fp8_kernel<D, 2, 32, 3, 2>), dim3(grid), dim3(256), 0, stream, a); break;
     case 4: hipLaunchKernelGGL((decode_fp8_kernel<D, 4, 16, 4, 3>), dim3(grid), dim3(256), 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((decode_fp8_kernel<D, 8, PKV_F8G8_HT, PKV_F8G8_W, PKV_F8G8_NB>), dim3(grid), dim3(256), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -362,6 +352,10 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, int64_t n_items, int head_dim,
   if (grid64 == 0) return hipSuccess;
   if (grid64 > 0x7fffffffLL || a.group != group) return hipErrorInvalidValue;
   const uint32_t grid = static_cast<uint32_t>(grid64);
+  // groups of 8: the MFMA kernel (measured on the long-context E4M3 step: 166 us per decode
+  // pass against 278 us for this kernel with 16-key tiles at two waves per SIMD)
+  if (decode_fp8_mfma_supported(head_dim, group))
+    return launch_decode_fp8_mfma(a, grid, head_dim, group, stream);
   if (head_dim == 64) return launch_fp8_d<64>(a, grid, group, stream);
   if (head_dim == 128) return launch_fp8_d<128>(a, grid, group, stream);
   return hipErrorInvalidValue;

@@ -1,0 +1,403 @@
+// Decode split pass over E4M3 pools on bf16 MFMA (v_mfma_f32_16x16x32_bf16) for gfx950 (MI355X),
+// for groups of 8 query heads per kv head: there the per-key arithmetic of the float32 vector
+// kernel (decode_fp8.hip: G x head_dim multiply-adds for the scores and as many for P.V, plus the
+// code widening) bounds it far below the HBM rate of the half-size rows.
+//
+// Sources of the operation: "P3: native paged-KV continuous-batching sampler", section
+// "Design > paged.py", TritonPagedAttention (a fixed KV split per context length, no atomics),
+// "Finish RL Training Faster: Bitwise-Consistent ..." section 2 (batch independence) and section
+// 4.2 (FP8 KV storage with per-tensor scales, one read path).
+//
+// Work item: (query row, split, kv head), as for the other decode kernels (same lists, same
+// partial slots, same split merge). Four waves; tile i of the split (32 keys aligned at the split
+// start) goes to wave i % 4, which visits its tiles in ascending order. Per tile and wave:
+//   S^T[key][head] = K Q^T   two 16-key blocks x D/32 MFMAs. K codes come from HBM straight into
+//                            registers: lane l takes key l % 16 and the 16-byte pieces at 64 u +
+//                            16 (l / 16) of the row (each load instruction reads 64 contiguous
+//                            bytes of 16 rows) and widens 8 codes exactly to bf16 per k-step;
+//                            k-step st takes d = 64 (st / 2) + 16 (l / 16) + 8 (st % 2) + e, a
+//                            fixed order of the dot product's terms, the same for q and K. The G
+//                            query heads are the B operand's columns (columns past G are zero).
+//                            The K scale is folded into the score scale by the host.
+//   softmax, base 2          lane l holds head l % 16 at keys 4 (l / 16) + r of each block; the
+//                            lazy reference of the other decode kernels (rescale only when a
+//                            score passes it by 8), p = 2^(s scale_log2e - m), l summed per lane.
+//   O^T[d][head] += V^T P^T  D/16 MFMAs per P part; P = hi + lo (hi: p with its low 16 bits
+//                            cleared, a bf16 value; lo: the float32 remainder rounded to bf16),
+//                            about 16 bits of p. V codes are loaded row-coalesced into the wave's
+//                            LDS tile (16-byte chunks XOR-swizzled per row) and read back with one
+//                            ds_read_b64_tr_b8 per 16-wide d block, which hands each lane one d
+//                            column over its 8 keys; widened exactly to bf16 in registers.
+// Keys past the split's context are masked (-inf scores; their V rows zeroed before the LDS
+// write, so no pool value past the context enters a sum). The wave partials are merged in wave
+// order exactly as in the vector decode kernels, the V scale applied once to the merged
+// numerator. Every operation depends only on the row's query, its own keys and the split, never
+// on other rows of the batch.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "device_common.h"
+#include "kernels.h"
+#include "lane_ops.h"
+
+namespace pkv {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2_t lds_i32x2_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+
+constexpr int kMfmaTileKeys = 32;
+
+// E4M3 V tile: 16-byte chunk swizzle of row r (CPR chunks a row). The transposed read of a d
+// block takes 8 rows {4q .. 4q + 3, 16 + 4q .. 16 + 4q + 3} (q = lane quarter), both halves of
+// their chunk; rows of one parity share a bank half, so their chunks must differ - over the
+// rows of two neighbouring quarters too (for D = 128: bits 1, 4 and 2 of r; for D = 64, whose
+// rows cover a quarter of the banks: bits 2 and 4).
+template <int CPR>
+__device__ __forceinline__ int vswz8(int r) {
+  if constexpr (CPR == 8) return ((r >> 1) & 1) | (((r >> 4) & 1) << 1) | (((r >> 2) & 1) << 2);
+  else return ((r >> 2) & 1) | (((r >> 4) & 1) << 1);
+}
+
+// two E4M3 codes (bytes 0-1, or 2-3 with hi) of w -> a bfloat16 pair, exactly
+__device__ __forceinline__ uint32_t e4m3x2_bf16x2(uint32_t w, bool hi) {
+  return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                                         : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+}
+
+// eight E4M3 codes (w0 bytes 0-3, w1 bytes 0-3) -> eight bfloat16 values, exactly
+__device__ __forceinline__ uint4 e4m3x8_bf16x8(uint32_t w0, uint32_t w1) {
+  return make_uint4(e4m3x2_bf16x2(w0, false), e4m3x2_bf16x2(w0, true),
+                    e4m3x2_bf16x2(w1, false), e4m3x2_bf16x2(w1, true));
+}
+
+}  // namespace
+
+template <int D, int G, int W>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(W, W)))
+decode_fp8_mfma_kernel(DecodeArgs a) {
+  constexpr int TK = kMfmaTileKeys;
+  constexpr int RB = D;                   // bytes of a pool row (one key, one kv head)
+  constexpr int KS = D / 32;              // k-steps of S^T per 16-key block
+  constexpr int KU4 = D / 64;             // 16-byte K loads per lane per 16-key block
+  constexpr int CPRV = RB / 16;           // 16-byte chunks of a pool row
+  constexpr int RPI = 64 / CPRV;          // rows per V load instruction
+  constexpr int VU4 = TK / RPI;           // V load instructions per tile
+  constexpr int RS = RB;                  // LDS row stride of the V tile (bytes)
+  constexpr int DB = D / 16;              // 16-wide d blocks of O^T
+  constexpr float kRescaleLog2 = 8.f;
+  static_assert(G >= 1 && G <= 16 && KU4 >= 1 && VU4 >= 1 && TK % RPI == 0, "shape");
+
+  constexpr int kVBytes = kDecodeWaves * TK * RS;
+  constexpr int MD = D + 4;                // merge row stride (floats): heads on distinct banks
+  constexpr int kMergeBytes = kDecodeWaves * G * (MD + 2) * 4;
+  __shared__ __align__(16) char s_v[kVBytes > kMergeBytes ? kVBytes : kMergeBytes];
+  __shared__ uint32_t s_slot[kMaxDecodeSplit];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int quarter = lane >> 4;   // S^T / O^T rows 4 quarter .. + 3; K d range; P keys
+  const int col = lane & 15;       // S^T / O^T column: query head col of the group (< G)
+  // Items in grid order: the host lists them longest first and the hardware deals consecutive
+  // workgroups to the 8 XCDs in turn, so every XCD gets its share of full and short splits.
+  const int f = blockIdx.x;
+  const int item_idx = f / a.hkv;
+  const int g = f - item_idx * a.hkv;
+  const int hq0 = g * G;
+  const DecodeItem it = a.items[item_idx];
+
+  const int t0 = it.split * a.kv_split;
+  const int t1 = min(it.n_keys, t0 + a.kv_split);
+  const int nk = t1 - t0;
+  const int nk_pad = (nk + TK - 1) / TK * TK;
+  const int32_t* bt = a.block_tables + static_cast<int64_t>(it.seq) * a.max_blocks;
+  // slot of each key of the split (keys past the context: the last key's slot); an out-of-pool
+  // block id marks the row bad and reads slot 0
+  bool bad = false;
+  for (int k = tid; k < nk_pad; k += 256) {
+    const int pos = t0 + min(k, nk - 1);
+    int j, off;
+    if (a.bs_log2 >= 0) {
+      j = pos >> a.bs_log2;
+      off = pos & (a.block_size - 1);
+    } else {
+      j = pos / a.block_size;
+      off = pos - j * a.block_size;
+    }
+    const int b = bt[j];
+    const bool ok = static_cast<unsigned>(b) < static_cast<unsigned>(a.num_blocks);
+    bad |= !ok;
+    s_slot[k] = ok ? static_cast<uint32_t>(b * a.block_size + off) : 0u;
+  }
+
+  // B operand of S^T: q[head col][the 8 d of k-step st in this lane's quarter], zero for
+  // columns past G
+  bf16x8_t qf[KS];
+  {
+    const bool hv = col < G;
+    const uint4* qs = reinterpret_cast<const uint4*>(
+        static_cast<const char*>(a.q) +
+        (static_cast<int64_t>(it.row) * a.hq + hq0 + (hv ? col : 0)) * (D * 2));
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+      const int d0 = 64 * (st / 2) + 16 * quarter + 8 * (st % 2);
+      qf[st] = __builtin_bit_cast(bf16x8_t, hv ? qs[d0 / 8] : make_uint4(0u, 0u, 0u, 0u));
+    }
+  }
+  __syncthreads();
+
+  const uint64_t slot_bytes = static_cast<uint64_t>(a.hkv) * RB;
+  const char* kbase = static_cast<const char*>(a.k_cache) + g * RB + quarter * 16;
+  const int vrow = lane / CPRV;     // row of a V load instruction
+  const int vchunk = lane % CPRV;   // 16-byte chunk of that row
+  const char* vbase = static_cast<const char*>(a.v_cache) + g * RB + vchunk * 16;
+  // blocks of 16 keys or more (a power of two): the 16 keys of a tile half are consecutive
+  // slots of one block (tiles start at multiples of 32 keys)
+  const bool halves_in_block = a.bs_log2 >= 4;
+  const int last16 = (nk - 1) & ~15;
+
+  char* sv = s_v + wave * TK * RS;
+  lds_char_t* sv_lds = (lds_char_t*)(sv);
+  // transposed-read address of this lane: row 4 quarter + k (k = col >> 1 < 4) or
+  // 16 + 4 quarter + k - 4, the half col & 1 of chunk db (swizzled)
+  const int k8 = col >> 1;
+  const int tr8_row = k8 < 4 ? 4 * quarter + k8 : 16 + 4 * quarter + k8 - 4;
+  const int tr8_off = tr8_row * RS + 8 * (col & 1);
+  const int tr8_sw = vswz8<CPRV>(tr8_row);
+
+  float m_ref = -INFINITY;
+  float l_run = 0.f;
+  f32x4_t acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const float sl2 = a.scale_log2e;
+
+  // slots of the first keys of the tile's two halves (blocks of 16 keys or more)
+  auto half_bases = [&](int ts, uint32_t& base0, uint32_t& base1) {
+    base0 = __builtin_amdgcn_readfirstlane(s_slot[ts]);
+    base1 = __builtin_amdgcn_readfirstlane(s_slot[min(ts + 16, last16)]);
+  };
+  // slots first (one uniform branch per tile, the LDS reads of the general path issued
+  // together), then the loads
+  auto load_k = [&](uint4 (&kr)[2][KU4], int ts) {
+    uint32_t sl[2];
+    if (halves_in_block) {
+      uint32_t base0, base1;
+      half_bases(ts, base0, base1);
+      sl[0] = base0 + col;
+      sl[1] = base1 + col;
+    } else {
+      sl[0] = s_slot[ts + col];
+      sl[1] = s_slot[ts + 16 + col];
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const uint4* p = reinterpret_cast<const uint4*>(kbase + sl[kb] * slot_bytes);
+#pragma unroll
+      for (int u = 0; u < KU4; ++u) kr[kb][u] = load_nt(p + 4 * u);
+    }
+  };
+  auto load_v = [&](uint4 (&vr)[VU4], int ts) {
+    uint32_t sl[VU4];
+    if (halves_in_block) {
+      uint32_t base0, base1;
+      half_bases(ts, base0, base1);
+#pragma unroll
+      for (int u = 0; u < VU4; ++u) {
+        const int r = u * RPI + vrow;
+        sl[u] = (r < 16 ? base0 : base1) + (r & 15);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < VU4; ++u) sl[u] = s_slot[ts + u * RPI + vrow];
+    }
+#pragma unroll
+    for (int u = 0; u < VU4; ++u)
+      vr[u] = load_nt(reinterpret_cast<const uint4*>(vbase + sl[u] * slot_bytes));
+  };
+
+  // Tile ts from buffers kr / vr, which are refilled with tile nxt (when refill) once consumed
+  // (after the score MFMAs and the V tile's LDS write), so that tile stays in flight through
+  // the softmax and P.V of this one.
+  auto compute = [&](uint4 (&kr)[2][KU4], uint4 (&vr)[VU4], int ts, bool refill, int nxt) {
+    asm volatile("" ::: "memory");
+    const int n = nk - ts;   // keys of this tile inside the context (>= 1)
+    // ---- S^T = K Q^T, the two 16-key blocks interleaved ----
+    f32x4_t s[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int st = 0; st < KS; ++st)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint4 w = kr[kb][st / 2];
+        const uint4 kf = (st & 1) ? e4m3x8_bf16x8(w.z, w.w) : e4m3x8_bf16x8(w.x, w.y);
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf), qf[st],
+                                                        s[kb], 0, 0, 0);
+      }
+    // ---- V codes into the wave's LDS tile (rows past the context: zero) ----
+#pragma unroll
+    for (int u = 0; u < VU4; ++u) {
+      const int r = u * RPI + vrow;
+      uint4 v = vr[u];
+      if (n < TK && r >= n) v = make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4*>(sv + r * RS + ((vchunk ^ vswz8<CPRV>(r)) * 16)) = v;
+    }
+
+    if (refill) {
+      load_v(vr, nxt);
+      load_k(kr, nxt);
+    }
+
+    // ---- lazy online softmax (base 2) for head col over this lane's 8 keys ----
+    float t[2][4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float x = s[kb][r] * sl2;
+        t[kb][r] = (n < TK && 16 * kb + 4 * quarter + r >= n) ? -INFINITY : x;
+        tmax = fmaxf(tmax, t[kb][r]);
+      }
+    tmax = across16(tmax, MaxOp());
+    tmax = across32(tmax, MaxOp());
+    const float m_cand = fmaxf(m_ref, tmax);
+    const bool need = m_cand > m_ref + kRescaleLog2;
+    if (__any(need)) {
+      // a multiply by exactly 1 (heads that keep their reference) changes nothing
+      const float al = need ? fast_exp2(m_ref - m_cand) : 1.f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[db][r] *= al;
+      l_run *= al;
+      m_ref = need ? m_cand : m_ref;
+    }
+    uint32_t phw[4], plw[4];
+    float ps = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; r += 2) {
+        const float p0 = fast_exp2(t[kb][r] - m_ref);
+        const float p1 = fast_exp2(t[kb][r + 1] - m_ref);
+        ps += p0;
+        ps += p1;
+        const uint32_t b0 = __float_as_uint(p0), b1 = __float_as_uint(p1);
+        phw[2 * kb + r / 2] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+        const float l0 = p0 - __uint_as_float(b0 & 0xffff0000u);
+        const float l1 = p1 - __uint_as_float(b1 & 0xffff0000u);
+        plw[2 * kb + r / 2] =
+            __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{l0, l1}, bf16x2_t));
+      }
+    l_run += ps;
+    const bf16x8_t phi = __builtin_bit_cast(bf16x8_t, phw);
+    const bf16x8_t plo = __builtin_bit_cast(bf16x8_t, plw);
+
+    // ---- O^T += V^T P^T: V^T from one transposed read per d block (keys 4 quarter + 0..3,
+    //      16 + 4 quarter + 0..3 at d = 16 db + col) ----
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const i32x2_t c8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (lds_i32x2_t*)(sv_lds + tr8_off + ((db ^ tr8_sw) * 16)));
+      const bf16x8_t va = __builtin_bit_cast(
+          bf16x8_t, e4m3x8_bf16x8(static_cast<uint32_t>(c8.x), static_cast<uint32_t>(c8.y)));
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, acc[db], 0, 0, 0);
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, acc[db], 0, 0, 0);
+    }
+  };
+
+  // Tiles j = 0 .. n_tiles - 1 of this wave (keys wave TK + j kStep ..), ascending, through one
+  // register buffer: tile j + 1 is loaded as soon as tile j's registers are consumed, inside
+  // the loop unconditionally, so the compiler's wait before each tile covers just that tile (a
+  // load under a condition between a load and its use makes it wait for every load). Measured
+  // on the long-context E4M3 step: two or three buffers at two waves per SIMD, or one buffer at
+  // four (with spills), were slower than one buffer at three.
+  constexpr int kStep = kDecodeWaves * TK;
+  const int n_tiles = nk > wave * TK ? (nk - wave * TK + kStep - 1) / kStep : 0;
+  uint4 kbuf[2][KU4];
+  uint4 vbuf[VU4];
+  if (n_tiles > 0) {
+    load_v(vbuf, wave * TK);
+    load_k(kbuf, wave * TK);
+    for (int j = 0; j + 1 < n_tiles; ++j)
+      compute(kbuf, vbuf, wave * TK + j * kStep, true, wave * TK + (j + 1) * kStep);
+    compute(kbuf, vbuf, wave * TK + (n_tiles - 1) * kStep, false, 0);
+  }
+
+  // l over the four key quarters of head col (the same sum in every lane of the head)
+  l_run = across16(l_run, AddOp());
+  l_run = across32(l_run, AddOp());
+
+  const bool bad_row = __syncthreads_or(bad) != 0;   // also: every wave is done with s_v
+  float* mg_acc = reinterpret_cast<float*>(s_v);          // [4][G][MD]
+  float* mg_m = mg_acc + kDecodeWaves * G * MD;            // [4][G]
+  float* mg_l = mg_m + kDecodeWaves * G;                   // [4][G]
+  if (col < G) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      *reinterpret_cast<f32x4_t*>(mg_acc + (wave * G + col) * MD + 16 * db + 4 * quarter) = acc[db];
+    if (quarter == 0) {
+      mg_m[wave * G + col] = m_ref;
+      mg_l[wave * G + col] = l_run;
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int h = idx / D;
+    const int d = idx - h * D;
+    float M = mg_m[h];
+#pragma unroll
+    for (int w = 1; w < kDecodeWaves; ++w) M = fmaxf(M, mg_m[w * G + h]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) {
+      const float fw = fast_exp2(mg_m[w * G + h] - M);
+      num = fmaf(fw, mg_acc[(w * G + h) * MD + d], num);
+      den = fmaf(fw, mg_l[w * G + h], den);
+    }
+    num *= a.v_scale;
+    const uint32_t nan_bits = 0x7fc00000u;
+    const int hq = hq0 + h;
+    if (it.part < 0) {
+      const float o = num / den;
+      a.out[(static_cast<int64_t>(it.row) * a.hq + hq) * D + d] =
+          __uint_as_float(bad_row ? nan_bits : __float_as_uint(o));
+    } else {
+      const int64_t p = static_cast<int64_t>(it.part + it.split) * a.hq + hq;
+      a.part_acc[p * D + d] = __uint_as_float(bad_row ? nan_bits : __float_as_uint(num));
+      if (d == 0) {
+        a.part_m[p] = M;
+        a.part_l[p] = __uint_as_float(bad_row ? nan_bits : __float_as_uint(den));
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// launcher
+// ---------------------------------------------------------------------------------------
+bool decode_fp8_mfma_supported(int head_dim, int group) {
+  return (head_dim == 64 || head_dim == 128) && group == 8;
+}
+
+hipError_t launch_decode_fp8_mfma(const DecodeArgs& a, uint32_t grid, int head_dim, int group,
+                                  hipStream_t stream) {
+  if (group != 8) return hipErrorInvalidValue;
+  // three waves per SIMD: 155 registers at head_dim 128
+  if (head_dim == 64)
+    hipLaunchKernelGGL((decode_fp8_mfma_kernel<64, 8, 3>), dim3(grid), dim3(256), 0, stream, a);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL((decode_fp8_mfma_kernel<128, 8, 3>), dim3(grid), dim3(256), 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace pkv
