@@ -465,8 +465,8 @@ def _traffic_for(workload):
     try:
         rec = json.load(open(path))
         ent = rec[workload]
-        src_path = ent.get("kernel_source", rec["kernel_source"])
-        sha = ent.get("kernel_sha256", rec["kernel_sha256"])
+        src_path = ent.get("kernel_source") or rec["kernel_source"]
+        sha = ent.get("kernel_sha256") or rec["kernel_sha256"]
         src = open(os.path.join(ROOT, src_path), "rb").read()
         if sha != hashlib.sha256(src).hexdigest():
             return None
