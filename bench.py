@@ -28,6 +28,11 @@ group, against the batched step). The cpu_baseline leg times the oracle on the h
 workload and compares the oracle's rows with sampled GPU rows of every timed workload
 (`parity_vs_oracle`).
 
+Order per workload: build the step (host work, the GPU idle); 64 untimed steps (the first steps
+after the set-up run up to twice as long, steady from about the 50th); the untimed pass that
+brackets every kernel; the W warm-up steps and the K timed steps; the cold-cache pass, the
+protocol and the invariance checks.
+
 Prints ONE JSON line (rank 0, N = 1). `--gpus N` with N > 1 exits: this build runs on one GPU.
 """
 from __future__ import annotations
@@ -42,6 +47,7 @@ import time
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 EVENT_STRIDE = 5                 # timed steps per step whose dominant kernel is bracketed
+SETTLE_STEPS = 64                # untimed steps after a workload's set-up, before any figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
@@ -243,13 +249,35 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
                                       w.scale, out=out, workspace=workspace, kv_split=split,
                                       phase_consistent=phase_consistent)
 
+    # After the set-up (seconds of host work, the GPU idle) the first steps run up to twice as
+    # long and the next few dozen 10-20 % longer (measured on the long-context and mixed steps:
+    # steady from about the 50th step). SETTLE_STEPS untimed steps come first, then the
+    # untimed pass that brackets every kernel, then the W warm-up and the K timed steps, so
+    # that every figure is taken in the steady state whatever the warm-up count.
+    dominant = "decode" if (w.q_lens == 1).any() and not phase_consistent else "prefill"
+    # a decode pass may be two launches (per-row items, group items): both are bracketed
+    dominant_kinds = [dominant, "decode_group"] if dominant == "decode" else [dominant]
+    # long-lived objects (torch, the workload) go to the permanent generation, as serving
+    # loops do after start-up, so a collection inside the loop does not walk all of them; done
+    # here, not between the warm-up and the timed steps, where its tens of milliseconds of host
+    # work would leave the GPU idle again
+    gc.collect()
+    gc.freeze()
+    for _ in range(SETTLE_STEPS):
+        step()
+    kinds = ("write_kv", "prefill", "decode", "merge", "decode_group")
+    pkv.profile_set_kinds(list(kinds))
+    pkv.profile_enable(True)
+    for _ in range(steps):
+        step()
+    kern = {k: pkv.profile_read(k) for k in kinds}
+    dspan = pkv.profile_read_span(["decode", "decode_group"])
+    pkv.profile_enable(False)
+    torch.cuda.synchronize(device)
+
     for _ in range(warmup):
         step()
     torch.cuda.synchronize(device)
-    # long-lived objects (torch, the workload) go to the permanent generation, as serving
-    # loops do after start-up, so a collection inside the loop does not walk all of them
-    gc.collect()
-    gc.freeze()
     gc_pauses = []
 
     def on_gc(phase, info, _t=[0.0]):
@@ -261,11 +289,8 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
     # The dominant kernel's device time is taken inside the timed steps: the library brackets
     # its launch with HIP events on the launch stream in every EVENT_STRIDE-th step (an event
     # record costs the stream a few microseconds, so bracketing every launch of every kernel
-    # would stretch the step it times). Every kernel's time is then taken in a second, untimed
-    # pass of the same steps with all launches bracketed.
-    dominant = "decode" if (w.q_lens == 1).any() and not phase_consistent else "prefill"
-    # a decode pass may be two launches (per-row items, group items): both are bracketed
-    dominant_kinds = [dominant, "decode_group"] if dominant == "decode" else [dominant]
+    # would stretch the step it times). Every kernel's time came from the untimed pass above,
+    # with all launches bracketed.
     gc.callbacks.append(on_gc)
     if kernel_events == "timed":
         pkv.profile_set_kinds([])
@@ -293,16 +318,8 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
         gn = pkv.profile_read("decode_group")[1] if dominant == "decode" else 0
         timed = {"kernel": dominant, "launches_bracketed": tn,
                  "avg_ms": tms / tn if tn else None, "group_launches": gn}
-    kinds = ("write_kv", "prefill", "decode", "merge", "decode_group")
-    pkv.profile_set_kinds(list(kinds))
-    pkv.profile_enable(True)
-    for _ in range(steps):
-        step()
-    kern = {k: pkv.profile_read(k) for k in kinds}
-    dspan = pkv.profile_read_span(["decode", "decode_group"])
-    pkv.profile_enable(False)
-    torch.cuda.synchronize(device)
     assert np.array_equal(slots_np[:w.T], gst.new_slots)
+    ms_step = dt / steps * 1e3
 
     # Cold caches: before each of these steps a 1 GiB scratch write evicts L2 and the 256 MB
     # MALL, so the dominant kernel reads its K/V from HBM; its events give the cold time
@@ -322,7 +339,6 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
         cold = {"kernel": dominant, "launches": cn, "avg_ms": cms / cn if cn else None,
                 "flush_bytes": 1 << 30}
 
-    ms_step = dt / steps * 1e3
     kv = _kv_bytes(w)
     app0 = acc.append_bytes(w.T, s.Hkv, s.D, w.elem_bytes, w.kv_elem_bytes)
     decode_only0 = bool((w.q_lens <= 1).all())

@@ -124,6 +124,11 @@ EDGE = [
     (64, 8, 128, 32, [(17, 1), (4097, 1), (2049, 1), (300, 90)], {"kv_split": 2048}),
     (16, 2, 128, 5, [(7, 1), (129, 1), (1500, 1), (88, 20)]),
     (32, 4, 64, 16, [(2, 1), (513, 1), (1100, 1), (40, 9)]),
+    # groups of 8 on the per-key slot path (block size 1), 64-key blocks with splits of 64 and
+    # 128 keys (waves without tiles; a split that ends inside a tile's second half)
+    (16, 2, 128, 1, [(1, 1), (33, 1), (300, 1), (50, 7)]),
+    (16, 2, 128, 64, [(64, 1), (65, 1), (1000, 1), (200, 3)], {"kv_split": 64}),
+    (16, 2, 64, 64, [(112, 1), (129, 1), (1000, 1), (200, 3)], {"kv_split": 128}),
 ]
 
 
@@ -158,9 +163,12 @@ def test_fp8_alone_equals_batched_bitwise_and_run_to_run():
         assert np.array_equal(gst.attention().cpu().numpy(), batched)
 
 
-def test_fp8_out_of_range_block_id_gives_nan_not_a_fault():
-    w = make_workload(explicit_spec("badblock-fp8", "bf16", 8, 2, 128, 16, [(40, 1), (40, 1)],
-                                    kv_dtype="fp8", k_scale=0.05, v_scale=0.05))
+@pytest.mark.parametrize("hq,hkv,bs", [(8, 2, 16), (16, 2, 16), (16, 2, 5), (16, 2, 32)],
+                         ids=["G4-BS16", "G8-BS16", "G8-BS5", "G8-BS32"])
+def test_fp8_out_of_range_block_id_gives_nan_not_a_fault(hq, hkv, bs):
+    w = make_workload(explicit_spec(f"badblock-fp8-{hq}-{bs}", "bf16", hq, hkv, 128, bs,
+                                    [(40, 1), (40, 1)], kv_dtype="fp8", k_scale=0.05,
+                                    v_scale=0.05))
     gst = _harness()(w, device=DEV)
     good = gst.attention().cpu().numpy().copy()
     t = gst.block_tables.copy()
