@@ -22,8 +22,8 @@ prefix-shared group decode step (16 groups x 8 samples sharing a 2048-token prom
 the same way; decode-only
 steps carry a `roofline` object for their decode kernel (the prefix-shared step also on unique
 bytes). Each workload also gets the flushed-cache protocol (median, p10 and p90 of HIP-event
-step times over `--protocol-reps` reps, each after a 2 GiB scratch write that evicts L2 and the
-MALL) and bitwise invariance verdicts (sampled sequences alone, and for shared prompts each
+step times over `--protocol-reps` reps, each after a 2 GiB scratch read that evicts L2 and the
+MALL without leaving dirty lines behind) and bitwise invariance verdicts (sampled sequences alone, and for shared prompts each
 group, against the batched step). The cpu_baseline leg times the oracle on the headline
 workload and compares the oracle's rows with sampled GPU rows of every timed workload
 (`parity_vs_oracle`).
@@ -64,7 +64,7 @@ def _parse():
                     help="comma-separated workloads timed the same way, reported under 'extra'")
     ap.add_argument("--protocol-reps", type=int, default=50,
                     help="reps of the flushed-cache protocol per workload (median, p10, p90 of "
-                         "HIP-event step times, a 2 GiB scratch write before each rep); 0: off")
+                         "HIP-event step times, a 2 GiB scratch read before each rep); 0: off")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -176,17 +176,34 @@ def _invariance(w, gst, out, split, phase_consistent):
     return verdict
 
 
+def _clean_scratch(n_floats, device):
+    """A scratch buffer for cache eviction, written once and then read once, so that none of
+    its lines is still dirty in L2 or the MALL when the reads that evict start."""
+    import torch
+    buf = torch.ones(n_floats, dtype=torch.float32, device=device)
+    buf.sum()
+    torch.cuda.synchronize(device)
+    return buf
+
+
+def _evict(buf):
+    """Read the whole scratch buffer (a reduction): evicts L2 and the 256 MB MALL. A write
+    would leave its lines dirty there, and their write-back would then compete with the step
+    that follows for HBM bandwidth."""
+    buf.sum()
+
+
 def _protocol(step, reps, device, value_of):
-    """Flushed-cache timing: before each rep a 2 GiB scratch write evicts L2 and the 256 MB
+    """Flushed-cache timing: before each rep a 2 GiB scratch read evicts L2 and the 256 MB
     MALL (and keeps the GPU busy while the host enqueues the step); HIP events on the stream
     bracket the step. Returns the median and p10 / p90 of the reps."""
     import numpy as np
     import torch
-    flush = torch.empty(1 << 29, dtype=torch.float32, device=device)
+    flush = _clean_scratch(1 << 29, device)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(reps)]
     for i in range(reps):
-        flush.fill_(float(i))
+        _evict(flush)
         evs[i][0].record()
         step()
         evs[i][1].record()
@@ -321,16 +338,17 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
     assert np.array_equal(slots_np[:w.T], gst.new_slots)
     ms_step = dt / steps * 1e3
 
-    # Cold caches: before each of these steps a 1 GiB scratch write evicts L2 and the 256 MB
-    # MALL, so the dominant kernel reads its K/V from HBM; its events give the cold time
-    # (untimed pass, not part of ms_per_step).
+    # Cold caches: before each of these steps a 1 GiB scratch read evicts L2 and the 256 MB
+    # MALL (a read leaves no dirty lines whose write-back would compete with the step), so the
+    # dominant kernel reads its K/V from HBM; its events give the cold time (untimed pass, not
+    # part of ms_per_step).
     cold = {}
     if cold_steps > 0:
-        scratch = torch.empty(1 << 28, dtype=torch.float32, device=device)
+        scratch = _clean_scratch(1 << 28, device)
         pkv.profile_set_kinds(dominant_kinds)
         pkv.profile_enable(True)
         for i in range(cold_steps):
-            scratch.fill_(float(i))
+            _evict(scratch)
             step()
         cms, cn = pkv.profile_read_span(dominant_kinds)
         pkv.profile_enable(False)
