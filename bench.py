@@ -22,8 +22,8 @@ prefix-shared group decode step (16 groups x 8 samples sharing a 2048-token prom
 the same way; decode-only
 steps carry a `roofline` object for their decode kernel (the prefix-shared step also on unique
 bytes). Each workload also gets the flushed-cache protocol (median, p10 and p90 of HIP-event
-step times over `--protocol-reps` reps, each after a 2 GiB scratch read that evicts L2 and the
-MALL without leaving dirty lines behind) and bitwise invariance verdicts (sampled sequences alone, and for shared prompts each
+step times over `--protocol-reps` reps, each after a 2 GiB scratch write that evicts L2 and the
+MALL) and bitwise invariance verdicts (sampled sequences alone, and for shared prompts each
 group, against the batched step). The cpu_baseline leg times the oracle on the headline
 workload and compares the oracle's rows with sampled GPU rows of every timed workload
 (`parity_vs_oracle`).
@@ -64,7 +64,7 @@ def _parse():
                     help="comma-separated workloads timed the same way, reported under 'extra'")
     ap.add_argument("--protocol-reps", type=int, default=50,
                     help="reps of the flushed-cache protocol per workload (median, p10, p90 of "
-                         "HIP-event step times, a 2 GiB scratch read before each rep); 0: off")
+                         "HIP-event step times, a 2 GiB scratch write before each rep); 0: off")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -194,16 +194,16 @@ def _evict(buf):
 
 
 def _protocol(step, reps, device, value_of):
-    """Flushed-cache timing: before each rep a 2 GiB scratch read evicts L2 and the 256 MB
+    """Flushed-cache timing: before each rep a 2 GiB scratch write evicts L2 and the 256 MB
     MALL (and keeps the GPU busy while the host enqueues the step); HIP events on the stream
     bracket the step. Returns the median and p10 / p90 of the reps."""
     import numpy as np
     import torch
-    flush = _clean_scratch(1 << 29, device)
+    flush = torch.empty(1 << 29, dtype=torch.float32, device=device)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(reps)]
     for i in range(reps):
-        _evict(flush)
+        flush.fill_(float(i))
         evs[i][0].record()
         step()
         evs[i][1].record()
@@ -339,23 +339,32 @@ def time_workload(name, steps, warmup, device="cuda:0", phase_consistent=False,
     ms_step = dt / steps * 1e3
 
     # Cold caches: before each of these steps a 1 GiB scratch read evicts L2 and the 256 MB
-    # MALL (a read leaves no dirty lines whose write-back would compete with the step), so the
-    # dominant kernel reads its K/V from HBM; its events give the cold time (untimed pass, not
-    # part of ms_per_step).
+    # MALL, so the dominant kernel reads its K/V from HBM; its events give the cold time
+    # (untimed passes, not part of ms_per_step). A read leaves no dirty lines behind; after a
+    # scratch write (also measured, the protocol's flush), up to 256 MB of dirty MALL lines are
+    # written back while the step reads, which the step's own traffic does not include.
     cold = {}
     if cold_steps > 0:
-        scratch = _clean_scratch(1 << 28, device)
-        pkv.profile_set_kinds(dominant_kinds)
-        pkv.profile_enable(True)
-        for i in range(cold_steps):
-            _evict(scratch)
-            step()
-        cms, cn = pkv.profile_read_span(dominant_kinds)
-        pkv.profile_enable(False)
-        torch.cuda.synchronize(device)
-        del scratch
-        cold = {"kernel": dominant, "launches": cn, "avg_ms": cms / cn if cn else None,
-                "flush_bytes": 1 << 30}
+        def cold_pass(evict_read):
+            scratch = (_clean_scratch(1 << 28, device) if evict_read else
+                       torch.empty(1 << 28, dtype=torch.float32, device=device))
+            pkv.profile_set_kinds(dominant_kinds)
+            pkv.profile_enable(True)
+            for i in range(cold_steps):
+                if evict_read:
+                    _evict(scratch)
+                else:
+                    scratch.fill_(float(i))
+                step()
+            cms, cn = pkv.profile_read_span(dominant_kinds)
+            pkv.profile_enable(False)
+            torch.cuda.synchronize(device)
+            del scratch
+            return cms / cn if cn else None, cn
+        ms_r, n_r = cold_pass(True)
+        ms_w, _ = cold_pass(False)
+        cold = {"kernel": dominant, "launches": n_r, "avg_ms": ms_r, "flush_bytes": 1 << 30,
+                "evict": "scratch read", "avg_ms_after_scratch_write": ms_w}
 
     kv = _kv_bytes(w)
     app0 = acc.append_bytes(w.T, s.Hkv, s.D, w.elem_bytes, w.kv_elem_bytes)
@@ -517,14 +526,18 @@ def _decode_roofline(res, name, kernel):
     achieved = res["decode_kv_bytes"] / (ms * 1e-3) / 1e9 if ms else None
     cold = res.get("cold_cache_kernel") or {}
     cms = cold.get("avg_ms") if cold.get("kernel") == "decode" else None
+    wms = cold.get("avg_ms_after_scratch_write") if cold.get("kernel") == "decode" else None
+    kvb = res["decode_kv_bytes"]
     r = {"bound": "hbm", "kernel": kernel, "achieved": achieved, "peak": HBM_PEAK_GBS,
          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS if achieved else None,
-         "traffic": _traffic_for(name), "bytes_per_launch": res["decode_kv_bytes"],
+         "traffic": _traffic_for(name), "bytes_per_launch": kvb,
          "avg_launch_ms": ms,
-         "cold_cache": {"avg_launch_ms": cms,
-                        "achieved": res["decode_kv_bytes"] / (cms * 1e-3) / 1e9 if cms else None,
-                        "frac": res["decode_kv_bytes"] / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS
-                        if cms else None}}
+         "cold_cache": {"evict": "1 GiB scratch read", "avg_launch_ms": cms,
+                        "achieved": kvb / (cms * 1e-3) / 1e9 if cms else None,
+                        "frac": kvb / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS if cms else None,
+                        "after_scratch_write": {
+                            "avg_launch_ms": wms,
+                            "frac": kvb / (wms * 1e-3) / 1e9 / HBM_PEAK_GBS if wms else None}}}
     uq = res["unique_kv_bytes"]
     if uq != res["decode_kv_bytes"] and ms:
         # blocks shared by several sequences: `achieved` counts every sequence's reads
