@@ -551,10 +551,9 @@ def _decode_roofline(res, name, kernel):
 
 def _decode_kernel_name(w):
     """The decode kernel a decode-only workload runs on (its group and pool type)."""
-    if w.kv_fp8:
-        return "decode_fp8_mfma_kernel" if w.spec.Hq // w.spec.Hkv == 8 else "decode_fp8_kernel"
-    return "decode_pair_kernel" if (w.spec.Hq // w.spec.Hkv == 8 and w.spec.D == 128
-                                    and w.spec.dtype == "bf16") else "decode_split_kernel"
+    if w.spec.Hq // w.spec.Hkv == 8 and (w.kv_fp8 or w.spec.dtype == "bf16"):
+        return "decode_mfma_kernel"
+    return "decode_fp8_kernel" if w.kv_fp8 else "decode_split_kernel"
 
 
 def _clocks():

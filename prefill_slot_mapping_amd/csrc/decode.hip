@@ -16,7 +16,8 @@
 // is float32 throughout; bfloat16 products are formed exactly by v_dot2_f32_bf16 and summed
 // over the head dimension in ascending 16-byte chunks, one part of the dimension per lane of a
 // key's lane group, the parts then added in a fixed butterfly; probabilities stay float32 for
-// P.V.
+// P.V. bf16 groups of 8 run on the MFMA kernel of decode_mfma.hip instead, whose contract is
+// fixed per instance in the same way.
 //
 // This file is compiled with -fno-honor-nans (lets maxima fuse with their lane permutes): no
 // floating-point operation here sees a NaN; a row whose block table is bad is written as a NaN
@@ -443,273 +444,6 @@ decode_split_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Decode split pass for a group of 8 query heads (bf16): paired waves.
-//
-// Workgroup = 4 waves = one (query row, split, kv head) item, organised as two wave pairs.
-// Tiles of HT keys aligned at the split start go to pair (tile % 2). In a pair, one wave
-// loads the tile's K rows and the other its V rows (each double-buffered in registers); both
-// stage them in an LDS buffer the pair shares (two stages, one workgroup barrier per tile),
-// and each wave then runs the score, softmax and P.V stages of the kernel above for 4 of the
-// 8 query heads over the whole tile (wave half h serves heads 4h .. 4h + 3, with the lazy
-// reference rule). Per wave this is the work of a group of 4 with half the load registers,
-// so W waves share a SIMD. Each head's two pair partials are merged in pair order.
-// ---------------------------------------------------------------------------------------
-template <int D, int HT, int W>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(W, W)))
-decode_pair_kernel(DecodeArgs a) {
-  constexpr int G = 8;                       // query heads per item
-  constexpr int GW = 4;                      // query heads per wave
-  constexpr int ROWB = D * 2;                // bytes of one bf16 head row
-  constexpr int LPT = ROWB / 16;             // lanes per key row
-  constexpr int TPI = 64 / LPT;              // keys per load instruction (key groups)
-  constexpr int NI = HT / TPI;               // load instructions per tile
-  constexpr int EPL = 8;                     // bf16 elements per 16-byte chunk
-  constexpr int SPL = 64 / HT;               // score stage: lanes per key
-  constexpr int CPH = LPT / SPL;             // score stage: chunks per lane
-  constexpr int GO = GW / SPL;               // heads whose p a lane forms
-  constexpr int kStageU4 = HT * LPT;         // one tensor's tile, in uint4
-  constexpr float kRescaleLog2 = 8.f;
-  static_assert(LPT >= 8 && LPT <= 32 && HT % TPI == 0 && NI % 2 == 0 && GO >= 1, "shape");
-  static_assert(HT == 16 || HT == 32, "tile");
-  static_assert(2 * 2 * 2 * kStageU4 * 16 >= kDecodeWaves * GW * (D + 2) * 4, "merge scratch");
-
-  __shared__ uint4 s_stage[2][2][2][kStageU4];        // [stage][pair][K, V]
-  __shared__ __align__(16) float s_p[kDecodeWaves][HT * GW];
-  __shared__ uint4 s_q[G * LPT];
-  __shared__ __align__(16) uint32_t s_slot[kMaxDecodeSplit];
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int pair = wave >> 1;
-  const int half = wave & 1;                 // 0: loads K, 1: loads V; heads half*4 .. +3
-  const int f = blockIdx.x;                  // grid order, as decode_split_kernel
-  const int item_idx = f / a.hkv;
-  const int g = f - item_idx * a.hkv;
-  const int hq0 = g * G;
-  const DecodeItem it = a.items[item_idx];
-
-  const int t0 = it.split * a.kv_split;
-  const int t1 = min(it.n_keys, t0 + a.kv_split);
-  const int nk = t1 - t0;
-  const int n_tiles = (nk + HT - 1) / HT;
-  const int nk_pad = n_tiles * HT;
-  const int32_t* bt = a.block_tables + static_cast<int64_t>(it.seq) * a.max_blocks;
-  bool bad = false;
-  for (int k = tid; k < nk_pad; k += 256) {
-    const int pos = t0 + min(k, nk - 1);
-    int j, off;
-    if (a.bs_log2 >= 0) {
-      j = pos >> a.bs_log2;
-      off = pos & (a.block_size - 1);
-    } else {
-      j = pos / a.block_size;
-      off = pos - j * a.block_size;
-    }
-    const int b = bt[j];
-    const bool ok = static_cast<unsigned>(b) < static_cast<unsigned>(a.num_blocks);
-    bad |= !ok;
-    const int w = k % HT;
-    s_slot[(k - w) + (w % TPI) * NI + w / TPI] = ok ? static_cast<uint32_t>(b * a.block_size + off) : 0u;
-  }
-  const uint4* qsrc = reinterpret_cast<const uint4*>(
-      static_cast<const char*>(a.q) + (static_cast<int64_t>(it.row) * a.hq + hq0) * ROWB);
-  for (int c = tid; c < G * LPT; c += 256) s_q[c] = qsrc[c];
-  __syncthreads();
-
-  const int grp = lane / LPT;
-  const int cl = lane & (LPT - 1);
-  const int kk = lane / SPL;
-  const int hf = lane % SPL;
-  const uint32_t slot_bytes = static_cast<uint32_t>(a.hkv) * ROWB;
-  const char* base = static_cast<const char*>(half == 0 ? a.k_cache : a.v_cache) + g * ROWB +
-                     cl * 16;
-  float* sp = s_p[wave];
-  const uint4* sq = s_q + half * GW * LPT;
-
-  float m[GW], lo[GO], acc[GW][EPL];
-#pragma unroll
-  for (int h = 0; h < GW; ++h) {
-    m[h] = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
-  }
-#pragma unroll
-  for (int j = 0; j < GO; ++j) lo[j] = 0.f;
-
-  auto load = [&](uint4 (&r)[NI], int hs) {
-    const uint32_t* sl = s_slot + (hs - t0) + grp * NI;
-    constexpr int SV = NI % 4 == 0 ? 4 : 2;
-#pragma unroll
-    for (int i4 = 0; i4 < NI; i4 += SV) {
-      uint32_t ss[4];
-      if constexpr (SV == 4) {
-        const uint4 s4 = *reinterpret_cast<const uint4*>(sl + i4);
-        ss[0] = s4.x; ss[1] = s4.y; ss[2] = s4.z; ss[3] = s4.w;
-      } else {
-        const uint2 s2 = *reinterpret_cast<const uint2*>(sl + i4);
-        ss[0] = s2.x; ss[1] = s2.y;
-      }
-#pragma unroll
-      for (int u = 0; u < SV; ++u)
-        r[i4 + u] = load_nt(reinterpret_cast<const uint4*>(base + static_cast<uint64_t>(ss[u]) * slot_bytes));
-    }
-  };
-
-  // K rows are staged XOR-swizzled (score stage reads a key's chunks), V rows in load order
-  auto stage_write = [&](const uint4 (&r)[NI], uint4* st) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int tok = i * TPI + grp;
-      st[tok * LPT + (half == 0 ? (cl ^ (tok & (LPT - 1))) : cl)] = r[i];
-    }
-  };
-
-  auto compute = [&](const uint4* sk, const uint4* sv, int hs) {
-    asm volatile("" ::: "memory");
-    const int n = min(HT, t1 - hs);
-    float s[GW];
-#pragma unroll
-    for (int h = 0; h < GW; ++h) s[h] = 0.f;
-#pragma unroll
-    for (int u = 0; u < CPH; ++u) {
-      const int c = hf * CPH + u;
-      const uint4 kc = sk[kk * LPT + (c ^ (kk & (LPT - 1)))];
-#pragma unroll
-      for (int h = 0; h < GW; ++h) {
-        const uint4 qc = sq[h * LPT + c];
-        s[h] = dot2_bf16(qc.x, kc.x, s[h]);
-        s[h] = dot2_bf16(qc.y, kc.y, s[h]);
-        s[h] = dot2_bf16(qc.z, kc.z, s[h]);
-        s[h] = dot2_bf16(qc.w, kc.w, s[h]);
-      }
-    }
-    const bool valid = kk < n;
-    bool over = false;
-#pragma unroll
-    for (int h = 0; h < GW; ++h) {
-      s[h] += dpp_xor1(s[h]);
-      if constexpr (SPL == 4) s[h] += dpp_xor2(s[h]);
-      s[h] = valid ? s[h] * a.scale_log2e : -INFINITY;
-      over |= s[h] > m[h] + kRescaleLog2;
-    }
-    if (__any(over)) {
-#pragma unroll
-      for (int h = 0; h < GW; ++h) {
-        const float mt = max_over_groups<SPL>(s[h]);
-        const float mn = mt > m[h] + kRescaleLog2 ? mt : m[h];
-        const float al = fast_exp2(m[h] - mn);
-        m[h] = mn;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] *= al;
-        lo[h / SPL] = hf == h % SPL ? lo[h / SPL] * al : lo[h / SPL];
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < GO; ++j) {
-      float sv_ = s[j * SPL], mv = m[j * SPL];
-#pragma unroll
-      for (int r = 1; r < SPL; ++r) {
-        sv_ = hf == r ? opaque(s[j * SPL + r]) : sv_;
-        mv = hf == r ? opaque(m[j * SPL + r]) : mv;
-      }
-      const float p = fast_exp2(sv_ - mv);
-      lo[j] += p;
-      sp[kk * GW + j * SPL + hf] = p;
-    }
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int tok = i * TPI + grp;
-      const float4 pq = *reinterpret_cast<const float4*>(sp + tok * GW);
-      const float pp[GW] = {pq.x, pq.y, pq.z, pq.w};
-      const uint4 vr = sv[tok * LPT + cl];
-      float vf[EPL];
-      vf[0] = bf16_lo(vr.x); vf[1] = bf16_hi(vr.x);
-      vf[2] = bf16_lo(vr.y); vf[3] = bf16_hi(vr.y);
-      vf[4] = bf16_lo(vr.z); vf[5] = bf16_hi(vr.z);
-      vf[6] = bf16_lo(vr.w); vf[7] = bf16_hi(vr.w);
-#pragma unroll
-      for (int h = 0; h < GW; ++h)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pp[h], vf[e], acc[h][e]);
-    }
-  };
-
-  // every wave runs the same number of steps (one barrier each); a pair without a tile in the
-  // last step only takes part in the barrier
-  const int n_steps = (n_tiles + 1) / 2;
-  const int hs0 = t0 + HT * pair;
-  auto step = [&](const uint4 (&cur)[NI], uint4 (&nxt)[NI], int k) {
-    const int hs = hs0 + k * 2 * HT;
-    uint4* st = s_stage[k & 1][pair][0];
-    if (hs < t1) stage_write(cur, s_stage[k & 1][pair][half]);
-    if (hs + 2 * HT < t1) load(nxt, hs + 2 * HT);
-    __syncthreads();
-    if (hs < t1) compute(st, s_stage[k & 1][pair][1], hs);
-  };
-  uint4 ra[NI], rb[NI];
-  if (hs0 < t1) load(ra, hs0);
-  for (int k = 0; k < n_steps; k += 2) {
-    step(ra, rb, k);
-    if (k + 1 < n_steps) step(rb, ra, k + 1);
-  }
-
-#pragma unroll
-  for (int j = 0; j < GO; ++j) lo[j] = sum_same_class<SPL>(lo[j]);
-#pragma unroll
-  for (int h = 0; h < GW; ++h)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] = sum_key_groups<LPT>(acc[h][e]);
-
-  const bool bad_row = __syncthreads_or(bad) != 0;  // also: every wave is done with s_stage
-  float* mg_acc = reinterpret_cast<float*>(&s_stage[0][0][0][0]);  // [4][GW][D]
-  float* mg_m = mg_acc + kDecodeWaves * GW * D;                     // [4][GW]
-  float* mg_l = mg_m + kDecodeWaves * GW;                           // [4][GW]
-  if (lane < LPT) {
-#pragma unroll
-    for (int h = 0; h < GW; ++h)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) mg_acc[(wave * GW + h) * D + lane * EPL + e] = acc[h][e];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int h = 0; h < GW; ++h) mg_m[wave * GW + h] = m[h];
-  }
-  if (lane < SPL) {
-#pragma unroll
-    for (int j = 0; j < GO; ++j) mg_l[wave * GW + j * SPL + lane] = lo[j];
-  }
-  __syncthreads();
-  for (int idx = tid; idx < G * D; idx += 256) {
-    const int h = idx / D;                 // query head within the item
-    const int d = idx - h * D;
-    const int hw = h % GW;
-    const int w0 = h / GW;                 // wave of pair 0 serving h; pair 1's is w0 + 2
-    const float m0 = mg_m[w0 * GW + hw], m1 = mg_m[(w0 + 2) * GW + hw];
-    const float M = fmaxf(m0, m1);
-    const float f0 = fast_exp2(m0 - M), f1 = fast_exp2(m1 - M);
-    float num = f0 * mg_acc[(w0 * GW + hw) * D + d];
-    num = fmaf(f1, mg_acc[((w0 + 2) * GW + hw) * D + d], num);
-    float den = f0 * mg_l[w0 * GW + hw];
-    den = fmaf(f1, mg_l[(w0 + 2) * GW + hw], den);
-    const uint32_t nan_bits = 0x7fc00000u;
-    const int hq = hq0 + h;
-    if (it.part < 0) {
-      const float o = num / den;
-      a.out[(static_cast<int64_t>(it.row) * a.hq + hq) * D + d] =
-          __uint_as_float(bad_row ? nan_bits : __float_as_uint(o));
-    } else {
-      const int64_t p = static_cast<int64_t>(it.part + it.split) * a.hq + hq;
-      a.part_acc[p * D + d] = __uint_as_float(bad_row ? nan_bits : __float_as_uint(num));
-      if (d == 0) {
-        a.part_m[p] = M;
-        a.part_l[p] = __uint_as_float(bad_row ? nan_bits : __float_as_uint(den));
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------------------
 bool decode_supported(int head_dim, int group) {
@@ -720,8 +454,10 @@ bool decode_supported(int head_dim, int group) {
 // Keys per tile and waves per SIMD of each decode_split_kernel instance (measured on the
 // batched, long-context and prefix-shared decode steps): bf16 groups of 4 run 16-key tiles at
 // three waves per SIMD (160 registers at head_dim 128); other bf16 instances run 32-key tiles
-// at two waves (16-key tiles for a group of 8 at head_dim 128, which the paired-wave kernel
-// serves instead); float32 (twice the bytes per row) one wave.
+// at two waves; float32 (twice the bytes per row) one wave. bf16 groups of 8 run on the MFMA
+// kernel (decode_mfma.hip): on the long-context step 245 us per decode pass against 256 us for
+// the paired-wave kernel this file held before (one wave of a pair loading K, the other V,
+// each computing 4 of the 8 heads), and 161 against 221 us for this kernel at head_dim 64.
 template <int D, bool BF, int G>
 constexpr int tile_keys() {
   return (BF && D == 128 && G >= 4) ? 16 : (BF && D == 64 && G == 4) ? 16 : 32;
@@ -731,26 +467,25 @@ constexpr int waves_per_simd() {
   return !BF ? 1 : (G == 4 ? 3 : 2);
 }
 template <int D, bool BF, int G>
-static void launch_one(const DecodeArgs& a, uint32_t grid, hipStream_t stream) {
-  // bf16 groups of 8 at head_dim 128: paired waves, 16-key tiles, three waves per SIMD (151
-  // registers; 32-key tiles or a third register buffer measured no faster)
-  if constexpr (BF && G == 8 && D == 128)
-    hipLaunchKernelGGL((decode_pair_kernel<D, 16, 3>), dim3(grid), dim3(256), 0, stream, a);
-  else
+static hipError_t launch_one(const DecodeArgs& a, uint32_t grid, hipStream_t stream) {
+  if constexpr (BF && G == 8) {
+    return launch_decode_mfma(a, grid, D, G, false, stream);
+  } else {
     hipLaunchKernelGGL((decode_split_kernel<D, G, BF, tile_keys<D, BF, G>(), waves_per_simd<D, BF, G>()>),
                        dim3(grid), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
 }
 template <int D, bool BF>
 static hipError_t launch_decode_d(const DecodeArgs& a, uint32_t grid, int group,
                                   hipStream_t stream) {
   switch (group) {
-    case 1: launch_one<D, BF, 1>(a, grid, stream); break;
-    case 2: launch_one<D, BF, 2>(a, grid, stream); break;
-    case 4: launch_one<D, BF, 4>(a, grid, stream); break;
-    case 8: launch_one<D, BF, 8>(a, grid, stream); break;
+    case 1: return launch_one<D, BF, 1>(a, grid, stream);
+    case 2: return launch_one<D, BF, 2>(a, grid, stream);
+    case 4: return launch_one<D, BF, 4>(a, grid, stream);
+    case 8: return launch_one<D, BF, 8>(a, grid, stream);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 // Group items: bf16 groups up to 4, the single-row kernel with the state of kGroupR rows at

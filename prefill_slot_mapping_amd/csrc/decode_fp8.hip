@@ -352,10 +352,10 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, int64_t n_items, int head_dim,
   if (grid64 == 0) return hipSuccess;
   if (grid64 > 0x7fffffffLL || a.group != group) return hipErrorInvalidValue;
   const uint32_t grid = static_cast<uint32_t>(grid64);
-  // groups of 8: the MFMA kernel (measured on the long-context E4M3 step: 166 us per decode
+  // groups of 8: the MFMA kernel (measured on the long-context E4M3 step: 143 us per decode
   // pass against 278 us for this kernel with 16-key tiles at two waves per SIMD)
-  if (decode_fp8_mfma_supported(head_dim, group))
-    return launch_decode_fp8_mfma(a, grid, head_dim, group, stream);
+  if (decode_mfma_supported(head_dim, group))
+    return launch_decode_mfma(a, grid, head_dim, group, true, stream);
   if (head_dim == 64) return launch_fp8_d<64>(a, grid, group, stream);
   if (head_dim == 128) return launch_fp8_d<128>(a, grid, group, stream);
   return hipErrorInvalidValue;

@@ -1,7 +1,7 @@
-// Decode split pass over E4M3 pools on bf16 MFMA (v_mfma_f32_16x16x32_bf16) for gfx950 (MI355X),
-// for groups of 8 query heads per kv head: there the per-key arithmetic of the float32 vector
-// kernel (decode_fp8.hip: G x head_dim multiply-adds for the scores and as many for P.V, plus the
-// code widening) bounds it far below the HBM rate of the half-size rows.
+// Decode split pass on bf16 MFMA (v_mfma_f32_16x16x32_bf16) for gfx950 (MI355X), for groups of
+// 8 query heads per kv head, over bf16 pools and over E4M3 pools. There the vector kernels'
+// per-key arithmetic (G x head_dim multiply-adds for the scores and as many for P.V, plus the
+// code widening of E4M3) and their per-lane head layouts bound them below the HBM rate.
 //
 // Sources of the operation: "P3: native paged-KV continuous-batching sampler", section
 // "Design > paged.py", TritonPagedAttention (a fixed KV split per context length, no atomics),
@@ -10,27 +10,31 @@
 //
 // Work item: (query row, split, kv head), as for the other decode kernels (same lists, same
 // partial slots, same split merge). Four waves; tile i of the split (32 keys aligned at the split
-// start) goes to wave i % 4, which visits its tiles in ascending order. Per tile and wave:
-//   S^T[key][head] = K Q^T   two 16-key blocks x D/32 MFMAs. K codes come from HBM straight into
-//                            registers: lane l takes key l % 16 and the 16-byte pieces at 64 u +
-//                            16 (l / 16) of the row (each load instruction reads 64 contiguous
-//                            bytes of 16 rows) and widens 8 codes exactly to bf16 per k-step;
-//                            k-step st takes d = 64 (st / 2) + 16 (l / 16) + 8 (st % 2) + e, a
-//                            fixed order of the dot product's terms, the same for q and K. The G
-//                            query heads are the B operand's columns (columns past G are zero).
-//                            The K scale is folded into the score scale by the host.
+// start) goes to wave i % 4, which visits its tiles in ascending order. A tile's K and V rows are
+// loaded whole, 16 bytes a lane (each load instruction reads complete rows: 8 keys of E4M3 codes
+// at head_dim 128, 4 keys of bf16); reading 64-byte pieces of 16 rows per instruction straight
+// into the operand layout was 15 % slower. Per tile and wave:
+//   S^T[key][head] = K Q^T   two 16-key blocks x D/32 MFMAs. K rows go to the wave's LDS tile
+//                            (16-byte chunks XOR-swizzled per row, so the 16 rows of an operand
+//                            read fall on distinct banks) and come back as the A operand: lane l
+//                            takes key l % 16, k-step st the 8 values at d = 64 (st / 2) +
+//                            16 (l / 16) + 8 (st % 2) + e (E4M3 codes widened exactly to bf16) -
+//                            a fixed order of the dot product's terms, the same for q and K. The
+//                            G query heads are the B operand's columns (columns past G are
+//                            zero). An E4M3 K scale is folded into the score scale by the host.
 //   softmax, base 2          lane l holds head l % 16 at keys 4 (l / 16) + r of each block; the
 //                            lazy reference of the other decode kernels (rescale only when a
 //                            score passes it by 8), p = 2^(s scale_log2e - m), l summed per lane.
 //   O^T[d][head] += V^T P^T  D/16 MFMAs per P part; P = hi + lo (hi: p with its low 16 bits
 //                            cleared, a bf16 value; lo: the float32 remainder rounded to bf16),
-//                            about 16 bits of p. V codes are loaded row-coalesced into the wave's
-//                            LDS tile (16-byte chunks XOR-swizzled per row) and read back with one
-//                            ds_read_b64_tr_b8 per 16-wide d block, which hands each lane one d
-//                            column over its 8 keys; widened exactly to bf16 in registers.
+//                            about 16 bits of p. V rows replace K in the wave's LDS tile once the
+//                            scores are read (16-byte chunks XOR-swizzled per row) and come back
+//                            transposed, each lane one d column over its 8 keys: one
+//                            ds_read_b64_tr_b8 per 16-wide d block for E4M3 codes (widened
+//                            exactly to bf16 in registers), two ds_read_b64_tr_b16 for bf16.
 // Keys past the split's context are masked (-inf scores; their V rows zeroed before the LDS
 // write, so no pool value past the context enters a sum). The wave partials are merged in wave
-// order exactly as in the vector decode kernels, the V scale applied once to the merged
+// order exactly as in the vector decode kernels, an E4M3 V scale applied once to the merged
 // numerator. Every operation depends only on the row's query, its own keys and the split, never
 // on other rows of the batch.
 #include <hip/hip_runtime.h>
@@ -50,6 +54,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2_t lds_i32x2_t;
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 typedef __attribute__((address_space(3))) char lds_char_t;
 
 constexpr int kMfmaTileKeys = 32;
@@ -63,6 +69,25 @@ template <int CPR>
 __device__ __forceinline__ int vswz8(int r) {
   if constexpr (CPR == 8) return ((r >> 1) & 1) | (((r >> 4) & 1) << 1) | (((r >> 2) & 1) << 2);
   else return ((r >> 2) & 1) | (((r >> 4) & 1) << 1);
+}
+
+// bf16 V tile: chunk swizzle of row r (CPR chunks a row). The transposed read of d block db
+// takes chunks 2 db and 2 db + 1 of rows 4q .. 4q + 3 in lane quarter q; over the 8 rows of two
+// neighbouring quarters the chunk pairs must land on distinct banks (XOR with an even value keeps
+// a pair's chunks apart, the low bit separates the two row octets).
+template <int CPR>
+__device__ __forceinline__ int vswz16(int r) {
+  if constexpr (CPR == 16) return ((r & 7) << 1) | ((r >> 3) & 1);
+  else return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+}
+
+// K tile (either element type): chunk swizzle of row r, so that the 16 rows an A-operand read
+// takes (one chunk position each) fall on distinct banks: rows sharing a 256-byte bank span
+// (256 / row bytes of them) get distinct chunk positions.
+template <int CPR>
+__device__ __forceinline__ int kswz(int r) {
+  constexpr int kRowsPerSpan = CPR >= 16 ? 1 : 16 / CPR;
+  return (r / kRowsPerSpan) & (CPR - 1);
 }
 
 // two E4M3 codes (bytes 0-1, or 2-3 with hi) of w -> a bfloat16 pair, exactly
@@ -79,25 +104,23 @@ __device__ __forceinline__ uint4 e4m3x8_bf16x8(uint32_t w0, uint32_t w1) {
 
 }  // namespace
 
-template <int D, int G, int W>
+template <int D, int G, int W, bool FP8>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(W, W)))
-decode_fp8_mfma_kernel(DecodeArgs a) {
+decode_mfma_kernel(DecodeArgs a) {
   constexpr int TK = kMfmaTileKeys;
-  constexpr int RB = D;                   // bytes of a pool row (one key, one kv head)
+  constexpr int RB = FP8 ? D : 2 * D;     // bytes of a pool row (one key, one kv head)
   constexpr int KS = D / 32;              // k-steps of S^T per 16-key block
-  constexpr int KU4 = D / 64;             // 16-byte K loads per lane per 16-key block
   constexpr int CPRV = RB / 16;           // 16-byte chunks of a pool row
-  constexpr int RPI = 64 / CPRV;          // rows per V load instruction
-  constexpr int VU4 = TK / RPI;           // V load instructions per tile
-  constexpr int RS = RB;                  // LDS row stride of the V tile (bytes)
+  constexpr int RPI = 64 / CPRV;          // rows per K / V load instruction
+  constexpr int VU4 = TK / RPI;           // K / V load instructions per tile
   constexpr int DB = D / 16;              // 16-wide d blocks of O^T
   constexpr float kRescaleLog2 = 8.f;
-  static_assert(G >= 1 && G <= 16 && KU4 >= 1 && VU4 >= 1 && TK % RPI == 0, "shape");
+  static_assert(G >= 1 && G <= 16 && VU4 >= 1 && TK % RPI == 0, "shape");
 
-  constexpr int kVBytes = kDecodeWaves * TK * RS;
+  constexpr int kTileBytes = kDecodeWaves * TK * RB;
   constexpr int MD = D + 4;                // merge row stride (floats): heads on distinct banks
   constexpr int kMergeBytes = kDecodeWaves * G * (MD + 2) * 4;
-  __shared__ __align__(16) char s_v[kVBytes > kMergeBytes ? kVBytes : kMergeBytes];
+  __shared__ __align__(16) char s_kv[kTileBytes > kMergeBytes ? kTileBytes : kMergeBytes];
   __shared__ uint32_t s_slot[kMaxDecodeSplit];
 
   const int tid = threadIdx.x;
@@ -154,23 +177,27 @@ decode_fp8_mfma_kernel(DecodeArgs a) {
   __syncthreads();
 
   const uint64_t slot_bytes = static_cast<uint64_t>(a.hkv) * RB;
-  const char* kbase = static_cast<const char*>(a.k_cache) + g * RB + quarter * 16;
-  const int vrow = lane / CPRV;     // row of a V load instruction
+  const int vrow = lane / CPRV;     // row of a K / V load instruction
   const int vchunk = lane % CPRV;   // 16-byte chunk of that row
+  const char* kbase = static_cast<const char*>(a.k_cache) + g * RB + vchunk * 16;
   const char* vbase = static_cast<const char*>(a.v_cache) + g * RB + vchunk * 16;
   // blocks of 16 keys or more (a power of two): the 16 keys of a tile half are consecutive
   // slots of one block (tiles start at multiples of 32 keys)
   const bool halves_in_block = a.bs_log2 >= 4;
   const int last16 = (nk - 1) & ~15;
 
-  char* sv = s_v + wave * TK * RS;
-  lds_char_t* sv_lds = (lds_char_t*)(sv);
-  // transposed-read address of this lane: row 4 quarter + k (k = col >> 1 < 4) or
-  // 16 + 4 quarter + k - 4, the half col & 1 of chunk db (swizzled)
+  // the wave's LDS tile: K codes / values of the tile, then (once the scores are taken) its V
+  char* skv = s_kv + wave * TK * RB;
+  lds_char_t* skv_lds = (lds_char_t*)(skv);
+  // transposed-read address of this lane. E4M3: row 4 quarter + k (k = col >> 1 < 4) or
+  // 16 + 4 quarter + k - 4, the half col & 1 of chunk db. bf16: rows 4 quarter + (col >> 2) and
+  // 16 + that, 8 bytes at 4 (col & 3) values into d block db (chunk 2 db + ((col & 3) >> 1)).
   const int k8 = col >> 1;
-  const int tr8_row = k8 < 4 ? 4 * quarter + k8 : 16 + 4 * quarter + k8 - 4;
-  const int tr8_off = tr8_row * RS + 8 * (col & 1);
-  const int tr8_sw = vswz8<CPRV>(tr8_row);
+  const int tr_row = FP8 ? (k8 < 4 ? 4 * quarter + k8 : 16 + 4 * quarter + k8 - 4)
+                         : 4 * quarter + (col >> 2);
+  const int tr_off = tr_row * RB + 8 * (col & 1);
+  const int tr_sw = FP8 ? vswz8<CPRV>(tr_row) : vswz16<CPRV>(tr_row);
+  const int tr_h = (col & 3) >> 1;
 
   float m_ref = -INFINITY;
   float l_run = 0.f;
@@ -184,27 +211,10 @@ decode_fp8_mfma_kernel(DecodeArgs a) {
     base0 = __builtin_amdgcn_readfirstlane(s_slot[ts]);
     base1 = __builtin_amdgcn_readfirstlane(s_slot[min(ts + 16, last16)]);
   };
-  // slots first (one uniform branch per tile, the LDS reads of the general path issued
-  // together), then the loads
-  auto load_k = [&](uint4 (&kr)[2][KU4], int ts) {
-    uint32_t sl[2];
-    if (halves_in_block) {
-      uint32_t base0, base1;
-      half_bases(ts, base0, base1);
-      sl[0] = base0 + col;
-      sl[1] = base1 + col;
-    } else {
-      sl[0] = s_slot[ts + col];
-      sl[1] = s_slot[ts + 16 + col];
-    }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const uint4* p = reinterpret_cast<const uint4*>(kbase + sl[kb] * slot_bytes);
-#pragma unroll
-      for (int u = 0; u < KU4; ++u) kr[kb][u] = load_nt(p + 4 * u);
-    }
-  };
-  auto load_v = [&](uint4 (&vr)[VU4], int ts) {
+  // K and V rows of tile ts: the slots first (one uniform branch per tile, the LDS reads of
+  // the general path issued together), then the loads; lane (vrow, vchunk) of instruction u
+  // takes chunk vchunk of key u RPI + vrow of both tensors
+  auto load_kv = [&](uint4 (&kr)[VU4], uint4 (&vr)[VU4], int ts) {
     uint32_t sl[VU4];
     if (halves_in_block) {
       uint32_t base0, base1;
@@ -219,40 +229,56 @@ decode_fp8_mfma_kernel(DecodeArgs a) {
       for (int u = 0; u < VU4; ++u) sl[u] = s_slot[ts + u * RPI + vrow];
     }
 #pragma unroll
-    for (int u = 0; u < VU4; ++u)
+    for (int u = 0; u < VU4; ++u) {
+      kr[u] = load_nt(reinterpret_cast<const uint4*>(kbase + sl[u] * slot_bytes));
       vr[u] = load_nt(reinterpret_cast<const uint4*>(vbase + sl[u] * slot_bytes));
+    }
   };
 
   // Tile ts from buffers kr / vr, which are refilled with tile nxt (when refill) once consumed
-  // (after the score MFMAs and the V tile's LDS write), so that tile stays in flight through
-  // the softmax and P.V of this one.
-  auto compute = [&](uint4 (&kr)[2][KU4], uint4 (&vr)[VU4], int ts, bool refill, int nxt) {
+  // (after the K and V tiles' LDS writes), so that tile stays in flight through the score
+  // MFMAs, softmax and P.V of this one.
+  auto compute = [&](uint4 (&kr)[VU4], uint4 (&vr)[VU4], int ts, bool refill, int nxt) {
     asm volatile("" ::: "memory");
     const int n = nk - ts;   // keys of this tile inside the context (>= 1)
+    // ---- K rows into the wave's LDS tile (keys past the context are masked below) ----
+#pragma unroll
+    for (int u = 0; u < VU4; ++u) {
+      const int r = u * RPI + vrow;
+      *reinterpret_cast<uint4*>(skv + r * RB + ((vchunk ^ kswz<CPRV>(r)) * 16)) = kr[u];
+    }
+
     // ---- S^T = K Q^T, the two 16-key blocks interleaved ----
     f32x4_t s[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int st = 0; st < KS; ++st)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const uint4 w = kr[kb][st / 2];
-        const uint4 kf = (st & 1) ? e4m3x8_bf16x8(w.z, w.w) : e4m3x8_bf16x8(w.x, w.y);
+        const int key = 16 * kb + col;
+        uint4 kf;
+        if constexpr (FP8) {
+          const int c = 4 * (st / 2) + quarter;
+          const uint2 w2 = *reinterpret_cast<const uint2*>(
+              skv + key * RB + ((c ^ kswz<CPRV>(key)) * 16) + 8 * (st & 1));
+          kf = e4m3x8_bf16x8(w2.x, w2.y);
+        } else {
+          const int c = 8 * (st / 2) + 2 * quarter + (st & 1);
+          kf = *reinterpret_cast<const uint4*>(skv + key * RB + ((c ^ kswz<CPRV>(key)) * 16));
+        }
         s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf), qf[st],
                                                         s[kb], 0, 0, 0);
       }
-    // ---- V codes into the wave's LDS tile (rows past the context: zero) ----
+
+    // ---- V rows into the same tile once the scores are read (rows past the context: zero) ----
 #pragma unroll
     for (int u = 0; u < VU4; ++u) {
       const int r = u * RPI + vrow;
       uint4 v = vr[u];
       if (n < TK && r >= n) v = make_uint4(0u, 0u, 0u, 0u);
-      *reinterpret_cast<uint4*>(sv + r * RS + ((vchunk ^ vswz8<CPRV>(r)) * 16)) = v;
+      const int sw = FP8 ? vswz8<CPRV>(r) : vswz16<CPRV>(r);
+      *reinterpret_cast<uint4*>(skv + r * RB + ((vchunk ^ sw) * 16)) = v;
     }
-
-    if (refill) {
-      load_v(vr, nxt);
-      load_k(kr, nxt);
-    }
+    if (refill) load_kv(kr, vr, nxt);
 
     // ---- lazy online softmax (base 2) for head col over this lane's 8 keys ----
     float t[2][4];
@@ -300,14 +326,23 @@ decode_fp8_mfma_kernel(DecodeArgs a) {
     const bf16x8_t phi = __builtin_bit_cast(bf16x8_t, phw);
     const bf16x8_t plo = __builtin_bit_cast(bf16x8_t, plw);
 
-    // ---- O^T += V^T P^T: V^T from one transposed read per d block (keys 4 quarter + 0..3,
-    //      16 + 4 quarter + 0..3 at d = 16 db + col) ----
+    // ---- O^T += V^T P^T: V^T from transposed reads per d block (keys 4 quarter + 0..3,
+    //      16 + 4 quarter + 0..3 at d = 16 db + col): one of E4M3 codes, two of bf16 ----
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const i32x2_t c8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-          (lds_i32x2_t*)(sv_lds + tr8_off + ((db ^ tr8_sw) * 16)));
-      const bf16x8_t va = __builtin_bit_cast(
-          bf16x8_t, e4m3x8_bf16x8(static_cast<uint32_t>(c8.x), static_cast<uint32_t>(c8.y)));
+      bf16x8_t va;
+      if constexpr (FP8) {
+        const i32x2_t c8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (lds_i32x2_t*)(skv_lds + tr_off + ((db ^ tr_sw) * 16)));
+        va = __builtin_bit_cast(
+            bf16x8_t, e4m3x8_bf16x8(static_cast<uint32_t>(c8.x), static_cast<uint32_t>(c8.y)));
+      } else {
+        const int off = tr_off + (((2 * db + tr_h) ^ tr_sw) * 16);
+        const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(skv_lds + off));
+        const i16x4_t v1 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(skv_lds + off + 16 * RB));
+        va = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
       acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, acc[db], 0, 0, 0);
       acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, acc[db], 0, 0, 0);
     }
@@ -321,11 +356,10 @@ decode_fp8_mfma_kernel(DecodeArgs a) {
   // four (with spills), were slower than one buffer at three.
   constexpr int kStep = kDecodeWaves * TK;
   const int n_tiles = nk > wave * TK ? (nk - wave * TK + kStep - 1) / kStep : 0;
-  uint4 kbuf[2][KU4];
+  uint4 kbuf[VU4];
   uint4 vbuf[VU4];
   if (n_tiles > 0) {
-    load_v(vbuf, wave * TK);
-    load_k(kbuf, wave * TK);
+    load_kv(kbuf, vbuf, wave * TK);
     for (int j = 0; j + 1 < n_tiles; ++j)
       compute(kbuf, vbuf, wave * TK + j * kStep, true, wave * TK + (j + 1) * kStep);
     compute(kbuf, vbuf, wave * TK + (n_tiles - 1) * kStep, false, 0);
@@ -335,8 +369,8 @@ decode_fp8_mfma_kernel(DecodeArgs a) {
   l_run = across16(l_run, AddOp());
   l_run = across32(l_run, AddOp());
 
-  const bool bad_row = __syncthreads_or(bad) != 0;   // also: every wave is done with s_v
-  float* mg_acc = reinterpret_cast<float*>(s_v);          // [4][G][MD]
+  const bool bad_row = __syncthreads_or(bad) != 0;   // also: every wave is done with s_kv
+  float* mg_acc = reinterpret_cast<float*>(s_kv);          // [4][G][MD]
   float* mg_m = mg_acc + kDecodeWaves * G * MD;            // [4][G]
   float* mg_l = mg_m + kDecodeWaves * G;                   // [4][G]
   if (col < G) {
@@ -362,7 +396,7 @@ decode_fp8_mfma_kernel(DecodeArgs a) {
       num = fmaf(fw, mg_acc[(w * G + h) * MD + d], num);
       den = fmaf(fw, mg_l[w * G + h], den);
     }
-    num *= a.v_scale;
+    if constexpr (FP8) num *= a.v_scale;
     const uint32_t nan_bits = 0x7fc00000u;
     const int hq = hq0 + h;
     if (it.part < 0) {
@@ -383,20 +417,25 @@ decode_fp8_mfma_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------------------
-bool decode_fp8_mfma_supported(int head_dim, int group) {
+bool decode_mfma_supported(int head_dim, int group) {
   return (head_dim == 64 || head_dim == 128) && group == 8;
 }
 
-hipError_t launch_decode_fp8_mfma(const DecodeArgs& a, uint32_t grid, int head_dim, int group,
-                                  hipStream_t stream) {
-  if (group != 8) return hipErrorInvalidValue;
-  // three waves per SIMD: 155 registers at head_dim 128
-  if (head_dim == 64)
-    hipLaunchKernelGGL((decode_fp8_mfma_kernel<64, 8, 3>), dim3(grid), dim3(256), 0, stream, a);
-  else if (head_dim == 128)
-    hipLaunchKernelGGL((decode_fp8_mfma_kernel<128, 8, 3>), dim3(grid), dim3(256), 0, stream, a);
+// Waves per SIMD, measured on the long-context decode steps: three (E4M3 at head_dim 128: 160
+// registers; bf16 at head_dim 64: 145); bf16 at head_dim 128 two (226 registers; at three it
+// spills and takes 1.4 times as long).
+hipError_t launch_decode_mfma(const DecodeArgs& a, uint32_t grid, int head_dim, int group,
+                              bool fp8, hipStream_t stream) {
+  if (!decode_mfma_supported(head_dim, group)) return hipErrorInvalidValue;
+  const dim3 blk(256);
+  if (fp8 && head_dim == 64)
+    hipLaunchKernelGGL((decode_mfma_kernel<64, 8, 3, true>), dim3(grid), blk, 0, stream, a);
+  else if (fp8)
+    hipLaunchKernelGGL((decode_mfma_kernel<128, 8, 3, true>), dim3(grid), blk, 0, stream, a);
+  else if (head_dim == 64)
+    hipLaunchKernelGGL((decode_mfma_kernel<64, 8, 3, false>), dim3(grid), blk, 0, stream, a);
   else
-    return hipErrorInvalidValue;
+    hipLaunchKernelGGL((decode_mfma_kernel<128, 8, 2, false>), dim3(grid), blk, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -118,11 +118,11 @@ hipError_t launch_stage_write_kv_fp8(const StageArgs& st, const WriteFp8Args& a,
                                      hipStream_t stream);
 hipError_t launch_decode_fp8(const DecodeArgs& a, int64_t n_items, int head_dim, int group,
                              hipStream_t stream);
-// decode_fp8_mfma.hip: the E4M3 decode split pass on MFMA for groups of 8 (grid = items x hkv,
-// as launch_decode_fp8, which routes those groups here).
-bool decode_fp8_mfma_supported(int head_dim, int group);
-hipError_t launch_decode_fp8_mfma(const DecodeArgs& a, uint32_t grid, int head_dim, int group,
-                                  hipStream_t stream);
+// decode_mfma.hip: the decode split pass on MFMA for groups of 8, bf16 or E4M3 pools (grid =
+// items x hkv; launch_decode and launch_decode_fp8 route those groups here).
+bool decode_mfma_supported(int head_dim, int group);
+hipError_t launch_decode_mfma(const DecodeArgs& a, uint32_t grid, int head_dim, int group,
+                              bool fp8, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int64_t n_items, int head_dim, int group,
                          bool bf16, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int64_t n_items, int head_dim, hipStream_t stream);
