@@ -551,9 +551,7 @@ def _decode_roofline(res, name, kernel):
 
 def _decode_kernel_name(w):
     """The decode kernel a decode-only workload runs on (its group and pool type)."""
-    if w.spec.Hq // w.spec.Hkv == 8 and (w.kv_fp8 or w.spec.dtype == "bf16"):
-        return "decode_mfma_kernel"
-    return "decode_fp8_kernel" if w.kv_fp8 else "decode_split_kernel"
+    return "decode_mfma_kernel" if (w.kv_fp8 or w.spec.dtype == "bf16") else "decode_f32_kernel"
 
 
 def _clocks():

@@ -358,13 +358,13 @@ int32_t pkv_write_kv_attention(const void* q, const void* k_new, const void* v_n
  *                 block_size) only).
  * A decode split (kv_split keys aligned at a multiple of kv_split) that lies wholly inside the
  * contexts of several decode rows and covers the same physical blocks in each is read once per
- * group of up to 4 (or 2, per build) of those rows, instead of once per row: one work item
- * loads its K/V tiles once and runs every row's arithmetic of the per-row decode item on
- * them, row by row. So every output bit is the same as with pkv_write_kv_attention (and as
- * each row alone): only HBM and cache traffic change. Applies to bfloat16 pools with
- * num_q_heads / num_kv_heads in {1, 2, 4} on the split decode pass (not in the
- * phase-consistent mode, where decode rows run on the tile path); otherwise the call is
- * exactly pkv_write_kv_attention. If the device tables name other blocks than the host copy
+ * group of up to min(4, 16 / (num_q_heads / num_kv_heads)) of those rows, instead of once per
+ * row: one work item loads its K/V tiles once and runs every row's arithmetic of the per-row
+ * decode item on them (the rows' query heads side by side in the matrix-core tile). So every
+ * output bit is the same as with pkv_write_kv_attention (and as each row alone): only HBM and
+ * cache traffic change. Applies to bfloat16 pools with num_q_heads / num_kv_heads in
+ * {1, 2, 4, 8} on the split decode pass (not in the phase-consistent mode, where decode rows
+ * run on the tile path); otherwise the call is exactly pkv_write_kv_attention. If the device tables name other blocks than the host copy
  * for a row of a group, that row is written as NaN (never from another row's keys).
  * The workspace comes from pkv_write_kv_attention_shared_workspace_size with the same host
  * tables (the group items take the place of per-row items in the lists).

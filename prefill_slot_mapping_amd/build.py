@@ -21,20 +21,18 @@ LIB_PATH = os.path.join(PKG_DIR, "libpkv.so")
 ARCH = "gfx950"
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
-DEVICE_SOURCES = ["write_kv.hip", "decode.hip", "decode_fp8.hip", "decode_mfma.hip", "merge.hip",
+DEVICE_SOURCES = ["write_kv.hip", "decode.hip", "decode_mfma.hip", "merge.hip",
                   "prefill.hip", "noalloc.hip"]
 HOST_SOURCES = ["allocator.cpp", "api.cpp", "planner.cpp", "scheduler.cpp"]
 
 # Packed-FP32 instructions are disabled for all device code: the compiler may not form
 # v_pk_{add,mul,fma}_f32 from ordinary float code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-# Per-source extras. decode.hip, decode_fp8.hip, decode_mfma.hip: no floating-point operation
-# there sees a NaN (bad rows are written as a NaN bit pattern through an integer select), which
-# lets maxima fuse with their DPP lane permutes. decode.hip: no implicit contraction of a multiply and an add into an FMA
-# (every FMA is written out), so kernel instances that differ only in how many rows share a
-# tile compute every row with the same operations.
+# Per-source extras. decode.hip, decode_mfma.hip: no floating-point operation there sees a NaN
+# (bad rows are written as a NaN bit pattern through an integer select), which lets maxima fuse
+# with their DPP lane permutes. decode.hip: no implicit contraction of a multiply and an add into
+# an FMA (every FMA is written out).
 SOURCE_FLAGS = {"decode.hip": ["-fno-honor-nans", "-ffp-contract=off"],
-                "decode_fp8.hip": ["-fno-honor-nans"],
                 "decode_mfma.hip": ["-fno-honor-nans"]}
 
 

@@ -348,7 +348,7 @@ int32_t check_flags(uint32_t flags, int32_t hq, int32_t hkv, int32_t head_dim, i
 StepShape shape_for(const int32_t* ctx, const int32_t* cu, int32_t B, int32_t hq, int32_t hkv,
                     int32_t head_dim, int32_t kv_split, int32_t dtype, uint32_t flags,
                     const int32_t* bt_host = nullptr, int32_t bt_stride = 0,
-                    int32_t block_size = 0, bool fp8 = false) {
+                    int32_t block_size = 0) {
   StepShape s;
   s.all_mfma = (flags & PKV_ATTN_PHASE_CONSISTENT) != 0;
   s.ctx = ctx;
@@ -359,13 +359,14 @@ StepShape shape_for(const int32_t* ctx, const int32_t* cu, int32_t B, int32_t hq
   s.prefill_on_mfma = pkv::prefill_supported(head_dim, group, dtype == PKV_BF16);
   s.prefill_rows_per_item = pkv::kPrefillMRows / group;
   s.tile_split = s.all_mfma ? kv_split : 0;
-  // shared reads: bf16 pools on the split decode pass, groups the group-item kernel serves
-  if (bt_host != nullptr && !fp8 && dtype == PKV_BF16 && !s.all_mfma &&
+  // shared reads: bf16 or E4M3 pools on the split decode pass, groups the group-item kernel
+  // serves
+  if (bt_host != nullptr && dtype == PKV_BF16 && !s.all_mfma &&
       pkv::decode_groups_supported(head_dim, group)) {
     s.bt_host = bt_host;
     s.bt_stride = bt_stride;
     s.block_size = block_size;
-    s.group_rows = pkv::decode_group_rows();
+    s.group_rows = pkv::decode_group_rows(group);
   }
   return s;
 }
@@ -512,7 +513,7 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
 
   StepShape s = shape_for(ctx_lens_host, cu_seqlens_q_host, B, num_q_heads, num_kv_heads,
                           head_dim, kv_split, dtype, flags, block_tables_host, max_blocks,
-                          block_size, fp8_scales != nullptr);
+                          block_size);
   // the shared splits are found once for the layout and the lists
   pkv::SharedSplits shared;
   if (s.bt_host != nullptr && s.group_rows > 1) {
@@ -662,7 +663,8 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
       d.part_l = part_l;
       d.part_acc = part_acc;
       const int pr = prof_begin(4, gstrm);
-      hipError_t e = pkv::launch_decode_groups(d, L.n_group, head_dim, group, gstrm);
+      hipError_t e =
+          pkv::launch_decode_groups(d, L.n_group, head_dim, group, fp8_scales != nullptr, gstrm);
       prof_end(pr, gstrm);
       if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("decode group launch: ") + hipGetErrorString(e));
     }
@@ -750,7 +752,7 @@ int32_t workspace_size_impl(const int32_t* ctx_lens_host, const int32_t* cu_seql
   if (st != PKV_OK) return st;
   StepShape s = shape_for(ctx_lens_host, cu_seqlens_q_host, B, num_q_heads, num_kv_heads,
                           head_dim, kv_split, dtype, flags, block_tables_host, max_blocks,
-                          block_size, fp8);
+                          block_size);
   if (fp8 && !pkv::decode_fp8_supported(head_dim, num_q_heads / num_kv_heads))
     return fail(PKV_ERR_UNSUPPORTED, "attention_fp8: head_dim 64 or 128 and num_q_heads / "
                                      "num_kv_heads one of 1, 2, 4, 8");

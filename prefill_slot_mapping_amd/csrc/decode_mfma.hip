@@ -104,7 +104,7 @@ __device__ __forceinline__ uint4 e4m3x8_bf16x8(uint32_t w0, uint32_t w1) {
 
 }  // namespace
 
-template <int D, int G, int W, bool FP8>
+template <int D, int G, int W, bool FP8, int R>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(W, W)))
 decode_mfma_kernel(DecodeArgs a) {
   constexpr int TK = kMfmaTileKeys;
@@ -115,11 +115,12 @@ decode_mfma_kernel(DecodeArgs a) {
   constexpr int VU4 = TK / RPI;           // K / V load instructions per tile
   constexpr int DB = D / 16;              // 16-wide d blocks of O^T
   constexpr float kRescaleLog2 = 8.f;
-  static_assert(G >= 1 && G <= 16 && VU4 >= 1 && TK % RPI == 0, "shape");
+  constexpr int NC = R * G;               // MFMA columns in use: (row r, head h) at r G + h
+  static_assert(NC >= 1 && NC <= 16 && R <= kGroupRows && VU4 >= 1 && TK % RPI == 0, "shape");
 
   constexpr int kTileBytes = kDecodeWaves * TK * RB;
-  constexpr int MD = D + 4;                // merge row stride (floats): heads on distinct banks
-  constexpr int kMergeBytes = kDecodeWaves * G * (MD + 2) * 4;
+  constexpr int MD = D + 4;                // merge row stride (floats): columns on distinct banks
+  constexpr int kMergeBytes = kDecodeWaves * NC * (MD + 2) * 4;
   __shared__ __align__(16) char s_kv[kTileBytes > kMergeBytes ? kTileBytes : kMergeBytes];
   __shared__ uint32_t s_slot[kMaxDecodeSplit];
 
@@ -134,15 +135,36 @@ decode_mfma_kernel(DecodeArgs a) {
   const int item_idx = f / a.hkv;
   const int g = f - item_idx * a.hkv;
   const int hq0 = g * G;
-  const DecodeItem it = a.items[item_idx];
+  int split, n_keys, n_rows;
+  int row[R], seq[R], part[R];
+  if constexpr (R == 1) {
+    const DecodeItem it = a.items[item_idx];
+    split = it.split;
+    n_keys = it.n_keys;
+    n_rows = 1;
+    row[0] = it.row;
+    seq[0] = it.seq;
+    part[0] = it.part;
+  } else {
+    const DecodeGroupItem it = a.groups[item_idx];
+    split = it.split;
+    n_keys = it.n_keys;
+    n_rows = it.n_rows;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      row[r] = it.row[r];
+      seq[r] = it.seq[r];
+      part[r] = it.part[r];
+    }
+  }
 
-  const int t0 = it.split * a.kv_split;
-  const int t1 = min(it.n_keys, t0 + a.kv_split);
+  const int t0 = split * a.kv_split;
+  const int t1 = min(n_keys, t0 + a.kv_split);
   const int nk = t1 - t0;
   const int nk_pad = (nk + TK - 1) / TK * TK;
-  const int32_t* bt = a.block_tables + static_cast<int64_t>(it.seq) * a.max_blocks;
+  const int32_t* bt = a.block_tables + static_cast<int64_t>(seq[0]) * a.max_blocks;
   // slot of each key of the split (keys past the context: the last key's slot); an out-of-pool
-  // block id marks the row bad and reads slot 0
+  // block id marks the item bad and reads slot 0
   bool bad = false;
   for (int k = tid; k < nk_pad; k += 256) {
     const int pos = t0 + min(k, nk - 1);
@@ -159,15 +181,36 @@ decode_mfma_kernel(DecodeArgs a) {
     bad |= !ok;
     s_slot[k] = ok ? static_cast<uint32_t>(b * a.block_size + off) : 0u;
   }
+  // group items: rows after the first must name the same blocks over the split (else they are
+  // written as NaN rather than computed from the first row's keys)
+  bool row_bad[R];
+  row_bad[0] = false;
+  if constexpr (R > 1) {
+    const int j0 = a.bs_log2 >= 0 ? t0 >> a.bs_log2 : t0 / a.block_size;
+    const int j1 = a.bs_log2 >= 0 ? (t1 - 1) >> a.bs_log2 : (t1 - 1) / a.block_size;
+#pragma unroll
+    for (int r = 1; r < R; ++r) {
+      bool mis = false;
+      if (r < n_rows) {
+        const int32_t* btr = a.block_tables + static_cast<int64_t>(seq[r]) * a.max_blocks;
+        for (int j = j0 + tid; j <= j1; j += 256) mis |= btr[j] != bt[j];
+      }
+      row_bad[r] = __syncthreads_or(mis) != 0;
+    }
+  }
 
-  // B operand of S^T: q[head col][the 8 d of k-step st in this lane's quarter], zero for
-  // columns past G
+  // B operand of S^T: column col = (row col / G, head col % G) takes that q row's 8 d of k-step
+  // st in this lane's quarter; columns past the item's rows are zero
   bf16x8_t qf[KS];
   {
-    const bool hv = col < G;
+    const int cr = col / G;
+    int qrow = row[0];
+#pragma unroll
+    for (int r = 1; r < R; ++r) qrow = cr == r ? row[r] : qrow;
+    const bool hv = col < NC && cr < n_rows;
     const uint4* qs = reinterpret_cast<const uint4*>(
         static_cast<const char*>(a.q) +
-        (static_cast<int64_t>(it.row) * a.hq + hq0 + (hv ? col : 0)) * (D * 2));
+        (static_cast<int64_t>(hv ? qrow : row[0]) * a.hq + hq0 + (hv ? col % G : 0)) * (D * 2));
 #pragma unroll
     for (int st = 0; st < KS; ++st) {
       const int d0 = 64 * (st / 2) + 16 * quarter + 8 * (st % 2);
@@ -370,45 +413,56 @@ decode_mfma_kernel(DecodeArgs a) {
   l_run = across32(l_run, AddOp());
 
   const bool bad_row = __syncthreads_or(bad) != 0;   // also: every wave is done with s_kv
-  float* mg_acc = reinterpret_cast<float*>(s_kv);          // [4][G][MD]
-  float* mg_m = mg_acc + kDecodeWaves * G * MD;            // [4][G]
-  float* mg_l = mg_m + kDecodeWaves * G;                   // [4][G]
-  if (col < G) {
+  float* mg_acc = reinterpret_cast<float*>(s_kv);          // [4][NC][MD]
+  float* mg_m = mg_acc + kDecodeWaves * NC * MD;           // [4][NC]
+  float* mg_l = mg_m + kDecodeWaves * NC;                  // [4][NC]
+  if (col < NC) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
-      *reinterpret_cast<f32x4_t*>(mg_acc + (wave * G + col) * MD + 16 * db + 4 * quarter) = acc[db];
+      *reinterpret_cast<f32x4_t*>(mg_acc + (wave * NC + col) * MD + 16 * db + 4 * quarter) = acc[db];
     if (quarter == 0) {
-      mg_m[wave * G + col] = m_ref;
-      mg_l[wave * G + col] = l_run;
+      mg_m[wave * NC + col] = m_ref;
+      mg_l[wave * NC + col] = l_run;
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < G * D; idx += 256) {
-    const int h = idx / D;
-    const int d = idx - h * D;
-    float M = mg_m[h];
+  for (int idx = tid; idx < NC * D; idx += 256) {
+    const int c = idx / D;
+    const int d = idx - c * D;
+    const int cr = c / G;
+    if (cr >= n_rows) continue;
+    int orow = row[0], opart = part[0];
+    bool obad = row_bad[0];
 #pragma unroll
-    for (int w = 1; w < kDecodeWaves; ++w) M = fmaxf(M, mg_m[w * G + h]);
+    for (int r = 1; r < R; ++r) {
+      orow = cr == r ? row[r] : orow;
+      opart = cr == r ? part[r] : opart;
+      obad = cr == r ? row_bad[r] : obad;
+    }
+    obad = obad || bad_row;
+    float M = mg_m[c];
+#pragma unroll
+    for (int w = 1; w < kDecodeWaves; ++w) M = fmaxf(M, mg_m[w * NC + c]);
     float num = 0.f, den = 0.f;
 #pragma unroll
     for (int w = 0; w < kDecodeWaves; ++w) {
-      const float fw = fast_exp2(mg_m[w * G + h] - M);
-      num = fmaf(fw, mg_acc[(w * G + h) * MD + d], num);
-      den = fmaf(fw, mg_l[w * G + h], den);
+      const float fw = fast_exp2(mg_m[w * NC + c] - M);
+      num = fmaf(fw, mg_acc[(w * NC + c) * MD + d], num);
+      den = fmaf(fw, mg_l[w * NC + c], den);
     }
     if constexpr (FP8) num *= a.v_scale;
     const uint32_t nan_bits = 0x7fc00000u;
-    const int hq = hq0 + h;
-    if (it.part < 0) {
+    const int hq = hq0 + c - cr * G;
+    if (opart < 0) {
       const float o = num / den;
-      a.out[(static_cast<int64_t>(it.row) * a.hq + hq) * D + d] =
-          __uint_as_float(bad_row ? nan_bits : __float_as_uint(o));
+      a.out[(static_cast<int64_t>(orow) * a.hq + hq) * D + d] =
+          __uint_as_float(obad ? nan_bits : __float_as_uint(o));
     } else {
-      const int64_t p = static_cast<int64_t>(it.part + it.split) * a.hq + hq;
-      a.part_acc[p * D + d] = __uint_as_float(bad_row ? nan_bits : __float_as_uint(num));
+      const int64_t p = static_cast<int64_t>(opart + split) * a.hq + hq;
+      a.part_acc[p * D + d] = __uint_as_float(obad ? nan_bits : __float_as_uint(num));
       if (d == 0) {
         a.part_m[p] = M;
-        a.part_l[p] = __uint_as_float(bad_row ? nan_bits : __float_as_uint(den));
+        a.part_l[p] = __uint_as_float(obad ? nan_bits : __float_as_uint(den));
       }
     }
   }
@@ -418,25 +472,57 @@ decode_mfma_kernel(DecodeArgs a) {
 // launcher
 // ---------------------------------------------------------------------------------------
 bool decode_mfma_supported(int head_dim, int group) {
-  return (head_dim == 64 || head_dim == 128) && group == 8;
+  return (head_dim == 64 || head_dim == 128) &&
+         (group == 1 || group == 2 || group == 4 || group == 8);
 }
 
-// Waves per SIMD, measured on the long-context decode steps: three (E4M3 at head_dim 128: 160
-// registers; bf16 at head_dim 64: 145); bf16 at head_dim 128 two (226 registers; at three it
-// spills and takes 1.4 times as long).
-hipError_t launch_decode_mfma(const DecodeArgs& a, uint32_t grid, int head_dim, int group,
-                              bool fp8, hipStream_t stream) {
-  if (!decode_mfma_supported(head_dim, group)) return hipErrorInvalidValue;
-  const dim3 blk(256);
-  if (fp8 && head_dim == 64)
-    hipLaunchKernelGGL((decode_mfma_kernel<64, 8, 3, true>), dim3(grid), blk, 0, stream, a);
-  else if (fp8)
-    hipLaunchKernelGGL((decode_mfma_kernel<128, 8, 3, true>), dim3(grid), blk, 0, stream, a);
-  else if (head_dim == 64)
-    hipLaunchKernelGGL((decode_mfma_kernel<64, 8, 3, false>), dim3(grid), blk, 0, stream, a);
+// Rows of a group item: as many as fill the 16 MFMA columns, at most kGroupRows.
+int decode_mfma_group_rows(int group) {
+  return group >= 1 && group <= 16 ? (16 / group < kGroupRows ? 16 / group : kGroupRows) : 1;
+}
+
+namespace {
+
+// Waves per SIMD (measured on the long-context and batched decode steps): three, except bf16
+// at head_dim 128 (226 registers: two; at three it spills and takes 1.4 times as long).
+template <int D, bool FP8>
+constexpr int mfma_waves() {
+  return (!FP8 && D == 128) ? 2 : 3;
+}
+
+template <int D, int G, bool FP8>
+void launch_g(const DecodeArgs& a, uint32_t grid, bool groups, hipStream_t stream) {
+  constexpr int W = mfma_waves<D, FP8>();
+  constexpr int RG = 16 / G < kGroupRows ? 16 / G : kGroupRows;
+  if (groups)
+    hipLaunchKernelGGL((decode_mfma_kernel<D, G, W, FP8, RG>), dim3(grid), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_mfma_kernel<128, 8, 2, false>), dim3(grid), blk, 0, stream, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, G, W, FP8, 1>), dim3(grid), dim3(256), 0, stream, a);
+}
+
+template <int D, bool FP8>
+hipError_t launch_d(const DecodeArgs& a, uint32_t grid, int group, bool groups,
+                    hipStream_t stream) {
+  switch (group) {
+    case 1: launch_g<D, 1, FP8>(a, grid, groups, stream); break;
+    case 2: launch_g<D, 2, FP8>(a, grid, groups, stream); break;
+    case 4: launch_g<D, 4, FP8>(a, grid, groups, stream); break;
+    case 8: launch_g<D, 8, FP8>(a, grid, groups, stream); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, uint32_t grid, int head_dim, int group,
+                              bool fp8, bool groups, hipStream_t stream) {
+  if (!decode_mfma_supported(head_dim, group)) return hipErrorInvalidValue;
+  if (head_dim == 64)
+    return fp8 ? launch_d<64, true>(a, grid, group, groups, stream)
+               : launch_d<64, false>(a, grid, group, groups, stream);
+  return fp8 ? launch_d<128, true>(a, grid, group, groups, stream)
+             : launch_d<128, false>(a, grid, group, groups, stream);
 }
 
 }  // namespace pkv

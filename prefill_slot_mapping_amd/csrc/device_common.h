@@ -60,12 +60,4 @@ __device__ __forceinline__ float wave_max_pairs(float x) {
   return x;
 }
 
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                         __builtin_bit_cast(bf16x2_t, b), c, false);
-}
-
-__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
-
 }  // namespace pkv

@@ -118,26 +118,29 @@ hipError_t launch_stage_write_kv_fp8(const StageArgs& st, const WriteFp8Args& a,
                                      hipStream_t stream);
 hipError_t launch_decode_fp8(const DecodeArgs& a, int64_t n_items, int head_dim, int group,
                              hipStream_t stream);
-// decode_mfma.hip: the decode split pass on MFMA for groups of 8, bf16 or E4M3 pools (grid =
-// items x hkv; launch_decode and launch_decode_fp8 route those groups here).
+// decode_mfma.hip: the decode split pass on MFMA, bf16 or E4M3 pools (grid = items x hkv).
+// groups: a.groups holds group items of up to decode_mfma_group_rows(group) rows; otherwise
+// a.items holds per-row items.
 bool decode_mfma_supported(int head_dim, int group);
+int decode_mfma_group_rows(int group);
 hipError_t launch_decode_mfma(const DecodeArgs& a, uint32_t grid, int head_dim, int group,
-                              bool fp8, hipStream_t stream);
+                              bool fp8, bool groups, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int64_t n_items, int head_dim, int group,
                          bool bf16, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int64_t n_items, int head_dim, hipStream_t stream);
-// The group items a.groups[0 .. n_groups): each row computed exactly as by launch_decode.
+// The group items a.groups[0 .. n_groups): each row computed exactly as by launch_decode
+// (bf16 pools) or launch_decode_fp8 (fp8: E4M3 pools).
 hipError_t launch_decode_groups(const DecodeArgs& a, int64_t n_groups, int head_dim, int group,
-                                hipStream_t stream);
+                                bool fp8, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int64_t n_items, int head_dim, int group,
                           bool fp8, hipStream_t stream);
 
 // Whether a (head_dim, group, dtype) combination has a built decode / prefill kernel.
 bool decode_supported(int head_dim, int group);
-// Whether a (head_dim, group) combination of bf16 pools has a group-item decode kernel, and
-// how many rows its group items hold at most.
+// Whether a (head_dim, group) combination of bf16 or E4M3 pools has a group-item decode
+// kernel, and how many rows its group items hold at most.
 bool decode_groups_supported(int head_dim, int group);
-int decode_group_rows();
+int decode_group_rows(int group);
 bool decode_fp8_supported(int head_dim, int group);
 bool prefill_supported(int head_dim, int group, bool bf16);
 

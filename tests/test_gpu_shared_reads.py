@@ -58,6 +58,8 @@ SHARED_SPECS = [
     (4, 4, 64, 32, 2, 6, 2048, 1, 400, 256),       # group 1, head_dim 64
     (16, 4, 128, 16, 2, 3, 512, 1, 64, 512),        # one whole shared split each
     (16, 4, 128, 8, 1, 7, 704, 1, 2000, 64),       # many short splits
+    (32, 4, 128, 16, 2, 5, 1536, 1, 900, 512),     # group 8: two rows per group item
+    (64, 8, 64, 32, 2, 3, 1024, 1, 700, 256),      # group 8, head_dim 64
 ]
 
 
