@@ -458,6 +458,31 @@ int32_t pkv_write_kv_attention_fp8(const void* q, const void* k_new, const void*
                                    uint32_t flags, float* out, void* workspace,
                                    size_t workspace_bytes, void* stream);
 
+/* Fused E4M3 step with shared reads [P3 "Design > engine.py", Prefix sharing; "Finish RL
+ * Training Faster: Bitwise-Consistent ...", section 4.2, one read path for FP8 storage]:
+ * pkv_write_kv_attention_fp8 with a host copy of the block tables, exactly as
+ * pkv_write_kv_attention_shared is pkv_write_kv_attention with one: decode splits that lie
+ * wholly in the same physical blocks for several rows are read once per group of rows, every
+ * output bit the same as pkv_write_kv_attention_fp8 on the same step (and as each row alone).
+ * Arguments as pkv_write_kv_attention_fp8 plus block_tables_host / max_blocks as in
+ * pkv_write_kv_attention_shared; the workspace comes from
+ * pkv_write_kv_attention_shared_fp8_workspace_size with the same host tables. Errors: as
+ * pkv_write_kv_attention_fp8, plus those of the host tables in pkv_write_kv_attention_shared. */
+int32_t pkv_write_kv_attention_shared_fp8_workspace_size(
+    const int32_t* ctx_lens_host, const int32_t* cu_seqlens_q_host, int32_t B,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t kv_split,
+    uint32_t flags, int32_t n_rows, const int32_t* block_tables_host, int32_t max_blocks,
+    int32_t block_size, size_t* bytes);
+
+int32_t pkv_write_kv_attention_shared_fp8(
+    const void* q, const void* k_new, const void* v_new, const int32_t* slots_host,
+    int32_t n_rows, void* k_cache, void* v_cache, const int32_t* block_tables_dev,
+    const int32_t* block_tables_host, int32_t max_blocks, const int32_t* ctx_lens_host,
+    const int32_t* cu_seqlens_q_host, int32_t B, int32_t T, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+    float k_scale, float v_scale, int32_t kv_split, uint32_t flags, float* out, void* workspace,
+    size_t workspace_bytes, void* stream);
+
 /* ---- allocation-free attention ---------------------------------------------------------
  * For callers that cannot allocate device memory during a call: code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc.

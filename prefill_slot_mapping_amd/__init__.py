@@ -12,5 +12,6 @@ from ._lib import (  # noqa: F401
     staging_info, validate_slots, version, write_kv, write_kv_attention, write_kv_attention_workspace_size,
     write_kv_attention_shared, write_kv_attention_shared_workspace_size,
     write_kv_attention_fp8, write_kv_attention_fp8_workspace_size, write_kv_fp8,
+    write_kv_attention_shared_fp8, write_kv_attention_shared_fp8_workspace_size,
 )
 from . import accounting  # noqa: F401

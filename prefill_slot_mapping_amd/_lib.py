@@ -140,6 +140,16 @@ _SIGS = {
                                        _pi32, _pi32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                        ctypes.c_float, _i32, _i32, ctypes.c_uint32, _vp, _vp,
                                        ctypes.c_size_t, _vp], _i32),
+    "pkv_write_kv_attention_shared_fp8_workspace_size": ([_pi32, _pi32, _i32, _i32, _i32, _i32,
+                                                          _i32, ctypes.c_uint32, _i32, _pi32,
+                                                          _i32, _i32,
+                                                          ctypes.POINTER(ctypes.c_size_t)],
+                                                         _i32),
+    "pkv_write_kv_attention_shared_fp8": ([_vp, _vp, _vp, _pi32, _i32, _vp, _vp, _vp, _pi32,
+                                           _i32, _pi32, _pi32, _i32, _i32, _i32, _i32, _i32,
+                                           _i32, _i32, ctypes.c_float, ctypes.c_float,
+                                           ctypes.c_float, _i32, ctypes.c_uint32, _vp, _vp,
+                                           ctypes.c_size_t, _vp], _i32),
     "pkv_write_kv_fp8": ([_vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
                           ctypes.c_float, ctypes.c_float, _vp], _i32),
     "pkv_attention_fp8_workspace_size": ([_pi32, _pi32, _i32, _i32, _i32, _i32, _i32,
@@ -840,6 +850,74 @@ def write_kv_attention_fp8(q, k_new, v_new, slots, k_cache, v_cache, block_table
         _check(lib().pkv_write_kv_attention_fp8(
             q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), _ptr(sl), n_rows,
             k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+            int(block_tables.shape[1]), _ptr(ctx), _ptr(cu), B, T, hq, hkv, d, bs, nb,
+            float(scale), float(k_scale), float(v_scale), int(kv_split), flags, out.data_ptr(),
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            _stream_ptr(q, stream)))
+    return out
+
+
+def write_kv_attention_shared_fp8_workspace_size(ctx_lens, cu_seqlens_q, num_q_heads: int,
+                                                num_kv_heads: int, head_dim: int, n_rows: int,
+                                                block_tables_host, block_size: int,
+                                                kv_split: int = 512,
+                                                phase_consistent: bool = False) -> int:
+    ctx = _host_i32(ctx_lens)
+    cu = _host_i32(cu_seqlens_q)
+    bt = _host_i32(block_tables_host)
+    mb = int(bt.shape[1]) if bt.ndim == 2 else 0
+    out = ctypes.c_size_t(0)
+    flags = PKV_ATTN_PHASE_CONSISTENT if phase_consistent else 0
+    _check(lib().pkv_write_kv_attention_shared_fp8_workspace_size(
+        _ptr(ctx), _ptr(cu), ctx.size, int(num_q_heads), int(num_kv_heads), int(head_dim),
+        int(kv_split), flags, int(n_rows), _ptr(bt), mb, int(block_size), ctypes.byref(out)))
+    return int(out.value)
+
+
+def write_kv_attention_shared_fp8(q, k_new, v_new, slots, k_cache, v_cache, block_tables,
+                                  block_tables_host, ctx_lens, cu_seqlens_q, scale: float,
+                                  k_scale: float, v_scale: float, out=None, workspace=None,
+                                  kv_split: int = 512, stream=None,
+                                  phase_consistent: bool = False):
+    """pkv_write_kv_attention_shared_fp8: pkv_write_kv_attention_fp8 with a host copy of the
+    block tables, so that decode splits shared by several rows are read once per group of
+    rows; same output bits. Returns out."""
+    import torch
+    _need_cuda(q, k_new, v_new, k_cache, v_cache, block_tables)
+    _need_fp8_pools(k_cache, v_cache)
+    if block_tables.dtype != torch.int32:
+        raise ValueError("block_tables must be int32")
+    if q.dtype != torch.bfloat16 or k_new.dtype != torch.bfloat16 or \
+            v_new.dtype != torch.bfloat16:
+        raise ValueError("q, k_new and v_new must be bfloat16")
+    sl = slots if isinstance(slots, np.ndarray) and slots.dtype == np.int32 and \
+        slots.flags.c_contiguous else _host_i32(slots)
+    bth = _host_i32(block_tables_host)
+    ctx = _host_i32(ctx_lens)
+    cu = _host_i32(cu_seqlens_q)
+    T, hq, d = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    if d2 != d:
+        raise ValueError("q / pool head_dim mismatch")
+    n_rows = int(k_new.shape[0])
+    if sl.size != n_rows or v_new.shape != k_new.shape:
+        raise ValueError("slots / k_new / v_new row counts differ")
+    B = ctx.size
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or bth.ndim != 2 or \
+            bth.shape[0] != B or bth.shape[1] != block_tables.shape[1]:
+        raise ValueError("block_tables (device and host) must be [B, max_blocks]")
+    flags = PKV_ATTN_PHASE_CONSISTENT if phase_consistent else 0
+    with _on_stream(stream):
+        if out is None:
+            out = torch.empty((T, hq, d), dtype=torch.float32, device=q.device)
+        _need_cuda(out)
+        if workspace is None:
+            need = write_kv_attention_shared_fp8_workspace_size(
+                ctx, cu, hq, hkv, d, n_rows, bth, bs, kv_split, phase_consistent)
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        _check(lib().pkv_write_kv_attention_shared_fp8(
+            q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), _ptr(sl), n_rows,
+            k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), _ptr(bth),
             int(block_tables.shape[1]), _ptr(ctx), _ptr(cu), B, T, hq, hkv, d, bs, nb,
             float(scale), float(k_scale), float(v_scale), int(kv_split), flags, out.data_ptr(),
             workspace.data_ptr(), workspace.numel() * workspace.element_size(),

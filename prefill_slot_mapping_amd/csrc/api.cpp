@@ -1052,6 +1052,46 @@ extern "C" int32_t pkv_write_kv_attention_fp8(
                         workspace_bytes, stream, nullptr, slots_host, scales, &a);
 }
 
+extern "C" int32_t pkv_write_kv_attention_shared_fp8_workspace_size(
+    const int32_t* ctx_lens_host, const int32_t* cu_seqlens_q_host, int32_t B,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t kv_split,
+    uint32_t flags, int32_t n_rows, const int32_t* block_tables_host, int32_t max_blocks,
+    int32_t block_size, size_t* bytes) {
+  if (bytes != nullptr) *bytes = 0;
+  if (B > 0 && ctx_lens_host != nullptr) {
+    const int32_t st = check_host_tables(block_tables_host, max_blocks, block_size,
+                                         ctx_lens_host, B);
+    if (st != PKV_OK) return st;
+  }
+  return workspace_size_impl(ctx_lens_host, cu_seqlens_q_host, B, num_q_heads, num_kv_heads,
+                             head_dim, kv_split, PKV_BF16, flags, n_rows, bytes, true,
+                             block_tables_host, max_blocks, block_size);
+}
+
+extern "C" int32_t pkv_write_kv_attention_shared_fp8(
+    const void* q, const void* k_new, const void* v_new, const int32_t* slots_host,
+    int32_t n_rows, void* k_cache, void* v_cache, const int32_t* block_tables_dev,
+    const int32_t* block_tables_host, int32_t max_blocks, const int32_t* ctx_lens_host,
+    const int32_t* cu_seqlens_q_host, int32_t B, int32_t T, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+    float k_scale, float v_scale, int32_t kv_split, uint32_t flags, float* out, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  pkv::WriteFp8Args a;
+  int32_t st = check_write_fp8(k_new, v_new, n_rows, k_cache, v_cache, num_blocks, block_size,
+                               num_kv_heads, head_dim, k_scale, v_scale, &a);
+  if (st != PKV_OK) return st;
+  if (B > 0 && ctx_lens_host != nullptr) {
+    st = check_host_tables(block_tables_host, max_blocks, block_size, ctx_lens_host, B);
+    if (st != PKV_OK) return st;
+  }
+  const float scales[2] = {k_scale, v_scale};
+  return attention_impl(q, k_cache, v_cache, block_tables_dev, max_blocks, ctx_lens_host,
+                        cu_seqlens_q_host, B, T, num_q_heads, num_kv_heads, head_dim, block_size,
+                        num_blocks, scale, kv_split, PKV_BF16, flags, out, workspace,
+                        workspace_bytes, stream, nullptr, slots_host, scales, &a, false,
+                        block_tables_host);
+}
+
 extern "C" int32_t pkv_profile_set_kinds(uint32_t kinds) {
   if ((kinds & ~0x1Fu) != 0) return fail(PKV_ERR_INVALID, "profile_set_kinds: unknown kind bits");
   std::lock_guard<std::mutex> lk(g_prof_mu);

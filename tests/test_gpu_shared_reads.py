@@ -134,3 +134,52 @@ def test_host_tables_that_differ_from_the_device_give_nan_rows():
     others = [r for r in range(w.B) if r != b]
     assert np.array_equal(got[others].view(np.uint32), good[others].view(np.uint32))
     assert np.isnan(got[b]).all()
+
+
+FP8_SHARED_SPECS = [
+    # (Hq, Hkv, D, BS, groups, per_group, prefix, tail_lo, tail_hi, kv_split)
+    (16, 4, 128, 16, 3, 5, 1536, 1, 900, 512),     # group 4: four rows per group item
+    (32, 4, 128, 16, 2, 5, 1536, 1, 900, 512),     # group 8: two rows per group item
+    (4, 4, 64, 32, 2, 6, 2048, 1, 400, 256),       # group 1, head_dim 64
+    (8, 4, 128, 8, 1, 7, 704, 1, 2000, 64),        # group 2, many short splits
+]
+
+
+@pytest.mark.parametrize("dims", FP8_SHARED_SPECS,
+                         ids=[f"G{d[0] // d[1]}-D{d[2]}-BS{d[3]}-split{d[9]}"
+                              for d in FP8_SHARED_SPECS])
+def test_fp8_shared_reads_equal_per_row_reads_bitwise(dims):
+    """E4M3 pools ("Finish RL Training Faster: Bitwise-Consistent ...", section 4.2: one read
+    path for FP8 storage): the shared call equals pkv_write_kv_attention_fp8 and each row
+    alone bitwise, and the dequantising oracle within the bar."""
+    from oracle import build_oracle_step
+    hq, hkv, d, bs, groups, per, prefix, tlo, thi, split = dims
+    spec = Spec(f"shared-fp8-{hq}-{hkv}-{d}-{bs}-{split}", "bf16", Hq=hq, Hkv=hkv, D=d, BS=bs,
+                shared=(groups, per, prefix, max(tlo, 1), thi), kv_split=split, kv_dtype="fp8",
+                k_scale=1 / 32, v_scale=1 / 48)
+    w = make_workload(spec)
+    print(f"[shared-fp8] {spec.name} B={w.B}", flush=True)
+    gst = _gpu_step(w)
+    got = pkv.write_kv_attention_shared_fp8(
+        gst.q, gst.k_new, gst.v_new, gst.new_slots, gst.k_cache, gst.v_cache,
+        gst.block_tables_dev, gst.block_tables, w.ctx_lens, w.cu_seqlens_q, w.scale,
+        spec.k_scale, spec.v_scale, kv_split=split)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    assert np.isfinite(got).all()
+    plain = pkv.write_kv_attention_fp8(
+        gst.q, gst.k_new, gst.v_new, gst.new_slots, gst.k_cache, gst.v_cache,
+        gst.block_tables_dev, w.ctx_lens, w.cu_seqlens_q, w.scale, spec.k_scale, spec.v_scale,
+        kv_split=split)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.view(np.uint32), plain.cpu().numpy().view(np.uint32))
+    for b in range(0, w.B, 2):
+        lo, hi = int(w.cu_seqlens_q[b]), int(w.cu_seqlens_q[b + 1])
+        alone = pkv.attention_fp8(gst.q[lo:hi].contiguous(), gst.k_cache, gst.v_cache,
+                                  gst.block_tables_dev[b:b + 1].contiguous(),
+                                  [int(w.ctx_lens[b])], [0, hi - lo], w.scale, spec.k_scale,
+                                  spec.v_scale, kv_split=split)
+        torch.cuda.synchronize()
+        assert np.array_equal(alone.cpu().numpy().view(np.uint32), got[lo:hi].view(np.uint32)), b
+    ref = build_oracle_step(w).attention()
+    assert float(np.abs(got.astype(np.float64) - ref).max()) <= 2e-3
