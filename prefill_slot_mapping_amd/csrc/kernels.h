@@ -132,8 +132,10 @@ hipError_t launch_merge(const MergeArgs& a, int64_t n_items, int head_dim, hipSt
 // (bf16 pools) or launch_decode_fp8 (fp8: E4M3 pools).
 hipError_t launch_decode_groups(const DecodeArgs& a, int64_t n_groups, int head_dim, int group,
                                 bool fp8, hipStream_t stream);
+// lds_pad: dynamic LDS bytes the kernel does not use, reserved so that fewer workgroups share a
+// compute unit (room for other kernels' workgroups beside them)
 hipError_t launch_prefill(const PrefillArgs& a, int64_t n_items, int head_dim, int group,
-                          bool fp8, hipStream_t stream);
+                          bool fp8, hipStream_t stream, uint32_t lds_pad = 0);
 
 // Whether a (head_dim, group, dtype) combination has a built decode / prefill kernel.
 bool decode_supported(int head_dim, int group);

@@ -529,35 +529,35 @@ bool prefill_supported(int head_dim, int group, bool bf16) {
 
 template <int D>
 static hipError_t launch_prefill_d(const PrefillArgs& a, uint32_t grid, int group, bool fp8,
-                                   hipStream_t stream) {
+                                   uint32_t lds_pad, hipStream_t stream) {
   if (fp8) {
     switch (group) {   // E4M3 pools: the groups the E4M3 decode pass serves
-      case 1: hipLaunchKernelGGL((prefill_kernel<D, 1, true>), dim3(grid), dim3(256), 0, stream, a); break;
-      case 2: hipLaunchKernelGGL((prefill_kernel<D, 2, true>), dim3(grid), dim3(256), 0, stream, a); break;
-      case 4: hipLaunchKernelGGL((prefill_kernel<D, 4, true>), dim3(grid), dim3(256), 0, stream, a); break;
-      case 8: hipLaunchKernelGGL((prefill_kernel<D, 8, true>), dim3(grid), dim3(256), 0, stream, a); break;
+      case 1: hipLaunchKernelGGL((prefill_kernel<D, 1, true>), dim3(grid), dim3(256), lds_pad, stream, a); break;
+      case 2: hipLaunchKernelGGL((prefill_kernel<D, 2, true>), dim3(grid), dim3(256), lds_pad, stream, a); break;
+      case 4: hipLaunchKernelGGL((prefill_kernel<D, 4, true>), dim3(grid), dim3(256), lds_pad, stream, a); break;
+      case 8: hipLaunchKernelGGL((prefill_kernel<D, 8, true>), dim3(grid), dim3(256), lds_pad, stream, a); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
   }
   switch (group) {
-    case 1: hipLaunchKernelGGL((prefill_kernel<D, 1, false>), dim3(grid), dim3(256), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((prefill_kernel<D, 2, false>), dim3(grid), dim3(256), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((prefill_kernel<D, 4, false>), dim3(grid), dim3(256), 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((prefill_kernel<D, 8, false>), dim3(grid), dim3(256), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((prefill_kernel<D, 1, false>), dim3(grid), dim3(256), lds_pad, stream, a); break;
+    case 2: hipLaunchKernelGGL((prefill_kernel<D, 2, false>), dim3(grid), dim3(256), lds_pad, stream, a); break;
+    case 4: hipLaunchKernelGGL((prefill_kernel<D, 4, false>), dim3(grid), dim3(256), lds_pad, stream, a); break;
+    case 8: hipLaunchKernelGGL((prefill_kernel<D, 8, false>), dim3(grid), dim3(256), lds_pad, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int64_t n_items, int head_dim, int group,
-                          bool fp8, hipStream_t stream) {
+                          bool fp8, hipStream_t stream, uint32_t lds_pad) {
   const int64_t grid64 = n_items * a.hkv;
   if (grid64 == 0) return hipSuccess;
   if (grid64 > 0x7fffffffLL || n_items != a.n_items) return hipErrorInvalidValue;
   const uint32_t grid = static_cast<uint32_t>(grid64);
-  if (head_dim == 64) return launch_prefill_d<64>(a, grid, group, fp8, stream);
-  if (head_dim == 128) return launch_prefill_d<128>(a, grid, group, fp8, stream);
+  if (head_dim == 64) return launch_prefill_d<64>(a, grid, group, fp8, lds_pad, stream);
+  if (head_dim == 128) return launch_prefill_d<128>(a, grid, group, fp8, lds_pad, stream);
   return hipErrorInvalidValue;
 }
 
