@@ -33,7 +33,7 @@ after the set-up run up to twice as long, steady from about the 50th); the untim
 brackets every kernel; the W warm-up steps and the K timed steps; the cold-cache pass, the
 protocol and the invariance checks.
 
-Prints ONE JSON line (rank 0, N = 1). `--gpus N` with N > 1 exits: this build runs on one GPU.
+Prints ONE JSON line (rank 0, N = 1). `--gpus N` with N > 1 exits: the benchmark runs on one GPU.
 """
 from __future__ import annotations
 
@@ -579,8 +579,8 @@ def main():
     args = _parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
-                                   "(multi-GPU sharding is described in DESIGN.md, not run)"}))
+        print(json.dumps({"error": "the benchmark runs on exactly one GPU; --gpus must be 1 "
+                                   "(sharding across GPUs is not run)"}))
         sys.exit(2)
     import torch
     import prefill_slot_mapping_amd as pkv
