@@ -376,6 +376,7 @@ StepShape shape_for(const int32_t* ctx, const int32_t* cu, int32_t B, int32_t hq
     s.bt_stride = bt_stride;
     s.block_size = block_size;
     s.group_rows = pkv::decode_group_rows(group);
+    s.hkv = hkv;
   }
   return s;
 }

@@ -74,6 +74,7 @@ SharedSplits find_shared_splits(const StepShape& s) {
     const int32_t* ty = s.bt_host + static_cast<int64_t>(y.seq) * s.bt_stride;
     return std::equal(tx + x.j0, tx + x.j1 + 1, ty + y.j0);
   };
+  std::vector<std::vector<DecodeGroupItem>> runs;   // the group items of each shared split
   for (size_t i0 = 0; i0 < recs.size();) {
     size_t i1 = i0 + 1;
     while (i1 < recs.size() && recs[i1].h == recs[i0].h && recs[i1].split == recs[i0].split) ++i1;
@@ -101,9 +102,26 @@ SharedSplits find_shared_splits(const StepShape& s) {
         gi.n_keys = std::min(gi.n_keys, m.n_keys);
         out.taken.push_back({m.row, gi.split});
       }
-      out.groups.push_back(gi);
+      if (m0 == 0) runs.emplace_back();
+      runs.back().push_back(gi);
     }
     i0 = i1;
+  }
+  // The launch deals consecutive workgroups (item i, kv head g at index i hkv + g) to the 8
+  // XCDs in turn, so items d = 8 / gcd(hkv, 8) apart run on one XCD at about the same time:
+  // the items of one shared split are listed d apart (runs taken d at a time, round robin),
+  // so that they read the split through one L2. Measured on the prefix-shared step (4 kv
+  // heads, 2 items per prompt split): decode pass 121.6 -> 116.2 us. Item order changes no
+  // row's bits.
+  int d = 8;
+  for (int h = s.hkv; h % 2 == 0 && d > 1; h /= 2) d /= 2;
+  for (size_t r0 = 0; r0 < runs.size(); r0 += d) {
+    const size_t r1 = std::min(runs.size(), r0 + d);
+    size_t len = 0;
+    for (size_t r = r0; r < r1; ++r) len = std::max(len, runs[r].size());
+    for (size_t j = 0; j < len; ++j)
+      for (size_t r = r0; r < r1; ++r)
+        if (j < runs[r].size()) out.groups.push_back(runs[r][j]);
   }
   std::sort(out.taken.begin(), out.taken.end());
   return out;

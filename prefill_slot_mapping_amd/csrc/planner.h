@@ -35,6 +35,7 @@ struct StepShape {
   int32_t bt_stride = 0;
   int32_t block_size = 0;
   int32_t group_rows = 0;
+  int32_t hkv = 1;   // kv heads (the group launch runs each item once per kv head)
   const SharedSplits* shared = nullptr;   // find_shared_splits of this shape, when taken
 };
 
