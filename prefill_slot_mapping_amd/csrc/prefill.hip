@@ -30,9 +30,11 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "device_common.h"
 #include "kernels.h"
+#include "lane_ops.h"
 
 namespace pkv {
 
@@ -40,6 +42,15 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef unsigned u32x4v_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4v_t lds_u32x4_t;
+
+// x through an empty register-to-register asm: values derived from it inside a loop are
+// recomputed there instead of being held as loop invariants
+__device__ __forceinline__ uint32_t opaque_u32(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 
 // 16-byte chunk swizzle of a K/V row in LDS. For D = 128 (16 chunks): consecutive rows get
 // distinct chunk offsets for the S^T operand reads (16 rows, one chunk each), and four rows
@@ -318,13 +329,41 @@ prefill_kernel(PrefillArgs a) {
   float l_run = 0.f;
   const float sl2 = a.scale_log2e;   // |scale| * log2(e)
 
+  // Fixed parts of this lane's LDS operand addresses (tile rows are swizzled by swz).
+  // S^T operand: key row l32 (+ 32 kb), chunk (2 ks + h32) ^ swz(l32) (swz(l32 + 32 kb) is
+  // swz(l32)), at byte k_base + ((32 ks) ^ k_x0).
+  const uint32_t k_sw = swz<CPR>(l32);
+  const uint32_t k_base = static_cast<uint32_t>(l32 * CPR * 16) + 16u * (h32 ^ (k_sw & 1u));
+  const uint32_t k_x0 = 16u * (k_sw & ~1u);
+  // V^T operand of k-step q, d block db: this lane reads 4 elements at column
+  // 32 db + 16 (grp16 & 1) + csub of key row 16 q + r (slots 0..3, r = 4 (grp16 >> 1) + rsub)
+  // and of key row 16 q + r + 8 (slots 4..7); the chunk of row 16 q + r is swizzled by swz(r).
+  // The byte offset is 16 q CPR 16 + v_base + ((64 db) ^ v_y).
+  const int grp16 = lane >> 4;          // 16-lane group: d half (grp16 & 1), key half (>> 1)
+  const int i16 = lane & 15;
+  const int rsub = i16 >> 2;            // row this lane addresses inside a 4-row read
+  const int csub = 4 * (i16 & 3);       // element column offset inside the 16-wide d strip
+  const uint32_t vr0 = 4 * (grp16 >> 1) + rsub;
+  const uint32_t vc0 = 2 * (grp16 & 1) + (csub >> 3);   // chunk of the strip in d block 0
+  const uint32_t v_sw0 = swz<CPR>(vr0), v_sw1 = swz<CPR>(vr0 + 8);
+  const uint32_t v_base0 = vr0 * CPR * 16 + 16u * (vc0 ^ (v_sw0 & 3u)) + 2u * (csub & 7);
+  const uint32_t v_base1 = (vr0 + 8) * CPR * 16 + 16u * (vc0 ^ (v_sw1 & 3u)) + 2u * (csub & 7);
+  const uint32_t v_y0_ = 16u * (v_sw0 & ~3u), v_y1_ = 16u * (v_sw1 & ~3u);
+
   if (tid == 0) s_bad = 0;
   load_window();
   __syncthreads();
   if constexpr (F8) dma_codes(kt0, 0);
   else dma_tile(kt0, 0);
 
-  for (int kt = kt0; kt < n_tiles; ++kt) {
+  // Tiles kt0 .. kd - 1 cross no row of this wave (each of its rows sees every key of them)
+  // and take the unmasked form; tiles kd .. n_tiles - 1 take the masked form (on a tile that
+  // crosses none of the wave's rows the mask keeps every key of a used row, so masking there
+  // changes no value). Padding M-rows compute finite values that are never written. Each form
+  // has a loop of its own (register allocation of one form does not burden the other); both
+  // meet the same workgroup barriers per tile.
+  const int kd = min(max((wave_first_pos + 1) / kPrefillKeyTile, kt0), n_tiles);
+  auto tile_step = [&](int kt, auto masked_tag) {
     const int par = (kt - kt0) & 1;   // tile kt in buffer par (E4M3: its codes)
     const int buf = F8 ? 0 : par;
     // tile kt has landed in LDS; every wave is done with tile kt - 1 and with the block window
@@ -347,89 +386,102 @@ prefill_kernel(PrefillArgs a) {
       lds_barrier();
     }
 
-    if (kt * kPrefillKeyTile > wave_last_pos) continue;  // no row of this wave sees this tile
-    const uint4* sk = s_kv[buf][0];
+    if (kt * kPrefillKeyTile > wave_last_pos) return;  // no row of this wave sees this tile
+    // LDS byte addresses of the operand reads, derived once per tile from this lane's fixed
+    // parts (kept opaque so that the compiler recomputes them here instead of holding every
+    // derived address in a register across the loop)
+    const uint32_t k_x = opaque_u32(k_x0);
+    const uint32_t v_y0 = opaque_u32(v_y0_);
+    const uint32_t v_y1 = opaque_u32(v_y1_);
+    const uint32_t k_addr = lds_addr(s_kv[buf][0]) + k_base;
+    const uint32_t v_addr = lds_addr(s_kv[buf][1]);
 
-    // ---- S^T = K Q^T: two 32-key blocks; all K fragments of a block are read before its
-    //      MFMAs so that the LDS latency is paid once per block ----
+    // ---- S^T = K Q^T: two 32-key blocks; every K fragment of the tile is read before the
+    //      MFMAs so that the LDS latency is paid once ----
     f32x16_t s[2];
+    u32x4v_t kf[2][KS];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kf[kb][ks] =
+            *(const lds_u32x4_t*)(uintptr_t)(k_addr + kb * 32 * CPR * 16 + ((32u * ks) ^ k_x));
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-      const int row = kb * 32 + l32;
-      uint4 kf[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kf[ks] = sk[row * CPR + ((2 * ks + h32) ^ swz<CPR>(row))];
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[ks]),
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[kb][ks]),
                                                         qf[ks], s[kb], 0, 0, 0);
     }
 
     // ---- online softmax for this lane's M-row (keys split with lane ^ 32), base 2 ----
     // Exponents are taken against a reference m_ref that trails the running max by less than
-    // kRescaleSlack (p <= 2^slack); O and l are rescaled only when the max rises past it.
-    // Tiles that cross a row of the wave (and every tile of a wave with unused rows) take the
-    // masked path. The choice is made for the whole wave: on a tile that crosses none of its
-    // rows the mask keeps every key of a used row, so masking there changes no value.
-    const bool diag = __builtin_amdgcn_ballot_w64(
-        (kt + 1) * kPrefillKeyTile > wave_first_pos + 1 || !real) != 0;
-    float tmax = -INFINITY;
-    if (!diag) {
+    // kRescaleSlack (p <= 2^slack); O and l are rescaled only when the max rises past it. Each
+    // form is straight-line code, so the exponentials of one key group can be scheduled beside
+    // the MFMAs of the previous one.
+    const int tile_key0 = kt * kPrefillKeyTile;
+    // V^T operand of k-step q (key rows 16 q .. 16 q + 15), all d blocks
+    auto read_v = [&](int q, bf16x8_t (&vf)[DB]) {
+      const uint32_t qoff = 16u * q * CPR * 16;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const uint32_t a0 = v_addr + v_base0 + ((64u * db) ^ v_y0) + qoff;
+        const uint32_t a1 = v_addr + v_base1 + ((64u * db) ^ v_y1) + qoff;
+        const s16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)a0);
+        const s16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)a1);
+        const s16x4_t tt[2] = {t0, t1};
+        vf[db] = __builtin_bit_cast(bf16x8_t, tt);
+      }
+    };
+    auto softmax_pv = [&](auto masked_tag) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
+      // the first k-step's V^T reads are in flight during the max
+      bf16x8_t vf[DB];
+      read_v(0, vf);
+      __builtin_amdgcn_sched_barrier(0);
+      // key of score register r of block kb for this lane
+      auto key_of = [&](int kb, int r) {
+        return tile_key0 + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+      };
+      float tmax = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[kb][r]);
-    } else {
+        for (int r = 0; r < 16; ++r)
+          tmax = fmaxf(tmax, (!MASKED || key_of(kb, r) <= pos) ? s[kb][r] : -INFINITY);
+      tmax = across32(tmax, MaxOp());
+      // scale >= 0 keeps the order of scores; fmaxf drops the NaN of -inf * 0
+      const float m_cand = fmaxf(m_ref, tmax * sl2);
+      const bool need = m_cand > m_ref + kRescaleSlack;
+      if (__any(need)) {
+        // a multiply by exactly 1 (rows that keep their reference) changes nothing
+        const float alpha = need ? fast_exp2(m_ref - m_cand) : 1.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kt * kPrefillKeyTile + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-          tmax = fmaxf(tmax, key <= pos ? s[kb][r] : -INFINITY);
-        }
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    // scale >= 0 keeps the order of scores; fmaxf drops the NaN of -inf * 0
-    const float m_cand = fmaxf(m_ref, tmax * sl2);
-    const bool need = m_cand > m_ref + kRescaleSlack;
-    if (__any(need)) {
-      // a multiply by exactly 1 (rows that keep their reference) changes nothing
-      const float alpha = need ? fast_exp2(m_ref - m_cand) : 1.f;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-      l_run *= alpha;
-      m_ref = need ? m_cand : m_ref;
-    }
-    const float neg_m = -m_ref;
+          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+        l_run *= alpha;
+        m_ref = need ? m_cand : m_ref;
+      }
+      const float neg_m = -m_ref;
 
-    // ---- O^T += V^T P^T per 16-key k-step (kb, m); the A operand (V^T) comes from two
-    //      transpose reads, the B operand (P^T) is this lane's own probabilities ----
-    const int grp16 = lane >> 4;          // 16-lane group: d half (grp16 & 1), key half (>> 1)
-    const int i16 = lane & 15;
-    const int rsub = i16 >> 2;            // row this lane addresses inside a 4-row read
-    const int csub = 4 * (i16 & 3);       // element column offset inside the 16-wide d strip
-    __attribute__((address_space(3))) char* vbase =
-        (__attribute__((address_space(3))) char*)(s_kv[buf][1]);
-    float psum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        // P = hi + lo: hi = p with its low 16 bits cleared (a bfloat16 value), lo = the exact
-        // float32 remainder rounded to bfloat16, so hi + lo carries about 16 bits of p
+      // ---- O^T += V^T P^T per 16-key k-step q = (kb, m); the A operand (V^T) comes from two
+      //      transpose reads, the B operand (P^T) is this lane's own probabilities ----
+      float psum = 0.f;
+      // P = hi + lo for k-step q: hi = p with its low 16 bits cleared (a bfloat16 value), lo =
+      // the exact float32 remainder rounded to bfloat16, so hi + lo carries about 16 bits of p
+      auto make_p = [&](int q, bf16x8_t& phi, bf16x8_t& plo) {
+        const int kb = q >> 1, m = q & 1;
         uint32_t phw[4], plw[4];
 #pragma unroll
         for (int j = 0; j < 8; j += 2) {
           float p0 = fast_exp2(fmaf(s[kb][8 * m + j], sl2, neg_m));
           float p1 = fast_exp2(fmaf(s[kb][8 * m + j + 1], sl2, neg_m));
-          if (diag) {
-            const int r = 8 * m + j;
-            const int key = kt * kPrefillKeyTile + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+          if constexpr (MASKED) {
+            const int key = key_of(kb, 8 * m + j);
             p0 = key <= pos ? p0 : 0.f;
             p1 = key + 1 <= pos ? p1 : 0.f;
           }
@@ -442,29 +494,34 @@ prefill_kernel(PrefillArgs a) {
           typedef float f32x2_t __attribute__((ext_vector_type(2)));
           plw[j / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{l0, l1}, bf16x2_t));
         }
-        const bf16x8_t phi = __builtin_bit_cast(bf16x8_t, phw);
-        const bf16x8_t plo = __builtin_bit_cast(bf16x8_t, plw);
-        const int r0 = kb * 32 + 16 * m + 4 * (grp16 >> 1) + rsub;   // slots 0..3
-        const int r1 = r0 + 8;                                        // slots 4..7
+        phi = __builtin_bit_cast(bf16x8_t, phw);
+        plo = __builtin_bit_cast(bf16x8_t, plw);
+      };
+      bf16x8_t phi, plo;
+      make_p(0, phi, plo);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        // the next k-step's V^T reads are in flight during this one's MFMAs
+        bf16x8_t vn[DB];
+        if (q + 1 < 4) read_v(q + 1, vn);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const int dcol = 32 * db + 16 * (grp16 & 1) + csub;
-          const int cchunk = dcol >> 3;
-          const int cin = dcol & 7;
-          lds_s16x4_t* p0 =
-              (lds_s16x4_t*)(vbase + (r0 * CPR + (cchunk ^ swz<CPR>(r0))) * 16 + cin * 2);
-          lds_s16x4_t* p1 =
-              (lds_s16x4_t*)(vbase + (r1 * CPR + (cchunk ^ swz<CPR>(r1))) * 16 + cin * 2);
-          const s16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p0);
-          const s16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p1);
-          const s16x4_t tt[2] = {t0, t1};
-          const bf16x8_t va = __builtin_bit_cast(bf16x8_t, tt);
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, phi, acc[db], 0, 0, 0);
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, plo, acc[db], 0, 0, 0);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], phi, acc[db], 0, 0, 0);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], plo, acc[db], 0, 0, 0);
         }
+        if (q + 1 < 4) {
+          make_p(q + 1, phi, plo);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) vf[db] = vn[db];
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-    l_run += psum;
-  }
+      l_run += psum;
+    };
+    softmax_pv(masked_tag);
+  };
+  for (int kt = kt0; kt < kd; ++kt) tile_step(kt, std::false_type{});
+  for (int kt = kd; kt < n_tiles; ++kt) tile_step(kt, std::true_type{});
 
   if (bad) s_bad = 1;
   __syncthreads();
