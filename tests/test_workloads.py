@@ -1,7 +1,7 @@
 """The seeded synthetic steps have the shapes and structure their recipes state."""
 import numpy as np
 
-from workloads import CONFIGS, SMALL_CONFIGS, make_workload, stable_seed
+from workloads import CONFIGS, DIAGNOSTIC_CONFIGS, SMALL_CONFIGS, make_workload, stable_seed
 
 
 def test_seeds_are_stable_and_distinct():
@@ -61,3 +61,12 @@ def test_outliers_scale_about_one_percent_of_k_rows():
     rows = np.abs(bf16_bits_to_f64(k)).max(axis=-1)     # [ctx, Hkv]
     frac = (rows > 6.0).mean()
     assert 0.002 < frac < 0.03
+
+
+def test_prefill_rows_workload_is_the_mixed_steps_segments():
+    w = make_workload(CONFIGS["mixed-ragged-step"])
+    pre = w.q_lens > 1
+    d = make_workload(DIAGNOSTIC_CONFIGS["mixed-step-prefill-rows"])
+    assert (d.q_lens > 1).all()
+    assert sorted(zip(d.ctx_lens.tolist(), d.q_lens.tolist())) == \
+        sorted(zip(w.ctx_lens[pre].tolist(), w.q_lens[pre].tolist()))

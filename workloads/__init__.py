@@ -25,7 +25,7 @@ import numpy as np
 
 __all__ = [
     "stable_seed", "round_f32_to_bf16_bits", "Spec", "Admission", "Workload",
-    "make_workload", "CONFIGS", "SMALL_CONFIGS", "explicit_spec",
+    "make_workload", "CONFIGS", "SMALL_CONFIGS", "DIAGNOSTIC_CONFIGS", "explicit_spec",
 ]
 
 
@@ -392,4 +392,13 @@ FP8_SMALL_CONFIGS = {
                                     v_scale=1 / 64),
 }
 
-ALL_CONFIGS = {**CONFIGS, **FP8_CONFIGS}
+# Measurement only: the mixed step's eight chunked-prefill segments (the (ctx, q_len) pairs its
+# draw gives) with no decode rows, so that the prefill tile kernel runs alone, in one launch.
+DIAGNOSTIC_CONFIGS = {
+    "mixed-step-prefill-rows": Spec("mixed-step-prefill-rows", "bf16", Hq=32, Hkv=8, D=128,
+                                    BS=16, explicit=((2620, 512), (795, 512), (5169, 512),
+                                                     (3436, 512), (2650, 512), (8095, 512),
+                                                     (5333, 512), (6535, 512))),
+}
+
+ALL_CONFIGS = {**CONFIGS, **FP8_CONFIGS, **DIAGNOSTIC_CONFIGS}
