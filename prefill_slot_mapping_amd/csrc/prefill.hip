@@ -44,6 +44,7 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef unsigned u32x4v_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x4v_t lds_u32x4_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
 
 // x through an empty register-to-register asm: values derived from it inside a loop are
 // recomputed there instead of being held as loop invariants
@@ -393,8 +394,9 @@ prefill_kernel(PrefillArgs a) {
     const uint32_t k_x = opaque_u32(k_x0);
     const uint32_t v_y0 = opaque_u32(v_y0_);
     const uint32_t v_y1 = opaque_u32(v_y1_);
-    const uint32_t k_addr = lds_addr(s_kv[buf][0]) + k_base;
-    const uint32_t v_addr = lds_addr(s_kv[buf][1]);
+    // (LDS pointers, so that the k-step's and block's constant parts become instruction offsets)
+    lds_char_t* const k_ptr = (lds_char_t*)(s_kv[buf][0]) + k_base;
+    lds_char_t* const v_ptr = (lds_char_t*)(s_kv[buf][1]);
 
     // ---- S^T = K Q^T: two 32-key blocks; every K fragment of the tile is read before the
     //      MFMAs so that the LDS latency is paid once ----
@@ -405,7 +407,7 @@ prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         kf[kb][ks] =
-            *(const lds_u32x4_t*)(uintptr_t)(k_addr + kb * 32 * CPR * 16 + ((32u * ks) ^ k_x));
+            *(const lds_u32x4_t*)(k_ptr + ((32u * ks) ^ k_x) + kb * 32 * CPR * 16);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -428,10 +430,10 @@ prefill_kernel(PrefillArgs a) {
       const uint32_t qoff = 16u * q * CPR * 16;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const uint32_t a0 = v_addr + v_base0 + ((64u * db) ^ v_y0) + qoff;
-        const uint32_t a1 = v_addr + v_base1 + ((64u * db) ^ v_y1) + qoff;
-        const s16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)a0);
-        const s16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)a1);
+        lds_char_t* const a0 = v_ptr + (v_base0 + ((64u * db) ^ v_y0)) + qoff;
+        lds_char_t* const a1 = v_ptr + (v_base1 + ((64u * db) ^ v_y1)) + qoff;
+        const s16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)a0);
+        const s16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)a1);
         const s16x4_t tt[2] = {t0, t1};
         vf[db] = __builtin_bit_cast(bf16x8_t, tt);
       }
