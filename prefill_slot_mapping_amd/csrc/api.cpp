@@ -237,12 +237,12 @@ int32_t stage_and_copy(void* dst, size_t bytes, hipStream_t strm, const char* wh
 // thresholds the two event records and waits cost more than the overlap gains. Enqueueing the
 // fork and the join holds a per-device lock, so the events are never re-recorded in between.
 // Kernels, work lists and outputs are the same either way, so no output bit depends on it.
-// With bf16 pools a forked step's prefill pass is two launches of the same kernel: first one
-// round of its longest items at one workgroup per compute unit (unused LDS reserved, so that a
-// decode workgroup fits beside each: 256 + 226 registers per SIMD lane), then the rest at full
+// A forked step's prefill pass is two launches of the same kernel: first one round of its
+// longest items at one workgroup per compute unit (unused LDS reserved, so that a decode
+// workgroup fits beside each: about 220 + 226 registers per SIMD lane), then the rest at full
 // occupancy. Measured on the mixed ragged step: 711 against 783 us per step; a first part of
-// 81 % or 119 % of a round 727 / 770 us (a part round leaves units idle or adds a tail);
-// E4M3 pools gained nothing (its decode pass is shorter), so their prefill stays one launch.
+// 81 % or 119 % of a round 727 / 770 us (a part round leaves units idle or adds a tail), two or
+// three rounds 731 / 740 us; on the E4M3 mixed step 619-626 against 631-636 us.
 constexpr int64_t kForkMinPrefillWgs = 512;
 constexpr int64_t kForkMinDecodeWgs = 1024;
 constexpr uint32_t kPrefillSharePad = 32768;   // bytes of LDS reserved per prefill workgroup
@@ -645,8 +645,8 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
       p.part_l = part_l;
       p.part_acc = part_acc;
       const int pr = prof_begin(1, strm);
-      // forked bf16 step: first one round of the longest items beside the decode pass
-      const int64_t n_a = fork && fp8_scales == nullptr && side->n_cu > 0
+      // forked step: first one round of the longest items beside the decode pass
+      const int64_t n_a = fork && side->n_cu > 0
                               ? std::min<int64_t>(L.n_prefill, side->n_cu / num_kv_heads)
                               : 0;
       const uint32_t pad = kPrefillSharePad;
