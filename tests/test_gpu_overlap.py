@@ -1,7 +1,7 @@
 """A large mixed step runs its decode pass on the library's second stream, beside the prefill
 pass (it forks when the prefill grid has more than 512 workgroups and the decode grid at least
-1024; with bf16 pools its prefill pass is then two launches, one round of the longest items at
-one workgroup per compute unit first). Its rows must be bitwise those the same rows get from
+1024; its prefill pass is then two launches, one round of the longest items at one workgroup
+per compute unit first, with bf16 and with E4M3 pools). Its rows must be bitwise those the same rows get from
 steps that do not fork (the prefill segments alone, one launch; the decode rows alone), and
 work enqueued on the caller's stream after the call must see the finished output (the join
 back to that stream).
