@@ -90,6 +90,26 @@ __device__ __forceinline__ int kswz(int r) {
   return (r / kRowsPerSpan) & (CPR - 1);
 }
 
+// 16 bytes at base + off (base the same in every lane), nontemporal, as a global-memory load
+// with a scalar base and a 32-bit lane offset
+__device__ __forceinline__ uint4 load_nt_global(const char* base, uint32_t off) {
+  asm("" : "+v"(off));   // a 32-bit value here, so the offset is not widened ahead of time
+  typedef unsigned u4v __attribute__((ext_vector_type(4)));
+  const __attribute__((address_space(1))) u4v* p =
+      reinterpret_cast<const __attribute__((address_space(1))) u4v*>(
+          (const __attribute__((address_space(1))) char*)(base) + off);
+  const u4v t = __builtin_nontemporal_load(p);
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+// a pointer that is the same in every lane, as such (scalar registers)
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t x = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x >> 32));
+  return reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // two E4M3 codes (bytes 0-1, or 2-3 with hi) of w -> a bfloat16 pair, exactly
 __device__ __forceinline__ uint32_t e4m3x2_bf16x2(uint32_t w, bool hi) {
   return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
@@ -224,9 +244,14 @@ decode_mfma_kernel(DecodeArgs a) {
   const int vchunk = lane % CPRV;   // 16-byte chunk of that row
   const char* kbase = static_cast<const char*>(a.k_cache) + g * RB + vchunk * 16;
   const char* vbase = static_cast<const char*>(a.v_cache) + g * RB + vchunk * 16;
+  // this lane's byte offset from the slot of the first key its instruction row covers
+  const uint32_t lane_off = static_cast<uint32_t>(vrow * slot_bytes) + vchunk * 16;
+  const char* kbase_u = static_cast<const char*>(a.k_cache) + g * RB;   // the same in every lane
+  const char* vbase_u = static_cast<const char*>(a.v_cache) + g * RB;
   // blocks of 16 keys or more (a power of two): the 16 keys of a tile half are consecutive
-  // slots of one block (tiles start at multiples of 32 keys)
-  const bool halves_in_block = a.bs_log2 >= 4;
+  // slots of one block (tiles start at multiples of 32 keys); the lane's 32-bit offset from
+  // its instruction's first row (under 16 rows) needs slots of at most 64 MiB
+  const bool halves_in_block = a.bs_log2 >= 4 && slot_bytes <= (uint64_t{1} << 26);
   const int last16 = (nk - 1) & ~15;
 
   // the wave's LDS tile: K codes / values of the tile, then (once the scores are taken) its V
@@ -258,16 +283,26 @@ decode_mfma_kernel(DecodeArgs a) {
   // the general path issued together), then the loads; lane (vrow, vchunk) of instruction u
   // takes chunk vchunk of key u RPI + vrow of both tensors
   auto load_kv = [&](uint4 (&kr)[VU4], uint4 (&vr)[VU4], int ts) {
-    uint32_t sl[VU4];
     if (halves_in_block) {
+      // instruction u covers rows u RPI .. u RPI + RPI - 1, all in one half (RPI divides 16):
+      // the slot of its first row is the same in every lane, the lane adds its row and chunk
       uint32_t base0, base1;
       half_bases(ts, base0, base1);
 #pragma unroll
       for (int u = 0; u < VU4; ++u) {
-        const int r = u * RPI + vrow;
-        sl[u] = (r < 16 ? base0 : base1) + (r & 15);
+        const int r0 = u * RPI;
+        const uint64_t row0 = static_cast<uint64_t>((r0 < 16 ? base0 : base1) + (r0 & 15)) *
+                              slot_bytes;
+        // (the row's address kept uniform, so that the load takes it as its scalar base)
+        const char* kp = uniform_ptr(kbase_u + row0);
+        const char* vp = uniform_ptr(vbase_u + row0);
+        kr[u] = load_nt_global(kp, lane_off);
+        vr[u] = load_nt_global(vp, lane_off);
       }
-    } else {
+      return;
+    }
+    uint32_t sl[VU4];
+    {
 #pragma unroll
       for (int u = 0; u < VU4; ++u) sl[u] = s_slot[ts + u * RPI + vrow];
     }
@@ -325,15 +360,22 @@ decode_mfma_kernel(DecodeArgs a) {
 
     // ---- lazy online softmax (base 2) for head col over this lane's 8 keys ----
     float t[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) t[kb][r] = s[kb][r] * sl2;
+    if (n < TK) {   // the split's last tile: keys past the context get -inf
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (16 * kb + 4 * quarter + r >= n) t[kb][r] = -INFINITY;
+    }
     float tmax = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float x = s[kb][r] * sl2;
-        t[kb][r] = (n < TK && 16 * kb + 4 * quarter + r >= n) ? -INFINITY : x;
-        tmax = fmaxf(tmax, t[kb][r]);
-      }
+      for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, t[kb][r]);
     tmax = across16(tmax, MaxOp());
     tmax = across32(tmax, MaxOp());
     const float m_cand = fmaxf(m_ref, tmax);
