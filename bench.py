@@ -71,8 +71,10 @@ def _parse():
     ap.add_argument("--consistent", default="batched-bf16-decode,mixed-ragged-step",
                     help="comma-separated workloads also timed in the phase-consistent mode, "
                          "reported under 'extra' as '<name>/phase-consistent'")
-    ap.add_argument("--consistent-split", type=int, default=2048,
-                    help="kv_split of the phase-consistent runs (the tile path's KV split)")
+    ap.add_argument("--consistent-split", type=int, default=4096,
+                    help="kv_split of the phase-consistent runs (the tile path's KV split; "
+                         "4096 is the fastest of 2048 / 4096 / 8192 on both default "
+                         "consistent workloads)")
     ap.add_argument("--kernel-events", choices=("timed", "separate"), default="timed",
                     help="take the per-kernel HIP-event times inside the timed steps (default) "
                          "or in a second pass of the same steps")
