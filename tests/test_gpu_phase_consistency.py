@@ -80,6 +80,52 @@ def test_decode_row_equals_prefill_row_bitwise(dims):
         assert float(np.abs(plain.astype(np.float64) - dec).max()) <= TOL
 
 
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+def test_decode_row_equals_prefill_row_bitwise_at_4096_key_splits(kind):
+    """The same bit identity at 4096-key splits over a 9000-token context (three splits), so
+    that rows on both sides of each split boundary write partials and are merged; bf16 and
+    E4M3 pools. The workload's own decode row (the last position) is checked against the
+    float64 oracle as well."""
+    hq, hkv, d, bs, split, C = 32, 8, 128, 16, 4096, 9000
+    kw = dict(kv_dtype="fp8", k_scale=1 / 32, v_scale=1 / 40) if kind == "fp8" else {}
+    w = make_workload(explicit_spec(f"phase-4096-{kind}", "bf16", hq, hkv, d, bs, [(C, 1)],
+                                    kv_split=split, **kw))
+    gst = _gpu_step(w)
+    ref = build_oracle_step(w).attention()
+    got = gst.attention(phase_consistent=True).cpu().numpy().astype(np.float64)
+    torch.cuda.synchronize()
+    err = float(np.abs(got - ref).max())
+    print(f"[phase] {w.spec.name} last row max abs err {err:.3e}", flush=True)
+    assert err <= TOL
+    bt = gst.block_tables_dev[0:1].contiguous()
+
+    def run(rows, ctx, pc=True, kv_split=split):
+        n = rows.shape[0]
+        if kind == "fp8":
+            out = pkv.attention_fp8(rows.contiguous(), gst.k_cache, gst.v_cache, bt, [ctx],
+                                    [0, n], w.scale, w.spec.k_scale, w.spec.v_scale,
+                                    kv_split=kv_split, phase_consistent=pc)
+        else:
+            out = pkv.attention(rows.contiguous(), gst.k_cache, gst.v_cache, bt, [ctx], [0, n],
+                                w.scale, kv_split=kv_split, phase_consistent=pc)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+    rng = np.random.default_rng(11)
+    qs = torch.from_numpy(rng.standard_normal((C, hq, d)).astype(np.float32)).to(
+        torch.bfloat16).to(DEV)
+    for p in [4095, 4096, 4097, 8191, 8192, C - 1]:
+        print(f"[phase] {kind} split={split} p={p}", flush=True)
+        dec = run(qs[p:p + 1], p + 1)[0]
+        lo = p - 200
+        assert np.array_equal(dec, run(qs[lo:p + 1], p + 1)[-1]), f"chunk ending at {p}"
+        hi = min(C, p + 50)
+        assert np.array_equal(dec, run(qs[lo:hi], hi)[p - lo]), f"chunk through {p}"
+        # the default mode's split decode path: two paths each within TOL of the exact value
+        plain = run(qs[p:p + 1], p + 1, pc=False, kv_split=512)[0]
+        assert float(np.abs(plain.astype(np.float64) - dec).max()) <= 2 * TOL
+
+
 def test_consistent_mode_alone_equals_batched_bitwise():
     w = make_workload(SMALL_CONFIGS["mixed-ragged-step"])
     gst = _gpu_step(w)
