@@ -78,6 +78,9 @@ def _parse():
     ap.add_argument("--kernel-events", choices=("timed", "separate"), default="timed",
                     help="take the per-kernel HIP-event times inside the timed steps (default) "
                          "or in a second pass of the same steps")
+    ap.add_argument("--stream-reference", action="store_true",
+                    help="only time torch's 2 GiB device copy and float32 sum (HBM rate "
+                         "references) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 1 GiB device copies (scale reference for PMC byte "
                          "counters) and exit")
@@ -95,6 +98,34 @@ def copy_calibration(reps=5, nbytes=1 << 30):
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration": {"bytes_per_copy": nbytes, "reps": reps,
                                            "kib_per_copy": nbytes / 1024}}))
+
+
+def stream_reference(reps=20, nbytes=2 << 30):
+    """Bandwidth that torch's own device streams reach on this GPU, as a reference for the
+    kernels' HBM rates: a copy of nbytes (read + write) and a float32 sum over nbytes (read),
+    each averaged over reps launches between two HIP events."""
+    import torch
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps * 1e-3
+
+    t_copy = timed(lambda: y.copy_(x))
+    t_sum = timed(lambda: x.sum())
+    print(json.dumps({"stream_reference": {
+        "bytes": nbytes, "reps": reps,
+        "copy_us": t_copy * 1e6, "copy_tbs_read_plus_write": 2 * nbytes / t_copy / 1e12,
+        "sum_us": t_sum * 1e6, "sum_tbs_read": nbytes / t_sum / 1e12}}))
 
 
 def _step_inputs(w, gst):
@@ -589,6 +620,9 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
+    if args.stream_reference:
+        stream_reference()
+        return
     if args.copy_calibration:
         copy_calibration()
         return
