@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 
 TOL = {"bf16": 2e-3, "f32": 1e-5}
 DEV = "cuda:0"
-N_CASES = 48
+N_CASES = 144
 
 
 def _draw(i):
