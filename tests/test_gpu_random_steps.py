@@ -7,7 +7,9 @@ tests: attention within max abs error 2e-3 (bf16 inputs) or 1e-5 (float32) of th
 oracle, in the default mode and (bf16 and E4M3 pools) the phase-consistent mode, and every
 sequence run alone bitwise equal to its rows in the batch. The draws cover what fixed cases
 rarely combine: segments whose rows start inside a 64-key tile, waves of a prefill item that
-hold only padding rows, splits that end inside a tile, blocks of 1 and 3 keys.
+hold only padding rows, splits that end inside a tile, blocks of 1 and 3 keys. A second, smaller
+set draws contexts of up to 6000 keys, chunks of up to 300 rows and splits of up to 2048 keys, so
+that rows span many splits.
 """
 import numpy as np
 import pytest
@@ -22,26 +24,27 @@ pytestmark = pytest.mark.gpu
 TOL = {"bf16": 2e-3, "f32": 1e-5}
 DEV = "cuda:0"
 N_CASES = 144
+N_LONG = 24    # contexts to 6000 keys and chunks to 300 rows: many splits per row
 
 
-def _draw(i):
-    rng = np.random.default_rng(20260000 + i)
+def _draw(i, long=False):
+    rng = np.random.default_rng((20270000 if long else 20260000) + i)
     group = int(rng.choice([1, 2, 4, 8]))
     hkv = int(rng.choice([1, 2])) if group < 8 else 1
     d = int(rng.choice([64, 128]))
     bs = int(rng.choice([1, 3, 8, 16, 32, 64]))
     kind = ("fp8", "f32", "bf16", "bf16")[i % 4]
-    kv_split = int(rng.choice([64, 128, 512, 1024]))
+    kv_split = int(rng.choice([64, 512, 1024, 2048] if long else [64, 128, 512, 1024]))
     seqs = []
     for _ in range(int(rng.integers(1, 6))):
-        q = 1 if rng.random() < 0.4 else int(rng.integers(2, 140))
-        prior = int(rng.integers(0, 600))
+        q = 1 if rng.random() < 0.4 else int(rng.integers(2, 300 if long else 140))
+        prior = int(rng.integers(0, 6000 if long else 600))
         seqs.append((prior + q, q))
     kw = {"kv_split": kv_split}
     if kind == "fp8":
         kw.update(kv_dtype="fp8", k_scale=1 / 64, v_scale=1 / 64)
     dtype = "f32" if kind == "f32" else "bf16"
-    name = f"random-{i}-{kind}-G{group}-Hkv{hkv}-D{d}-BS{bs}-S{kv_split}"
+    name = f"random-{'long-' if long else ''}{i}-{kind}-G{group}-Hkv{hkv}-D{d}-BS{bs}-S{kv_split}"
     return explicit_spec(name, dtype, group * hkv, hkv, d, bs, seqs, **kw), kind
 
 
@@ -61,10 +64,12 @@ def _alone(gst, w, b, phase_consistent):
     return out.cpu().numpy()
 
 
-@pytest.mark.parametrize("i", range(N_CASES))
+@pytest.mark.parametrize("i", [(i, False) for i in range(N_CASES)] +
+                         [(i, True) for i in range(N_LONG)],
+                         ids=lambda x: f"{'long-' if x[1] else ''}{x[0]}")
 def test_random_step_matches_oracle_and_is_batch_invariant(i):
     from prefill_slot_mapping_amd.harness import build_gpu_step
-    spec, kind = _draw(i)
+    spec, kind = _draw(*i)
     w = make_workload(spec)
     print(f"[random] {spec.name} seqs={list(zip(w.ctx_lens.tolist(), w.q_lens.tolist()))}",
           flush=True)
