@@ -9,7 +9,8 @@ sequence run alone bitwise equal to its rows in the batch. The draws cover what 
 rarely combine: segments whose rows start inside a 64-key tile, waves of a prefill item that
 hold only padding rows, splits that end inside a tile, blocks of 1 and 3 keys. A second, smaller
 set draws contexts of up to 6000 keys, chunks of up to 300 rows and splits of up to 2048 keys, so
-that rows span many splits.
+that rows span many splits; a third set does the same in the phase-consistent mode alone at
+splits of 4096 and 8192 keys (beyond the default mode's limit of 2048).
 """
 import numpy as np
 import pytest
@@ -25,16 +26,20 @@ TOL = {"bf16": 2e-3, "f32": 1e-5}
 DEV = "cuda:0"
 N_CASES = 144
 N_LONG = 24    # contexts to 6000 keys and chunks to 300 rows: many splits per row
+N_PC = 12      # the same, phase-consistent mode only, at splits beyond the default mode's 2048
+SEED_BASE = {"short": 20260000, "long": 20270000, "pc": 20280000}
 
 
-def _draw(i, long=False):
-    rng = np.random.default_rng((20270000 if long else 20260000) + i)
+def _draw(i, set_="short"):
+    long = set_ != "short"
+    rng = np.random.default_rng(SEED_BASE[set_] + i)
     group = int(rng.choice([1, 2, 4, 8]))
     hkv = int(rng.choice([1, 2])) if group < 8 else 1
     d = int(rng.choice([64, 128]))
     bs = int(rng.choice([1, 3, 8, 16, 32, 64]))
-    kind = ("fp8", "f32", "bf16", "bf16")[i % 4]
-    kv_split = int(rng.choice([64, 512, 1024, 2048] if long else [64, 128, 512, 1024]))
+    kind = ("fp8", "bf16" if set_ == "pc" else "f32", "bf16", "bf16")[i % 4]
+    kv_split = int(rng.choice([4096, 8192] if set_ == "pc" else
+                              [64, 512, 1024, 2048] if long else [64, 128, 512, 1024]))
     seqs = []
     for _ in range(int(rng.integers(1, 6))):
         q = 1 if rng.random() < 0.4 else int(rng.integers(2, 300 if long else 140))
@@ -44,7 +49,7 @@ def _draw(i, long=False):
     if kind == "fp8":
         kw.update(kv_dtype="fp8", k_scale=1 / 64, v_scale=1 / 64)
     dtype = "f32" if kind == "f32" else "bf16"
-    name = f"random-{'long-' if long else ''}{i}-{kind}-G{group}-Hkv{hkv}-D{d}-BS{bs}-S{kv_split}"
+    name = f"random-{set_}-{i}-{kind}-G{group}-Hkv{hkv}-D{d}-BS{bs}-S{kv_split}"
     return explicit_spec(name, dtype, group * hkv, hkv, d, bs, seqs, **kw), kind
 
 
@@ -64,9 +69,9 @@ def _alone(gst, w, b, phase_consistent):
     return out.cpu().numpy()
 
 
-@pytest.mark.parametrize("i", [(i, False) for i in range(N_CASES)] +
-                         [(i, True) for i in range(N_LONG)],
-                         ids=lambda x: f"{'long-' if x[1] else ''}{x[0]}")
+@pytest.mark.parametrize("i", [(i, "short") for i in range(N_CASES)] +
+                         [(i, "long") for i in range(N_LONG)] + [(i, "pc") for i in range(N_PC)],
+                         ids=lambda x: f"{x[1]}-{x[0]}")
 def test_random_step_matches_oracle_and_is_batch_invariant(i):
     from prefill_slot_mapping_amd.harness import build_gpu_step
     spec, kind = _draw(*i)
@@ -75,7 +80,7 @@ def test_random_step_matches_oracle_and_is_batch_invariant(i):
           flush=True)
     gst = build_gpu_step(w, device=DEV)
     ref = build_oracle_step(w).attention()
-    modes = [False] if kind == "f32" else [False, True]
+    modes = [True] if i[1] == "pc" else [False] if kind == "f32" else [False, True]
     for pc in modes:
         out = gst.attention(phase_consistent=pc).cpu().numpy().copy()
         torch.cuda.synchronize()
